@@ -1,0 +1,248 @@
+"""Pins for the oracle's norm, codes and byte layouts."""
+import bisect
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import codec
+from oracle.hadamard import sylvester
+from oracle.lloyd_max import mse_normal
+from synth import sign_vector
+
+getcontext().prec = 60
+_POS_FP16 = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)      # every finite fp16 >= 0, ascending
+_POS_DEC = [Decimal(float(v)) for v in _POS_FP16]
+
+
+def _brute_fp16_round(d: Decimal) -> float:
+    """Nearest fp16 to a high-precision decimal, ties to even significand, saturating at 65504."""
+    if d >= Decimal(65504):
+        return 65504.0
+    i = bisect.bisect_left(_POS_DEC, d)
+    if _POS_DEC[i] == d:
+        return float(_POS_FP16[i])
+    lo, hi = i - 1, i
+    dl, dh = d - _POS_DEC[lo], _POS_DEC[hi] - d
+    if dl < dh:
+        return float(_POS_FP16[lo])
+    if dh < dl:
+        return float(_POS_FP16[hi])
+    return float(_POS_FP16[lo] if (_POS_FP16[lo:lo + 1].view(np.uint16)[0] & 1) == 0 else _POS_FP16[hi])
+
+
+def _brute_norm(x16) -> float:
+    s = sum(Fraction(float(v)) ** 2 for v in x16)
+    d = (Decimal(s.numerator) / Decimal(s.denominator)).sqrt()
+    return _brute_fp16_round(d)
+
+
+def _group(vals):
+    x = np.zeros(128, dtype=np.float16)
+    x[:len(vals)] = np.array(vals, dtype=np.float64).astype(np.float16)
+    return x
+
+
+# ----------------------------------------------------------------------------- norm
+
+@pytest.mark.parametrize("vals,want", [
+    ([2048, 64, 1], 2048.0),                  # sqrt = 2049 exactly: tie between 2048 and 2050, even wins
+    ([2048, 110, 14, 1], 2052.0),             # sqrt = 2051 exactly: tie between 2050 and 2052, even wins
+    ([2048, 64, 1, 2.0 ** -24], 2050.0),      # a hair above the tie; an fp64 sum of squares would lose it
+    ([3 * 2.0 ** -24, 4 * 2.0 ** -24], 5 * 2.0 ** -24),   # subnormal, exact
+    ([-7.5], 7.5),
+    ([0.0], 0.0),
+])
+def test_norm_special_cases(vals, want):
+    assert float(codec.group_norm_fp16(_group(vals)[None])[0]) == want
+
+
+def test_norm_saturates():
+    x = np.full((1, 128), 65504.0, dtype=np.float16)
+    assert float(codec.group_norm_fp16(x)[0]) == 65504.0
+
+
+def test_norm_brute_force_random():
+    rng = np.random.default_rng(7)
+    xs = [rng.standard_normal(128).astype(np.float16) for _ in range(12)]
+    xs += [(rng.standard_normal(128) * 1e-3).astype(np.float16) for _ in range(4)]      # subnormal-heavy
+    xs += [np.clip(rng.standard_t(3, 128) * 300, -65504, 65504).astype(np.float16) for _ in range(4)]
+    got = codec.group_norm_fp16(np.stack(xs))
+    for x, g in zip(xs, got):
+        assert float(g) == _brute_norm(x)
+
+
+# ----------------------------------------------------------------------------- codes
+
+def _brute_codes(x16, signs, cb16, n16):
+    """argmin_k |y_i - n c_k| in 60-digit decimal, lower index on ties."""
+    h = sylvester(128)
+    xs = [Fraction(float(v)) * int(s) for v, s in zip(x16, signs)]
+    root = Decimal(128).sqrt()
+    c = [Decimal(float(v)) for v in cb16]
+    n = Decimal(float(n16))
+    out = []
+    for i in range(128):
+        yhat = sum(xs[j] * int(h[i, j]) for j in range(128))
+        y = Decimal(yhat.numerator) / Decimal(yhat.denominator) / root
+        d = [abs(y - n * ck) for ck in c]
+        out.append(min(range(len(c)), key=lambda k: (d[k], k)))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("fmt", ["turbo3", "turbo4"])
+def test_codes_equal_brute_force_argmin(fmt, codebooks):
+    rng = np.random.default_rng(11)
+    s = sign_vector(5, "k")
+    x = rng.standard_normal((3, 128)).astype(np.float16)
+    x[2] = (x[2] * 40).astype(np.float16)
+    codes, n16 = codec.encode(x, s, codebooks[fmt])
+    for g in range(3):
+        np.testing.assert_array_equal(codes[g], _brute_codes(x[g], s, codebooks[fmt], n16[g]))
+
+
+@pytest.mark.parametrize("fmt", ["turbo3", "turbo4"])
+def test_zero_coordinates_go_to_lower_middle_index(fmt, codebooks):
+    s = sign_vector(0, "k")
+    x = np.zeros((1, 128), dtype=np.float16)
+    x[0, 0] = np.float16(1.0 * s[0])
+    x[0, 1] = np.float16(1.0 * s[1])          # y_i = (H_i0 + H_i1)/sqrt(128): zero on every odd i
+    codes, n16 = codec.encode(x, s, codebooks[fmt])
+    K = len(codebooks[fmt])
+    y = codec.rotated_coordinates(x, s)[0]
+    assert np.all(y[1::2] == 0.0)
+    assert np.all(codes[0, 1::2] == K // 2 - 1)
+
+
+@pytest.mark.parametrize("fmt", ["turbo3", "turbo4"])
+def test_zero_group(fmt, codebooks):
+    codes, n16 = codec.encode(np.zeros((1, 128), dtype=np.float16), sign_vector(0, "v"), codebooks[fmt])
+    assert float(n16[0]) == 0.0 and np.all(codes == 0)
+    assert np.all(codec.dequant(codes, n16, codebooks[fmt], sign_vector(0, "v")) == 0.0)
+
+
+@pytest.mark.parametrize("fmt", ["turbo3", "turbo4"])
+def test_power_of_two_scaling_and_negation(fmt, codebooks):
+    rng = np.random.default_rng(3)
+    s = sign_vector(2, "k")
+    x = rng.standard_normal((64, 128)).astype(np.float16)
+    c1, n1 = codec.encode(x, s, codebooks[fmt])
+    c2, n2 = codec.encode((x.astype(np.float64) * 4).astype(np.float16), s, codebooks[fmt])
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(n2.astype(np.float64), 4 * n1.astype(np.float64))
+    c3, n3 = codec.encode(-x, s, codebooks[fmt])
+    np.testing.assert_array_equal(n3, n1)
+    np.testing.assert_array_equal(c3.astype(int), len(codebooks[fmt]) - 1 - c1.astype(int))
+
+
+@pytest.mark.parametrize("fmt,bits", [("turbo3", 3), ("turbo4", 4)])
+def test_reconstruction_error_matches_lloyd_max_mse(fmt, bits, codebooks):
+    rng = np.random.default_rng(4)
+    s = sign_vector(0, "v")
+    x = rng.standard_normal((4000, 128)).astype(np.float16)
+    codes, n16 = codec.encode(x, s, codebooks[fmt])
+    xh = codec.dequant(codes, n16, codebooks[fmt], s)
+    xf = x.astype(np.float64)
+    rel = np.sum((xf - xh) ** 2, axis=1) / np.sum(xf ** 2, axis=1)
+    want = mse_normal(codebooks[fmt].astype(np.float64) * np.sqrt(128))
+    assert abs(rel.mean() / want - 1) < 0.03
+
+
+@pytest.mark.parametrize("fmt,bound", [("turbo3", 1e-4), ("turbo4", 1e-4)])
+def test_boundary_margin_fraction(fmt, bound, codebooks):
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((20000, 128)).astype(np.float16)
+    frac = codec.boundary_margin(x, sign_vector(0, "k"), codebooks[fmt]).mean()
+    assert 0 < frac < bound
+
+
+# ----------------------------------------------------------------------------- layouts
+
+def _hex(b):
+    return bytes(np.asarray(b, dtype=np.uint8)).hex(" ")
+
+
+def test_sub3_hand_worked_bytes():
+    # all 32 codes = 5 (0b101): A,B bytes = 01|101|101 = 0x6D; C bytes = 1|1|101|101 = 0xED
+    assert _hex(codec.pack_sub3(np.full(32, 5))) == "6d 6d 6d 6d 6d 6d 6d 6d ed ed ed ed"
+    # element 25 = 6 (0b110): j = 1 -> A bits 14..15 = 0b10 (A = 0x8000), C bit 14 = 1 (C = 0x4000)
+    c = np.zeros(32, dtype=int)
+    c[25] = 6
+    assert _hex(codec.pack_sub3(c)) == "00 80 00 00 00 00 00 00 00 40 00 00"
+    # element 30 = 7: j = 2 -> B bits 22..23 = 0b11 (0x00C00000), C bit 23 = 1 (0x00800000)
+    c = np.zeros(32, dtype=int)
+    c[30] = 7
+    assert _hex(codec.pack_sub3(c)) == "00 00 00 00 00 00 c0 00 00 00 80 00"
+    # element 13 = 3: B bits 11..13 = 0b011 -> B = 0x1800
+    c = np.zeros(32, dtype=int)
+    c[13] = 3
+    assert _hex(codec.pack_sub3(c)) == "00 00 00 00 00 18 00 00 00 00 00 00"
+
+
+def test_oct4_hand_worked_bytes():
+    # ascending indices -> sign-magnitude nibbles: 0->F, 15->7, 7->8, 8->0, 1->E, 14->6, 9->1, 6->9
+    # low nibbles of bytes 0..3 = F,7,8,0 ; high nibbles = E,6,1,9
+    assert _hex(codec.pack_oct4(np.array([0, 15, 7, 8, 1, 14, 9, 6]))) == "ef 67 18 90"
+
+
+def test_turbo4_nibble_semantics(codebooks):
+    cb = codebooks["turbo4"].astype(np.float64)
+    for k in range(16):
+        nib = int(codec.turbo4_nibble(k))
+        assert bool(nib & 8) == (cb[k] < 0)
+        assert codec.turbo4_index(nib) == k
+    mags = sorted(range(8), key=lambda m: abs(cb[codec.turbo4_index(m)]))
+    assert mags == list(range(8))
+
+
+def test_v_tile_hand_worked_bytes():
+    # turbo4: token slot 21 = (g=1, i=5), dim 42 = (n=5, nb=2) -> chunk 21, word 2, high nibble of byte 1
+    # -> byte 21*32 + 8 + 1 = 681 holds nibble(10) = 2 << 4; all other codes 8 (nibble 0)
+    c = np.full((32, 128), 8)
+    c[21, 42] = 10
+    t = codec.pack_v_tiles(c, "turbo4")[0]
+    nz = np.nonzero(t)[0]
+    assert list(nz) == [681] and t[681] == 0x20
+    # turbo3: slot 2 = (g=0, i=2), dim 127 = (n=15, nb=7) -> chunk 15, element 58 = sub-block 1 element 26
+    # -> C word of that sub-block, bit 22 -> byte 15*24 + 12 + 8 + 2 = 382 = 0x40
+    c = np.zeros((32, 128), dtype=int)
+    c[2, 127] = 4
+    t = codec.pack_v_tiles(c, "turbo3")[0]
+    nz = np.nonzero(t)[0]
+    assert list(nz) == [382] and t[382] == 0x40
+
+
+def test_v_tile_slot_is_a_bijection():
+    slots = sorted(codec.v_tile_slot(g, i) for g in range(4) for i in range(8))
+    assert slots == list(range(32))
+
+
+def test_k_record_byte_positions():
+    # turbo3: dim 32q + e lives in sub-block q; turbo4: dim 8w + e lives in word w
+    for d in (0, 37, 95, 127):
+        c = np.zeros(128, dtype=int)
+        c[d] = 7
+        nz = np.nonzero(codec.pack_k_record(c, "turbo3"))[0]
+        assert all(12 * (d // 32) <= b < 12 * (d // 32) + 12 for b in nz)
+        c4 = np.full(128, 8)
+        c4[d] = 0
+        nz = np.nonzero(codec.pack_k_record(c4, "turbo4"))[0]
+        assert list(nz) == [4 * (d // 8) + (d % 8) % 4]
+
+
+@pytest.mark.parametrize("fmt,k", [("turbo3", 8), ("turbo4", 16)])
+def test_pack_round_trip_every_value_every_position(fmt, k):
+    rng = np.random.default_rng(5)
+    rows = []
+    for pos in range(128):
+        for v in range(k):
+            r = rng.integers(0, k, 128)
+            r[pos] = v
+            rows.append(r)
+    codes = np.array(rows)
+    np.testing.assert_array_equal(codec.unpack_k_record(codec.pack_k_record(codes, fmt), fmt), codes)
+    tiles = codes[:(len(codes) // 32) * 32]
+    np.testing.assert_array_equal(codec.unpack_v_tiles(codec.pack_v_tiles(tiles, fmt), fmt), tiles)
+    assert codec.pack_k_record(codes[:1], fmt).shape[-1] == codec.K_RECORD_BYTES[fmt]
+    assert codec.pack_v_tiles(codes[:32], fmt).shape[-1] == codec.V_TILE_BYTES[fmt]

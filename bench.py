@@ -1,0 +1,246 @@
+"""Benchmark of one decode step of the rotated-codec KV cache on one MI355X.
+
+A step is the whole hot path for one new token per sequence:
+  tq_encode_append (1 token) -> tq_rotate_q -> tq_decode_attention -> tq_inverse_rotate_out
+on seeded synthetic inputs of the Qwen2.5-7B-shaped layer (B=1, Hq=28, Hkv=4,
+head dim 128, 8192 visible tokens, turbo3 K and V) unless --workload says
+otherwise.  The cache is replicated into distinct HBM copies (>= 1 GiB in all)
+and the steps rotate through them, so every step streams its cache from HBM
+rather than from the 256 MB Infinity Cache (each copy stands for another layer
+of the model).  Steps are captured in a HIP graph and replayed, so host launch
+overhead is not in the timed region.
+
+Prints ONE JSON line.  value = KV token-heads per second of whole steps
+(visible tokens x KV heads / step time).  roofline = the decode call
+(split-K kernel + LSE combine) timed by HIP events on its stream, eagerly
+enqueued behind a GPU sleep so the calls run back to back: algorithmic packed
+K+V bytes per call / average call duration, against 8 TB/s.
+cpu_baseline = the float64 oracle (oracle/) doing the same step on a bounded
+sample, on the host cores.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized-KV decode attention: KV tokens/s/head + % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+BYTES_PER_TOKEN_HEAD = {"turbo3": 50, "turbo4": 66, "f16": 256}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3200)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--workload", type=int, default=1, help="workload index (0..4); default the 8K Qwen2.5-7B layer")
+    p.add_argument("--variant", type=int, default=0, help="decode kernel variant (0 default, 1 VALU, 2 MFMA)")
+    p.add_argument("--copies-gib", type=float, default=1.0, help="total size of the rotated cache copies")
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def algorithmic_bytes(w, lengths):
+    return int(sum(lengths)) * w.num_kv_heads * (BYTES_PER_TOKEN_HEAD[w.k_format] + BYTES_PER_TOKEN_HEAD[w.v_format])
+
+
+def clone_cache(master):
+    """A new Cache whose device buffers are copies of master's (distinct HBM)."""
+    import copy
+
+    import quantized_kv_cache_decode_amd as tq
+    c = copy.copy(master)
+    for name in ("k_data", "k_norms", "v_data", "v_norms", "seq_lens"):
+        t = getattr(master, name)
+        setattr(c, name, None if t is None else t.clone())
+    c.lengths = master.lengths.copy()
+    c._desc = tq.binding.tq_cache(
+        master.batch, master.num_kv_heads, 128, master.capacity, master._desc.k_format, master._desc.v_format,
+        c.k_data.data_ptr(), 0 if c.k_norms is None else c.k_norms.data_ptr(), c.v_data.data_ptr(),
+        c.v_norms.data_ptr(), c.seq_lens.data_ptr(), master.k_signs.data_ptr(), master.v_signs.data_ptr(),
+        master.k_codebook.data_ptr(), master.v_codebook.data_ptr())
+    return c
+
+
+def cache_bytes(c):
+    return sum(t.numel() * t.element_size() for t in (c.k_data, c.k_norms, c.v_data, c.v_norms) if t is not None)
+
+
+def cpu_baseline(w, seed, budget_s):
+    """The oracle doing the same step (append one token, full-dequant attention) on host cores."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import codec, reference
+    from synth import kv_slice, new_token_kv, queries, sign_vector
+    from tests.conftest import load_codebook
+    cbs = {"turbo3": load_codebook("turbo3"), "turbo4": load_codebook("turbo4")}
+    sk, sv = sign_vector(seed, "k"), sign_vector(seed, "v")
+    b = 0
+    L = int(w.context or 8192)
+    pre = L - 1
+    k16 = np.stack([kv_slice(w, seed, "k", b, h, pre) for h in range(w.num_kv_heads)])
+    v16 = np.stack([kv_slice(w, seed, "v", b, h, pre) for h in range(w.num_kv_heads)])
+    enc = reference.encode_sequence(k16, v16, w.k_format, w.v_format, sk, sv, cbs, capacity=((L + 31) // 32) * 32)
+    kn = np.stack([new_token_kv(w, seed, "k", b, h, 0) for h in range(w.num_kv_heads)])
+    vn = np.stack([new_token_kv(w, seed, "v", b, h, 0) for h in range(w.num_kv_heads)])
+    q = queries(w, seed)[b]
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        # append: encode the new token into slot L-1
+        if w.k_format == "f16":
+            enc["k_f16"][:, pre] = kn[:, 0]
+        else:
+            c, n = codec.encode(kn, sk, cbs[w.k_format])
+            enc["k_codes"][:, pre], enc["k_norms"][:, pre] = c[:, 0], n[:, 0]
+        c, n = codec.encode(vn, sv, cbs[w.v_format])
+        enc["v_codes"][:, pre], enc["v_norms"][:, pre] = c[:, 0], n[:, 0]
+        k_hat, v_hat = reference.dequant_sequence(enc, w.k_format, w.v_format, sk, sv, cbs, L)
+        reference.decode_sequence(q, k_hat, v_hat, L)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": steps * L * w.num_kv_heads / el,
+        "unit": "KV token-heads/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{steps} steps of sequence 0 of {w.name} (append 1 token + float64 full-dequant "
+                  f"attention over {L} tokens x {w.num_kv_heads} KV heads x {w.group} query heads each) "
+                  f"in {el:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode path is built and measured "
+              "on a single MI355X; sharding is described, not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    from synth import get_workload, new_token_kv
+    from tests import support as S
+    tq.load_library()
+    torch.cuda.set_device(0)
+    w = get_workload(args.workload)
+    seed = 0
+
+    # ---- setup (not timed): prefill L-1 tokens, append the step's token once
+    master, _, _, L, q_np = S.prefill_and_step(w, seed)
+    pre = (L - 1).astype(np.int32)
+    per_copy = cache_bytes(master)
+    n_copies = max(1, int(math.ceil(args.copies_gib * (1 << 30) / per_copy)))
+    caches = [master] + [clone_cache(master) for _ in range(n_copies - 1)]
+    kn = S.padded_tensor([np.stack([new_token_kv(w, seed, "k", b, h, 0) for h in range(w.num_kv_heads)])
+                          for b in range(w.batch)], 1)
+    vn = S.padded_tensor([np.stack([new_token_kv(w, seed, "v", b, h, 0) for h in range(w.num_kv_heads)])
+                          for b in range(w.batch)], 1)
+    q = torch.from_numpy(np.ascontiguousarray(q_np)).cuda()
+    B, Hq = w.batch, w.num_q_heads
+    q_rot = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+    out_rot = torch.empty_like(q_rot)
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    ws = torch.zeros(tq.tq_decode_workspace_size(master, Hq, L), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(128.0)
+    per_graph = n_copies
+
+    def step(i):
+        c = caches[i % n_copies]
+        tq.tq_encode_append(c, kn, vn, seq_lens_host=pre)
+        tq.tq_rotate_q(c, q, q_rot)
+        tq.tq_decode_attention(c, q_rot, scale, out_rot, ws, seq_lens_host=L, variant=args.variant)
+        tq.tq_inverse_rotate_out(c, out_rot, out)
+
+    use_graph = not args.no_graph
+    graph = None
+    if use_graph:
+        try:
+            for i in range(per_graph):       # warm the launch path outside capture
+                step(i)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(per_graph):
+                    step(i)
+        except Exception as e:  # pragma: no cover - reported, then eager timing
+            print(f"graph capture unavailable ({e!r}); timing eager launches", file=sys.stderr)
+            graph, use_graph = None, False
+
+    reps = max(1, args.steps // per_graph) if use_graph else 0
+    steps = reps * per_graph if use_graph else args.steps
+    warm_reps = max(1, args.warmup // per_graph) if use_graph else 0
+    if use_graph:
+        for _ in range(warm_reps):
+            graph.replay()
+    else:
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps, synchronised on both sides
+    t0 = time.perf_counter()
+    if use_graph:
+        for _ in range(reps):
+            graph.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    # ---- decode-call duration by HIP events on the launch stream.  Events cannot be
+    # recorded inside a captured graph here, so the calls are enqueued eagerly behind a
+    # GPU sleep long enough for the host to queue them all: they then run back to back
+    # and each event pair brackets exactly one call (split-K kernel + LSE combine).
+    call_ms = []
+    n_calls = min(per_graph, 512)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    torch.cuda._sleep(int(5e7))
+    for i in range(n_calls):
+        c = caches[i % n_copies]
+        ev[i][0].record()
+        tq.tq_decode_attention(c, q_rot, scale, out_rot, ws, seq_lens_host=L, variant=args.variant)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    token_heads = int(L.sum()) * w.num_kv_heads
+    value = token_heads / (ms_per_step * 1e-3)
+
+    alg = algorithmic_bytes(w, L)
+    dec_ms = float(np.mean(call_ms)) if call_ms else float("nan")
+    achieved = alg / (dec_ms * 1e-3) / 1e9 if call_ms else None
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
+            "kernel": "tq_decode_attention (split-K decode + LSE combine)", "call_us": dec_ms * 1e3,
+            "algorithmic_bytes_per_call": alg}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, seed, args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": value, "unit": "KV token-heads/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm_reps * per_graph if use_graph else args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8 codes, f32 accumulate" if args.variant != 2 else "u8 codes, f16 mfma, f32 accumulate",
+        "data": "synthetic (seeded; no model weights)",
+        "config": {"workload": w.name, "batch": w.batch, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads,
+                   "context_total": int(L.sum()), "k_format": w.k_format, "v_format": w.v_format,
+                   "cache_copies": n_copies, "graph": use_graph, "variant": args.variant},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

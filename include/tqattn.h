@@ -1,0 +1,186 @@
+/*
+ * libtqattn — single-token decode attention over a KV cache compressed with a
+ * rotated scalar codec, for AMD Instinct MI355X (gfx950).
+ *
+ * Codec (per 128-element head-dim group of one token and one KV head):
+ *   n   = fp16 L2 norm of the group (round to nearest even, saturating at 65504);
+ *   y   = H (s * x) / sqrt(128): Rademacher sign flip s, then orthonormal
+ *         Walsh-Hadamard H (natural Sylvester order);
+ *   idx = nearest fp16 codebook entry to y / n: 8 entries ("turbo3", 3 bits)
+ *         or 16 entries ("turbo4", 4 bits);
+ *   reconstruction x_hat = s * H (n * c[idx]) / sqrt(128).
+ * The pages this follows: turboquant_plus "SMEM Pre-Dequant Experiment"
+ * (section "What Would Actually Work", item 1: dequant is a table entry at the
+ * index times the group norm) and mlxcel PR #369 "route Turbo4Asym decode
+ * through dequant-SDPA" (section "Change": codes live in the WHT-rotated basis;
+ * fp16 K + 4-bit V is the asymmetric mode; attention runs in V's rotated basis
+ * and only the [B, Hq, D] output is inverse-rotated, by
+ * rotate(SDPA(q,k,v)) == SDPA(q,k,rotate(v))).
+ *
+ * Conventions shared by every call:
+ *   - Every data pointer is DEVICE memory owned by the caller; the library
+ *     allocates nothing and keeps no state between calls (apart from the
+ *     thread-local error string).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *     enqueued on it; nothing synchronises.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-OK status means nothing was launched.  TQ_EHIP means a launch
+ *     failed; tq_last_error() describes the last non-OK status of the calling
+ *     thread.
+ *   - Query head h attends KV head h / (num_q_heads / num_kv_heads)
+ *     (contiguous GQA groups).  Group sizes 1..16 are supported.
+ *   - Only tq_encode_append writes the cache; the other calls read it.
+ *
+ * Byte layouts (this library's own; the pages print none):
+ *   turbo4 octet word: 8 codes in one little-endian u32; code e (0..3) in bits
+ *     8e..8e+3, code e (4..7) in bits 8(e-4)+4..8(e-4)+7; each field is
+ *     sign-magnitude (bit 3 set for the 8 negative centroids, bits 0..2 the
+ *     magnitude rank, 0 = smallest |c|).
+ *   turbo3 sub-block: 32 three-bit ascending indices c[0..31] in 3 u32 words
+ *     A, B, C; for j = 0..3:
+ *       A[8j..8j+2]=c[j]    A[8j+3..8j+5]=c[4+j]  A[8j+6..8j+7]=c[24+j]&3
+ *       B[8j..8j+2]=c[8+j]  B[8j+3..8j+5]=c[12+j] B[8j+6..8j+7]=c[28+j]&3
+ *       C[8j..8j+2]=c[16+j] C[8j+3..8j+5]=c[20+j] C[8j+6]=c[24+j]>>2
+ *       C[8j+7]=c[28+j]>>2
+ *   K record (token-major): turbo3 48 bytes = 4 sub-blocks (dims 32q..32q+31);
+ *     turbo4 64 bytes = 16 octet words (dims 8w..8w+7).
+ *   V tile (32 tokens, token-tiled): 64 chunks; chunk 16g+n holds dims
+ *     8n..8n+7 of the 8 tokens in tile slots r = 16(i/4) + 4g + (i%4),
+ *     i = 0..7; chunk element 8*nb + i is dim 8n+nb of token slot r(g, i).
+ *     turbo3 chunk = 2 sub-blocks (24 bytes); turbo4 chunk = 8 octet words,
+ *     word nb = elements 8nb..8nb+7 (32 bytes).  Tile: 1536 / 2048 bytes.
+ */
+#ifndef TQATTN_H
+#define TQATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,        /* bad pointer, shape or value */
+  TQ_EUNSUPPORTED = 2,  /* head_dim != 128, group size > 16, unknown format */
+  TQ_ECAPACITY = 3,     /* an append would pass `capacity`, or a length exceeds it */
+  TQ_EWORKSPACE = 4,    /* workspace smaller than tq_decode_workspace_size() */
+  TQ_EHIP = 5           /* a HIP launch failed */
+} tq_status;
+
+typedef enum {
+  TQ_FMT_F16 = 0,       /* raw half-precision K (asymmetric mode only) */
+  TQ_FMT_TURBO3 = 3,    /* 3-bit codes + fp16 norm, 50 bytes per 128-group */
+  TQ_FMT_TURBO4 = 4     /* 4-bit codes + fp16 norm, 66 bytes per 128-group */
+} tq_format;
+
+/* The cache of one attention layer.  All pointers are device memory.
+ *   k_data   TURBO3/TURBO4: u8 [B][Hkv][capacity][48 | 64] K records;
+ *            F16: fp16 [B][Hkv][capacity][128].
+ *   k_norms  fp16 bits [B][Hkv][capacity]; NULL when k_format == TQ_FMT_F16.
+ *   v_data   u8 [B][Hkv][capacity/32][1536 | 2048] V tiles.
+ *   v_norms  fp16 bits [B][Hkv][capacity].
+ *   seq_lens int32 [B]: visible tokens per sequence (the cache "offset");
+ *            written by tq_encode_append, read by tq_decode_attention.
+ *   k_signs, v_signs   float [128] of +1/-1 (k_signs unused for F16 K).
+ *   k_codebook, v_codebook   fp16 bits, ascending, 8 (turbo3) or 16 (turbo4)
+ *            entries, symmetric (c[i] = -c[n-1-i]); k_codebook unused for F16 K.
+ * capacity must be a positive multiple of 32; head_dim must be 128. */
+typedef struct tq_cache {
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;
+  int32_t k_format;
+  int32_t v_format;
+  void* k_data;
+  uint16_t* k_norms;
+  void* v_data;
+  uint16_t* v_norms;
+  int32_t* seq_lens;
+  const float* k_signs;
+  const float* v_signs;
+  const uint16_t* k_codebook;
+  const uint16_t* v_codebook;
+} tq_cache;
+
+/* Encode new tokens and append them to each sequence
+ * (mlxcel PR #369, "Change": the cache update is the only mutation).
+ *   seq_lens_host  HOST int32 [B]: current visible length of each sequence.
+ *   k_new, v_new   device fp16 [B][Hkv][t_new][128] (token rows before encoding).
+ *   counts_host    HOST int32 [B] or NULL: sequence b appends its first
+ *                  n_b = counts_host[b] rows (0 <= n_b <= t_new); NULL means
+ *                  n_b = t_new for every sequence (the decode step's append).
+ * Rows go to slots seq_lens_host[b] .. +n_b-1 and the kernel sets
+ * cache->seq_lens[b] = seq_lens_host[b] + n_b.
+ * Symmetric K and every V: rotate, take the fp16 norm, pick the nearest
+ * centroid, pack (layouts above); F16 K rows are copied unchanged.  Norm and
+ * decisions are computed exactly (integer sum of squares, binary64 rotation).
+ * Sequences with n_b == 0 are left untouched.  Errors: TQ_ECAPACITY if
+ * seq_lens_host[b] + n_b > capacity for some b; TQ_EINVAL for NULL pointers,
+ * negative lengths or a count outside [0, t_new]. */
+tq_status tq_encode_append(const tq_cache* cache, const int32_t* seq_lens_host,
+                           const void* k_new, const void* v_new, int32_t t_new,
+                           const int32_t* counts_host, void* stream);
+
+/* Rotate queries into K's codec basis: q_rot = H (s_K * q) / sqrt(128)
+ * (mlxcel PR #369, "Change": symmetric modes rotate Q because K is stored
+ * rotated; the asymmetric fp16-K mode needs no Q rotation, and then q_rot = q).
+ *   q      device [B][num_q_heads][128], fp32 if q_is_fp32 else fp16 bits.
+ *   q_rot  device fp32 [B][num_q_heads][128]. */
+tq_status tq_rotate_q(const tq_cache* cache, const void* q, int32_t q_is_fp32,
+                      int32_t num_q_heads, float* q_rot, void* stream);
+
+/* Bytes of device workspace tq_decode_attention needs for these lengths
+ * (split-K partials).  seq_lens_host: HOST int32 [B].  Returns 0 on invalid
+ * arguments (see tq_last_error). */
+size_t tq_decode_workspace_size(const tq_cache* cache, int32_t num_q_heads,
+                                const int32_t* seq_lens_host);
+
+/* Decode attention of one new query token per sequence against every visible
+ * token, in V's rotated basis (mlxcel PR #369, "Change"; output of the full
+ * dequant-then-attend reference up to rounding, "Result"):
+ *   out_rot[b,h] = sum_t softmax_t(scale * q_rot[b,h] . k_t) * (n_V,t * c_V[idx_V,t])
+ * with k_t = n_K,t * c_K[idx_K,t] (symmetric) or the fp16 K row (F16).
+ * Split-K over the context with a per-sequence split count, then a
+ * log-sum-exp merge of the splits.
+ *   seq_lens_host  HOST int32 [B]; must equal cache->seq_lens (it sizes the
+ *                  launch; the kernels read the device lengths).
+ *   q_rot          device fp32 [B][num_q_heads][128] (from tq_rotate_q).
+ *   out_rot        device fp32 [B][num_q_heads][128]; a sequence of length 0
+ *                  gives zeros.
+ *   workspace      device, >= tq_decode_workspace_size() bytes.
+ * The cache is not modified. */
+tq_status tq_decode_attention(const tq_cache* cache, const int32_t* seq_lens_host,
+                              const float* q_rot, int32_t num_q_heads, float scale,
+                              float* out_rot, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Same as tq_decode_attention with an explicit kernel variant, for A/B
+ * comparison of kernel designs: 0 = default (fastest), 1 = plain VALU
+ * reference kernel, 2 = MFMA kernel.  Unknown variants give TQ_EINVAL. */
+tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_lens_host,
+                                      const float* q_rot, int32_t num_q_heads, float scale,
+                                      float* out_rot, void* workspace, size_t workspace_bytes,
+                                      int32_t variant, void* stream);
+
+/* Back to the original basis: out = s_V * H (out_rot) / sqrt(128), rounded to
+ * nearest-even fp16 (mlxcel PR #369, "Change": only the small [B, Hq, D]
+ * output is inverse-rotated).
+ *   out_rot  device fp32 [B][num_q_heads][128];  out  device fp16 bits, same shape. */
+tq_status tq_inverse_rotate_out(const tq_cache* cache, const float* out_rot,
+                                int32_t num_q_heads, uint16_t* out, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* tq_last_error(void);
+
+/* Library version string. */
+const char* tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQATTN_H */

@@ -1,0 +1,191 @@
+"""Thin ctypes binding of libtqattn: argument marshalling only.
+
+Every function has the C ABI's name and forwards device pointers
+(torch tensors' data_ptr()) and the current HIP stream.  All arithmetic of the
+decode path runs in the library's kernels; torch provides device memory and
+streams.  Importing works without a GPU; calling a compute entry point needs
+the built library and a GPU, and fails loudly otherwise.
+"""
+import ctypes
+import json
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtqattn.so")
+TABLE_PATH = os.path.join(HERE, "tables", "codebooks.json")
+
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_ECAPACITY, TQ_EWORKSPACE, TQ_EHIP = range(6)
+TQ_FMT = {"f16": 0, "turbo3": 3, "turbo4": 4}
+K_RECORD_BYTES = {"turbo3": 48, "turbo4": 64}
+V_TILE_BYTES = {"turbo3": 1536, "turbo4": 2048}
+EXPORTED = (
+    "tq_encode_append", "tq_rotate_q", "tq_decode_workspace_size", "tq_decode_attention",
+    "tq_decode_attention_variant", "tq_inverse_rotate_out", "tq_last_error", "tq_version",
+)
+
+
+class TqError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"libtqattn status {status}: {message}")
+        self.status = status
+
+
+class tq_cache(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("capacity", ctypes.c_int32), ("k_format", ctypes.c_int32), ("v_format", ctypes.c_int32),
+        ("k_data", ctypes.c_void_p), ("k_norms", ctypes.c_void_p), ("v_data", ctypes.c_void_p),
+        ("v_norms", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p), ("k_signs", ctypes.c_void_p),
+        ("v_signs", ctypes.c_void_p), ("k_codebook", ctypes.c_void_p), ("v_codebook", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libtqattn.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is missing: build it with `python -m quantized_kv_cache_decode_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    cp = ctypes.POINTER(tq_cache)
+    lib.tq_encode_append.argtypes = [cp, P, P, P, I32, P, P]
+    lib.tq_rotate_q.argtypes = [cp, P, I32, I32, P, P]
+    lib.tq_decode_workspace_size.argtypes = [cp, I32, P]
+    lib.tq_decode_workspace_size.restype = SZ
+    lib.tq_decode_attention.argtypes = [cp, P, P, I32, F32, P, P, SZ, P]
+    lib.tq_decode_attention_variant.argtypes = [cp, P, P, I32, F32, P, P, SZ, I32, P]
+    lib.tq_inverse_rotate_out.argtypes = [cp, P, I32, P, P]
+    lib.tq_last_error.restype = ctypes.c_char_p
+    lib.tq_version.restype = ctypes.c_char_p
+    for name in ("tq_encode_append", "tq_rotate_q", "tq_decode_attention", "tq_decode_attention_variant",
+                 "tq_inverse_rotate_out"):
+        getattr(lib, name).restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def codebook_bits(fmt: str) -> np.ndarray:
+    """Frozen fp16 codebook (uint16 bit patterns, ascending) of a quantised format."""
+    with open(TABLE_PATH) as f:
+        t = json.load(f)
+    return np.array([int(h, 16) for h in t[fmt]["codebook_fp16_hex"]], dtype=np.uint16)
+
+
+def _check(status):
+    if status != TQ_OK:
+        raise TqError(status, load_library().tq_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _host_i32(lengths):
+    arr = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+class Cache:
+    """Device buffers of one layer's KV cache (torch tensors) and their C descriptor.
+
+    k_format: "turbo3" | "turbo4" | "f16"; v_format: "turbo3" | "turbo4".
+    `lengths` is the host copy of the visible length per sequence; it is advanced
+    by tq_encode_append together with the device copy."""
+
+    def __init__(self, batch, num_kv_heads, capacity, k_format, v_format, k_signs, v_signs, device="cuda"):
+        import torch
+        if capacity % 32:
+            raise ValueError("capacity must be a multiple of 32")
+        self.batch, self.num_kv_heads, self.capacity = batch, num_kv_heads, capacity
+        self.k_format, self.v_format = k_format, v_format
+        dev = torch.device(device)
+        slots = (batch, num_kv_heads, capacity)
+        if k_format == "f16":
+            self.k_data = torch.zeros(slots + (128,), dtype=torch.float16, device=dev)
+            self.k_norms = None
+        else:
+            self.k_data = torch.zeros(slots + (K_RECORD_BYTES[k_format],), dtype=torch.uint8, device=dev)
+            self.k_norms = torch.zeros(slots, dtype=torch.int16, device=dev)
+        self.v_data = torch.zeros((batch, num_kv_heads, capacity // 32, V_TILE_BYTES[v_format]),
+                                  dtype=torch.uint8, device=dev)
+        self.v_norms = torch.zeros(slots, dtype=torch.int16, device=dev)
+        self.seq_lens = torch.zeros(batch, dtype=torch.int32, device=dev)
+        self.k_signs = torch.as_tensor(np.asarray(k_signs, dtype=np.float32)).to(dev)
+        self.v_signs = torch.as_tensor(np.asarray(v_signs, dtype=np.float32)).to(dev)
+        cbk = codebook_bits(k_format) if k_format != "f16" else np.zeros(16, np.uint16)
+        self.k_codebook = torch.as_tensor(cbk.view(np.int16).copy()).to(dev)
+        self.v_codebook = torch.as_tensor(codebook_bits(v_format).view(np.int16).copy()).to(dev)
+        self.lengths = np.zeros(batch, dtype=np.int32)
+        self._desc = tq_cache(
+            batch, num_kv_heads, 128, capacity, TQ_FMT[k_format], TQ_FMT[v_format],
+            self.k_data.data_ptr(), 0 if self.k_norms is None else self.k_norms.data_ptr(),
+            self.v_data.data_ptr(), self.v_norms.data_ptr(), self.seq_lens.data_ptr(),
+            self.k_signs.data_ptr(), self.v_signs.data_ptr(), self.k_codebook.data_ptr(),
+            self.v_codebook.data_ptr())
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+    def set_lengths(self, lengths):
+        """Set the visible length of every sequence (host and device copies)."""
+        import torch
+        self.lengths = np.asarray(lengths, dtype=np.int32).copy()
+        self.seq_lens.copy_(torch.as_tensor(self.lengths))
+
+
+def tq_encode_append(cache: Cache, k_new, v_new, seq_lens_host=None, counts=None, stream=None):
+    """Append fp16 rows k_new, v_new [B, Hkv, t_new, 128] at each sequence's current length.
+
+    counts: optional per-sequence number of rows to take (ragged prefill)."""
+    t_new = int(k_new.shape[2])
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
+    if counts is None:
+        cnt, pc = np.full(cache.batch, t_new, dtype=np.int32), ctypes.c_void_p(0)
+    else:
+        cnt, pc = _host_i32(counts)
+    _check(load_library().tq_encode_append(cache.desc, p, _ptr(k_new), _ptr(v_new), t_new, pc, _stream(stream)))
+    cache.lengths = arr + cnt
+
+
+def tq_rotate_q(cache: Cache, q, q_rot, stream=None):
+    """q [B, Hq, 128] (fp16 or fp32) -> q_rot fp32 in K's codec basis."""
+    import torch
+    _check(load_library().tq_rotate_q(cache.desc, _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]),
+                                      _ptr(q_rot), _stream(stream)))
+
+
+def tq_decode_workspace_size(cache: Cache, num_q_heads: int, seq_lens_host=None) -> int:
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
+    n = load_library().tq_decode_workspace_size(cache.desc, num_q_heads, p)
+    if n == 0:
+        raise TqError(TQ_EINVAL, load_library().tq_last_error().decode())
+    return int(n)
+
+
+def tq_decode_attention(cache: Cache, q_rot, scale, out_rot, workspace, seq_lens_host=None, variant=0,
+                        stream=None):
+    """out_rot [B, Hq, 128] fp32 = decode attention in V's rotated basis (workspace: device uint8)."""
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
+    _check(load_library().tq_decode_attention_variant(
+        cache.desc, p, _ptr(q_rot), int(q_rot.shape[1]), float(scale), _ptr(out_rot), _ptr(workspace),
+        int(workspace.numel() * workspace.element_size()), int(variant), _stream(stream)))
+
+
+def tq_inverse_rotate_out(cache: Cache, out_rot, out, stream=None):
+    """out_rot fp32 [B, Hq, 128] -> out fp16 [B, Hq, 128] in the original basis."""
+    _check(load_library().tq_inverse_rotate_out(cache.desc, _ptr(out_rot), int(out_rot.shape[1]), _ptr(out),
+                                                _stream(stream)))

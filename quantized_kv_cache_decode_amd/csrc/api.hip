@@ -1,0 +1,232 @@
+// C ABI of libtqattn: argument validation, split planning and kernel launches.
+// Everything is validated on the host before the first launch; see include/tqattn.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/tqattn.h"
+#include "tq_device.h"
+#include "tq_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tq_status fail(tq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+tq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TQ_OK;
+  return fail(TQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_turbo(int f) { return f == TQ_FMT_TURBO3 || f == TQ_FMT_TURBO4; }
+
+tq_status check_cache(const tq_cache* c) {
+  if (!c) return fail(TQ_EINVAL, "cache is NULL");
+  if (c->head_dim != 128) return fail(TQ_EUNSUPPORTED, "head_dim %d: only 128 is supported", c->head_dim);
+  if (c->batch <= 0 || c->num_kv_heads <= 0) return fail(TQ_EINVAL, "batch and num_kv_heads must be positive");
+  if (c->capacity <= 0 || c->capacity % 32) return fail(TQ_EINVAL, "capacity %d must be a positive multiple of 32", c->capacity);
+  if (!is_turbo(c->v_format)) return fail(TQ_EUNSUPPORTED, "v_format %d: must be TURBO3 or TURBO4", c->v_format);
+  if (!is_turbo(c->k_format) && c->k_format != TQ_FMT_F16)
+    return fail(TQ_EUNSUPPORTED, "k_format %d: must be F16, TURBO3 or TURBO4", c->k_format);
+  if (!c->k_data || !c->v_data || !c->v_norms || !c->seq_lens || !c->v_signs || !c->v_codebook)
+    return fail(TQ_EINVAL, "NULL cache pointer");
+  if (is_turbo(c->k_format) && (!c->k_norms || !c->k_signs || !c->k_codebook))
+    return fail(TQ_EINVAL, "NULL K norm/sign/codebook pointer for a quantised K format");
+  const long long slots = (long long)c->batch * c->num_kv_heads * c->capacity;
+  if (slots * 128 > (1LL << 46)) return fail(TQ_EINVAL, "cache too large");
+  return TQ_OK;
+}
+
+tq_status check_heads(const tq_cache* c, int32_t num_q_heads) {
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads)
+    return fail(TQ_EINVAL, "num_q_heads %d must be a positive multiple of num_kv_heads %d", num_q_heads,
+                c->num_kv_heads);
+  if (num_q_heads / c->num_kv_heads > tq::kMaxGroup)
+    return fail(TQ_EUNSUPPORTED, "group size %d > %d", num_q_heads / c->num_kv_heads, tq::kMaxGroup);
+  return TQ_OK;
+}
+
+tq_status check_lengths(const tq_cache* c, const int32_t* lens, int32_t extra) {
+  if (!lens) return fail(TQ_EINVAL, "seq_lens_host is NULL");
+  for (int b = 0; b < c->batch; ++b) {
+    if (lens[b] < 0) return fail(TQ_EINVAL, "seq_lens_host[%d] = %d is negative", b, lens[b]);
+    if ((long long)lens[b] + extra > c->capacity)
+      return fail(TQ_ECAPACITY, "sequence %d: %d + %d tokens exceed capacity %d", b, lens[b], extra, c->capacity);
+  }
+  return TQ_OK;
+}
+
+// Split plan shared by the workspace query and the launch.  About 2048 work
+// items over the chip (8 per CU), each a multiple of 256 tokens.  Once the call
+// is bandwidth-bound (>= 4M token-heads) the chunk is also kept long enough that
+// the partials (G x 130 floats, written then read) stay under ~4% of the packed
+// bytes of the chunk.
+tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
+  long long total = 0;
+  int lmax = 0;
+  for (int b = 0; b < c->batch; ++b) {
+    total += (long long)lens[b] * c->num_kv_heads;
+    lmax = std::max(lmax, (int)lens[b]);
+  }
+  long long chunk = (total + 2047) / 2048;
+  if (total >= (4LL << 20)) chunk = std::max(chunk, 260LL * group);
+  chunk = std::max(256LL, (chunk + 255) / 256 * 256);
+  tq::DecodePlan p;
+  p.chunk = (int)chunk;
+  p.max_splits = std::max(1, (int)((lmax + chunk - 1) / chunk));
+  return p;
+}
+
+size_t workspace_bytes(const tq_cache* c, int32_t num_q_heads, const tq::DecodePlan& p) {
+  const size_t items = (size_t)c->batch * c->num_kv_heads * p.max_splits;
+  const size_t g = num_q_heads / c->num_kv_heads;
+  return items * g * (128 + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_last_error(void) { return g_err; }
+
+const char* tq_version(void) { return "libtqattn 0.1 (gfx950)"; }
+
+tq_status tq_encode_append(const tq_cache* cache, const int32_t* seq_lens_host, const void* k_new,
+                           const void* v_new, int32_t t_new, const int32_t* counts_host, void* stream) {
+  tq_status st = check_cache(cache);
+  if (st != TQ_OK) return st;
+  if (t_new < 0) return fail(TQ_EINVAL, "t_new %d is negative", t_new);
+  if ((st = check_lengths(cache, seq_lens_host, 0)) != TQ_OK) return st;
+  for (int b = 0; b < cache->batch; ++b) {
+    const int n = counts_host ? counts_host[b] : t_new;
+    if (n < 0 || n > t_new) return fail(TQ_EINVAL, "counts_host[%d] = %d outside [0, %d]", b, n, t_new);
+    if ((long long)seq_lens_host[b] + n > cache->capacity)
+      return fail(TQ_ECAPACITY, "sequence %d: %d + %d tokens exceed capacity %d", b, seq_lens_host[b], n,
+                  cache->capacity);
+  }
+  if (t_new == 0) return TQ_OK;
+  if (!k_new || !v_new) return fail(TQ_EINVAL, "k_new / v_new is NULL");
+  tq::EncodeArgs a;
+  a.hkv = cache->num_kv_heads;
+  a.cap = cache->capacity;
+  a.kfmt = cache->k_format;
+  a.vfmt = cache->v_format;
+  a.t_new = t_new;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_data = static_cast<uint8_t*>(cache->k_data);
+  a.k_norms = cache->k_norms;
+  a.v_data = static_cast<uint8_t*>(cache->v_data);
+  a.v_norms = cache->v_norms;
+  a.seq_lens = cache->seq_lens;
+  a.k_signs = cache->k_signs;
+  a.v_signs = cache->v_signs;
+  a.k_cb = cache->k_codebook;
+  a.v_cb = cache->v_codebook;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int b0 = 0; b0 < cache->batch; b0 += tq::kAppendChunk) {
+    const int nb = std::min(tq::kAppendChunk, cache->batch - b0);
+    tq::AppendStarts starts;
+    memset(&starts, 0, sizeof(starts));
+    int max_tiles = 0;
+    for (int i = 0; i < nb; ++i) {
+      const int st0 = seq_lens_host[b0 + i];
+      const int n = counts_host ? counts_host[b0 + i] : t_new;
+      starts.start[i] = st0;
+      starts.count[i] = n;
+      if (n > 0) max_tiles = std::max(max_tiles, (st0 + n - 1) / 32 - st0 / 32 + 1);
+    }
+    if (max_tiles == 0) continue;
+    a.b0 = b0;
+    st = hip_status(tq::launch_encode_append(a, starts, nb, max_tiles, s), "encode_append launch");
+    if (st != TQ_OK) return st;
+  }
+  return TQ_OK;
+}
+
+tq_status tq_rotate_q(const tq_cache* cache, const void* q, int32_t q_is_fp32, int32_t num_q_heads,
+                      float* q_rot, void* stream) {
+  tq_status st = check_cache(cache);
+  if (st != TQ_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != TQ_OK) return st;
+  if (!q || !q_rot) return fail(TQ_EINVAL, "q / q_rot is NULL");
+  const bool rotate = cache->k_format != TQ_FMT_F16;
+  return hip_status(tq::launch_rotate_q(q, q_is_fp32 != 0, rotate, cache->k_signs, q_rot,
+                                        cache->batch * num_q_heads, static_cast<hipStream_t>(stream)),
+                    "rotate_q launch");
+}
+
+size_t tq_decode_workspace_size(const tq_cache* cache, int32_t num_q_heads, const int32_t* seq_lens_host) {
+  if (check_cache(cache) != TQ_OK || check_heads(cache, num_q_heads) != TQ_OK ||
+      check_lengths(cache, seq_lens_host, 0) != TQ_OK)
+    return 0;
+  return workspace_bytes(cache, num_q_heads, make_plan(cache, seq_lens_host, num_q_heads / cache->num_kv_heads));
+}
+
+tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_lens_host, const float* q_rot,
+                                      int32_t num_q_heads, float scale, float* out_rot, void* workspace,
+                                      size_t ws_bytes, int32_t variant, void* stream) {
+  tq_status st = check_cache(cache);
+  if (st != TQ_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != TQ_OK) return st;
+  if ((st = check_lengths(cache, seq_lens_host, 0)) != TQ_OK) return st;
+  if (!q_rot || !out_rot) return fail(TQ_EINVAL, "q_rot / out_rot is NULL");
+  if (variant < 0 || variant > 2) return fail(TQ_EINVAL, "unknown decode variant %d", variant);
+  const tq::DecodePlan plan = make_plan(cache, seq_lens_host, num_q_heads / cache->num_kv_heads);
+  const size_t need = workspace_bytes(cache, num_q_heads, plan);
+  if (!workspace || ws_bytes < need)
+    return fail(TQ_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  tq::DecodeArgs a;
+  a.hkv = cache->num_kv_heads;
+  a.cap = cache->capacity;
+  a.kfmt = cache->k_format;
+  a.vfmt = cache->v_format;
+  a.group = num_q_heads / cache->num_kv_heads;
+  a.scale = scale;
+  a.plan = plan;
+  a.k_data = static_cast<const uint8_t*>(cache->k_data);
+  a.k_norms = cache->k_norms;
+  a.v_data = static_cast<const uint8_t*>(cache->v_data);
+  a.v_norms = cache->v_norms;
+  a.seq_lens = cache->seq_lens;
+  a.k_cb = cache->k_codebook;
+  a.v_cb = cache->v_codebook;
+  a.q_rot = q_rot;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = a.part_o + (size_t)cache->batch * cache->num_kv_heads * plan.max_splits * a.group * 128;
+  a.out_rot = out_rot;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = (variant == 2) ? tq::launch_decode_mfma(a, cache->batch, s)
+                                : tq::launch_decode_reference(a, cache->batch, s);
+  if ((st = hip_status(e, "decode launch")) != TQ_OK) return st;
+  return hip_status(tq::launch_combine(a, cache->batch, s), "combine launch");
+}
+
+tq_status tq_decode_attention(const tq_cache* cache, const int32_t* seq_lens_host, const float* q_rot,
+                              int32_t num_q_heads, float scale, float* out_rot, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  return tq_decode_attention_variant(cache, seq_lens_host, q_rot, num_q_heads, scale, out_rot, workspace, ws_bytes,
+                                     0, stream);
+}
+
+tq_status tq_inverse_rotate_out(const tq_cache* cache, const float* out_rot, int32_t num_q_heads, uint16_t* out,
+                                void* stream) {
+  tq_status st = check_cache(cache);
+  if (st != TQ_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != TQ_OK) return st;
+  if (!out_rot || !out) return fail(TQ_EINVAL, "out_rot / out is NULL");
+  return hip_status(tq::launch_inverse_rotate(out_rot, cache->v_signs, out, cache->batch * num_q_heads,
+                                              static_cast<hipStream_t>(stream)),
+                    "inverse_rotate launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Device-side constants and bit-layout helpers shared by the libtqattn kernels.
+// Layouts are described in include/tqattn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int kDim = 128;
+constexpr int kTileTokens = 32;
+constexpr int kMaxGroup = 16;
+constexpr int kFmtF16 = 0;
+constexpr int kFmtTurbo3 = 3;
+constexpr int kFmtTurbo4 = 4;
+
+__host__ __device__ constexpr int k_record_bytes(int fmt) { return fmt == kFmtTurbo3 ? 48 : 64; }
+__host__ __device__ constexpr int v_chunk_bytes(int fmt) { return fmt == kFmtTurbo3 ? 24 : 32; }
+__host__ __device__ constexpr int v_tile_bytes(int fmt) { return 64 * v_chunk_bytes(fmt); }
+__host__ __device__ constexpr int levels(int fmt) { return fmt == kFmtTurbo3 ? 8 : 16; }
+
+// V tile: token slot r (0..31) <-> (slot group g = 0..3, element-token i = 0..7),
+// r = 16*(i/4) + 4*g + (i%4).
+__host__ __device__ inline int slot_group(int r) { return (r & 15) >> 2; }
+__host__ __device__ inline int slot_elem(int r) { return ((r >> 4) << 2) | (r & 3); }
+__host__ __device__ inline int slot_of(int g, int i) { return ((i >> 2) << 4) | (g << 2) | (i & 3); }
+
+// ---- turbo3 sub-block: 32 three-bit codes in words w[0..2] (A, B, C).
+__host__ __device__ inline uint32_t sub3_get(const uint32_t* w, int e) {
+  const int j = e & 3;
+  if (e < 24) return (w[e >> 3] >> (8 * j + ((e >> 2) & 1) * 3)) & 7u;
+  const int word = e >= 28 ? 1 : 0;
+  const uint32_t lo = (w[word] >> (8 * j + 6)) & 3u;
+  const uint32_t hi = (w[2] >> (8 * j + 6 + word)) & 1u;
+  return lo | (hi << 2);
+}
+
+__host__ __device__ inline void sub3_pack(const uint8_t* c, uint32_t* w) {
+  uint32_t a = 0, b = 0, cc = 0;
+  for (int j = 0; j < 4; ++j) {
+    a |= (uint32_t(c[j]) & 7u) << (8 * j);
+    a |= (uint32_t(c[4 + j]) & 7u) << (8 * j + 3);
+    a |= (uint32_t(c[24 + j]) & 3u) << (8 * j + 6);
+    b |= (uint32_t(c[8 + j]) & 7u) << (8 * j);
+    b |= (uint32_t(c[12 + j]) & 7u) << (8 * j + 3);
+    b |= (uint32_t(c[28 + j]) & 3u) << (8 * j + 6);
+    cc |= (uint32_t(c[16 + j]) & 7u) << (8 * j);
+    cc |= (uint32_t(c[20 + j]) & 7u) << (8 * j + 3);
+    cc |= ((uint32_t(c[24 + j]) >> 2) & 1u) << (8 * j + 6);
+    cc |= ((uint32_t(c[28 + j]) >> 2) & 1u) << (8 * j + 7);
+  }
+  w[0] = a;
+  w[1] = b;
+  w[2] = cc;
+}
+
+// ---- turbo4 octet word: 8 sign-magnitude nibbles.
+__host__ __device__ inline int oct4_bit(int e) { return e < 4 ? 8 * e : 8 * (e - 4) + 4; }
+__host__ __device__ inline uint32_t oct4_get_nibble(uint32_t w, int e) { return (w >> oct4_bit(e)) & 15u; }
+__host__ __device__ inline uint32_t t4_index_of_nibble(uint32_t nib) {
+  return (nib & 8u) ? 7u - (nib & 7u) : 8u + (nib & 7u);
+}
+__host__ __device__ inline uint32_t t4_nibble_of_index(uint32_t k) { return k >= 8u ? k - 8u : (8u | (7u - k)); }
+
+__host__ __device__ inline uint32_t oct4_pack(const uint8_t* idx) {
+  uint32_t w = 0;
+  for (int e = 0; e < 8; ++e) w |= t4_nibble_of_index(idx[e]) << oct4_bit(e);
+  return w;
+}
+
+__device__ inline float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+}  // namespace tq

@@ -1,0 +1,71 @@
+// Host-side launchers of the libtqattn kernels (one translation unit per kernel family).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+// ---- encode / append
+constexpr int kAppendChunk = 256;  // sequences per encode launch (start offsets travel as kernel arguments)
+
+struct EncodeArgs {
+  int hkv, cap, kfmt, vfmt, t_new, b0;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* k_data;
+  uint16_t* k_norms;
+  uint8_t* v_data;
+  uint16_t* v_norms;
+  int32_t* seq_lens;
+  const float* k_signs;
+  const float* v_signs;
+  const uint16_t* k_cb;
+  const uint16_t* v_cb;
+};
+
+struct AppendStarts {
+  int32_t start[kAppendChunk];  // first slot written, per sequence of the launch
+  int32_t count[kAppendChunk];  // rows appended, per sequence of the launch
+};
+
+hipError_t launch_encode_append(const EncodeArgs& a, const AppendStarts& starts, int nb, int max_tiles,
+                                hipStream_t stream);
+
+// ---- rotations
+hipError_t launch_rotate_q(const void* q, bool q_fp32, bool rotate, const float* signs, float* q_rot, int rows,
+                           hipStream_t stream);
+hipError_t launch_inverse_rotate(const float* o_rot, const float* signs, uint16_t* out, int rows,
+                                 hipStream_t stream);
+
+// ---- decode
+// Split plan: sequence b is cut into ceil(L_b / chunk) splits of `chunk` tokens
+// (at most max_splits; the last split takes the remainder).  Partials of split
+// s of (b, kv head h) live at index ((b*hkv + h)*max_splits + s).
+struct DecodePlan {
+  int chunk;
+  int max_splits;
+};
+
+struct DecodeArgs {
+  int hkv, cap, kfmt, vfmt, group;
+  float scale;
+  DecodePlan plan;
+  const uint8_t* k_data;
+  const uint16_t* k_norms;
+  const uint8_t* v_data;
+  const uint16_t* v_norms;
+  const int32_t* seq_lens;
+  const uint16_t* k_cb;
+  const uint16_t* v_cb;
+  const float* q_rot;       // [B][Hq][128]
+  float* part_o;            // [B*Hkv*max_splits][group][128]
+  float* part_ml;           // [B*Hkv*max_splits][group][2]
+  float* out_rot;           // [B][Hq][128]
+};
+
+hipError_t launch_decode_reference(const DecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs& a, int batch, hipStream_t stream);
+
+}  // namespace tq

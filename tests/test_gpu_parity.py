@@ -1,0 +1,223 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: packed codes and fp16 norms bit-exact (codes within 1e-5 of a decision
+threshold excluded and counted, at most 1e-4 of all codes); decode outputs
+(fp16) within relative-L2 1e-3 and max-abs 5e-3 of the oracle's unrounded
+float64 output.  Decode parity is checked twice: (i) on the GPU-written bytes
+(unpacked by the oracle), (ii) end to end from the same fp16 inputs.
+"""
+import hashlib
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import codec, reference
+from oracle.hadamard import inverse_rotate, rotate
+from synth import get_workload, queries, sign_vector
+from tests import support as S
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = [1]
+
+
+def _say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_kv_cache_decode_amd as tq
+    tq.load_library()     # raises if the library is missing: no silent fallback
+
+
+# ----------------------------------------------------------------------------- rotations
+
+@pytest.mark.parametrize("q_fp32", [False, True])
+@pytest.mark.parametrize("k_format", ["turbo3", "f16"])
+def test_rotate_q(q_fp32, k_format):
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    w = S.scaled(get_workload(1), k_format=k_format, v_format="turbo4" if k_format == "f16" else "turbo3")
+    cache = S.make_cache(w, 32)
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((1, 28, 128)).astype(np.float32 if q_fp32 else np.float16)
+    qt = torch.from_numpy(q).cuda()
+    q_rot = torch.empty((1, 28, 128), dtype=torch.float32, device="cuda")
+    tq.tq_rotate_q(cache, qt, q_rot)
+    got = q_rot.cpu().numpy().astype(np.float64)
+    want = rotate(q.astype(np.float64), sign_vector(0, "k")) if k_format != "f16" else q.astype(np.float64)
+    assert np.abs(got - want).max() <= 1e-5 * np.abs(want).max()
+
+
+def test_inverse_rotate_out():
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    cache = S.make_cache(S.scaled(get_workload(0), batch=3), 32)
+    rng = np.random.default_rng(1)
+    o = rng.standard_normal((3, 4, 128)).astype(np.float32)
+    out = torch.empty((3, 4, 128), dtype=torch.float16, device="cuda")
+    tq.tq_inverse_rotate_out(cache, torch.from_numpy(o).cuda(), out)
+    got = out.cpu().numpy().astype(np.float64)
+    want = inverse_rotate(o.astype(np.float64), sign_vector(0, "v"))
+    # fp32 butterflies then one rounding to fp16: within one fp16 ulp of the exact value
+    ulp = np.spacing(np.abs(want).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(got - want) <= ulp)
+    assert np.mean(got == want.astype(np.float16).astype(np.float64)) > 0.99
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def _small_workloads():
+    return {
+        "c0": (get_workload(0), None),
+        "c1": (get_workload(1), None),
+        "c2": (get_workload(2), None),
+        "c3s": (S.scaled(get_workload(3), batch=3, context=2048), None),
+        "c4s": (S.scaled(get_workload(4), batch=6, context=None, ragged_range=(1, 3000)),
+                np.array([1, 31, 33, 2049, 700, 2999])),
+    }
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3s", "c4s"])
+def test_encode_bit_exact(name, codebooks):
+    w, lens = _small_workloads()[name]
+    cache, k_list, v_list, L, _ = S.prefill_and_step(w, lengths=lens)
+    np.testing.assert_array_equal(cache.seq_lens.cpu().numpy(), L)
+    mism = margin = total = 0
+    for b in range(w.batch):
+        m, g, t = S.compare_codes(cache, b, k_list[b], v_list[b], int(L[b]), w, codebooks)
+        mism, margin, total = mism + m, margin + g, total + t
+    _say(f"[{name}] code mismatches {mism} / {total}; within 1e-5 of a threshold {margin}")
+    assert margin <= 1e-4 * total
+    assert mism <= margin
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3s", "c4s"])
+def test_decode_parity(name, variant, codebooks):
+    w, lens = _small_workloads()[name]
+    cache, k_list, v_list, L, q = S.prefill_and_step(w, lengths=lens)
+    got = S.gpu_decode(cache, q, variant=variant)
+    worst = (0.0, 0.0)
+    for b in range(w.batch):
+        on_bytes = S.oracle_on_bytes(cache, b, int(L[b]), q[b], codebooks)
+        e2e = S.oracle_end_to_end(w, k_list[b], v_list[b], int(L[b]), q[b], codebooks)
+        r1 = S.assert_close(got[b], on_bytes, f"{name} b={b} on GPU bytes")
+        r2 = S.assert_close(got[b], e2e, f"{name} b={b} end to end")
+        worst = tuple(max(x) for x in zip(worst, r1, r2))
+    _say(f"[{name} v{variant}] worst rel-L2 {worst[0]:.2e} max-abs {worst[1]:.2e}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_sixteen_decode_steps_gqa_4_over_2(variant, codebooks):
+    """The parity shape of mlxcel PR #369 ("Result"): GQA 4 query heads over 2 KV heads,
+    16 successive decode steps, each compared with the full-dequant reference, and the
+    visible offset advancing by exactly one token per append."""
+    import quantized_kv_cache_decode_amd as tq
+    from synth import kv_slice, new_token_kv
+    w = get_workload(0)
+    pre = 240
+    k = [np.stack([kv_slice(w, 0, "k", 0, h, pre) for h in range(2)])]
+    v = [np.stack([kv_slice(w, 0, "v", 0, h, pre) for h in range(2)])]
+    cache = S.encode_on_gpu(w, k, v, [pre], 256)
+    for step in range(16):
+        kn = np.stack([new_token_kv(w, 0, "k", 0, h, step) for h in range(2)])
+        vn = np.stack([new_token_kv(w, 0, "v", 0, h, step) for h in range(2)])
+        tq.tq_encode_append(cache, S.padded_tensor([kn], 1), S.padded_tensor([vn], 1))
+        k[0] = np.concatenate([k[0], kn], axis=1)
+        v[0] = np.concatenate([v[0], vn], axis=1)
+        L = pre + step + 1
+        assert int(cache.seq_lens.cpu()[0]) == L and int(cache.lengths[0]) == L
+        q = queries(w, 0, step)
+        got = S.gpu_decode(cache, q, variant=variant)
+        S.assert_close(got[0], S.oracle_end_to_end(w, k[0], v[0], L, q[0], codebooks), f"step {step}")
+
+
+def test_decode_does_not_mutate_cache():
+    w = get_workload(0)
+    cache, _, _, _, q = S.prefill_and_step(w)
+
+    def digest():
+        h = hashlib.sha256()
+        for t in (cache.k_data, cache.k_norms, cache.v_data, cache.v_norms, cache.seq_lens):
+            h.update(t.cpu().numpy().tobytes())
+        return h.hexdigest()
+
+    before = digest()
+    for variant in VARIANTS:
+        S.gpu_decode(cache, q, variant=variant)
+    assert digest() == before
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_empty_and_single_token_sequences(variant, codebooks):
+    w = S.scaled(get_workload(0), batch=3)
+    cache, k_list, v_list, L, q = S.prefill_and_step(w, lengths=np.array([1, 0, 65]))
+    got = S.gpu_decode(cache, q, variant=variant)
+    assert np.all(got[1] == 0)
+    for b in (0, 2):
+        S.assert_close(got[b], S.oracle_end_to_end(w, k_list[b], v_list[b], int(L[b]), q[b], codebooks))
+    # one visible token: the output is that token's reconstructed value for every query head
+    d = S.download_sequence(cache, 0)
+    _, vc = reference.codes_from_library_layout(d.get("k_rec"), d["v_tiles"], w.k_format, w.v_format)
+    v0 = codec.dequant(vc[:, :1], d["v_norms"][:, :1], codebooks["turbo3"], sign_vector(0, "v"))[:, 0]
+    np.testing.assert_allclose(got[0].astype(np.float64), np.repeat(v0, 2, axis=0), atol=2e-3, rtol=0)
+
+
+@pytest.mark.parametrize("group", [1, 16])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_group_size_extremes(group, variant, codebooks):
+    w = S.scaled(get_workload(0), num_q_heads=2 * group, num_kv_heads=2, k_format="turbo4", v_format="turbo3")
+    cache, k_list, v_list, L, q = S.prefill_and_step(w, lengths=np.array([300]))
+    got = S.gpu_decode(cache, q, variant=variant)
+    S.assert_close(got[0], S.oracle_end_to_end(w, k_list[0], v_list[0], 300, q[0], codebooks), f"G={group}")
+
+
+def test_appends_merge_into_partial_tiles(codebooks):
+    """Appends of 5, 1, 37 and 100 rows land mid-tile and across tiles; earlier tokens of
+    a shared V tile keep their codes."""
+    import quantized_kv_cache_decode_amd as tq
+    from synth import kv_slice
+    for fmt in ("turbo3", "turbo4"):
+        w = S.scaled(get_workload(0), batch=2, k_format=fmt, v_format=fmt)
+        total = 3 + 5 + 1 + 37 + 100
+        full_k = [np.stack([kv_slice(w, 1, "k", b, h, total) for h in range(2)]) for b in range(2)]
+        full_v = [np.stack([kv_slice(w, 1, "v", b, h, total) for h in range(2)]) for b in range(2)]
+        cache = S.make_cache(w, 160, seed=1)
+        pos = 0
+        for n in (3, 5, 1, 37, 100):
+            tq.tq_encode_append(cache, S.padded_tensor([x[:, pos:pos + n] for x in full_k], n),
+                                S.padded_tensor([x[:, pos:pos + n] for x in full_v], n))
+            pos += n
+        for b in range(2):
+            m, _, _ = S.compare_codes(cache, b, full_k[b], full_v[b], total, w, codebooks, seed=1)
+            assert m == 0
+
+
+# ----------------------------------------------------------------------------- full size
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("index", [1, 2, 3, 4])
+def test_full_size_sampled(index, codebooks):
+    """Full-size workloads in the launch configuration the benchmark times; codes of the
+    sampled sequences are checked in full, outputs of the sampled sequences against the
+    oracle on the GPU bytes (codes equal the oracle's, so this is also end to end)."""
+    w = get_workload(index)
+    _say(f"[full {w.name}] generating + encoding")
+    cache, k_list, v_list, L, q = S.prefill_and_step(w)
+    got = S.gpu_decode(cache, q, variant=VARIANTS[-1])
+    sample = [int(np.argmin(L)), int(np.argmax(L))] if index == 4 else sorted({0, w.batch - 1})
+    for b in sample:
+        m, g, t = S.compare_codes(cache, b, k_list[b], v_list[b], int(L[b]), w, codebooks)
+        _say(f"[full {w.name}] b={b} L={int(L[b])} code mismatches {m}/{t}, margin {g}")
+        assert m <= g <= 1e-4 * t
+        rel, mx = S.assert_close(got[b], S.oracle_on_bytes(cache, b, int(L[b]), q[b], codebooks), f"b={b}")
+        _say(f"[full {w.name}] b={b} rel-L2 {rel:.2e} max-abs {mx:.2e}")
+    assert np.all(np.isfinite(got.astype(np.float32)))

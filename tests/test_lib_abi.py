@@ -1,0 +1,162 @@
+"""CPU-side checks of libtqattn: it loads, exports every declared entry point, and
+validates arguments on the host (no kernel is launched by these calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import quantized_kv_cache_decode_amd as tq
+from quantized_kv_cache_decode_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tqattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from quantized_kv_cache_decode_amd import build
+        build.build(verbose=False)
+    return tq.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert "tq_decode_attention" in names and "tq_encode_append" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (tq_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+    assert set(binding.EXPORTED) == set(names)
+
+
+def test_library_is_built_for_gfx950(lib):
+    data = open(binding.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+
+
+def _desc(**over):
+    fake = 0x10000
+    d = dict(batch=2, num_kv_heads=2, head_dim=128, capacity=64, k_format=3, v_format=3,
+             k_data=fake, k_norms=fake, v_data=fake, v_norms=fake, seq_lens=fake, k_signs=fake,
+             v_signs=fake, k_codebook=fake, v_codebook=fake)
+    d.update(over)
+    return binding.tq_cache(**d)
+
+
+def _lens(*v):
+    a = np.array(v, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _err(lib):
+    return lib.tq_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=64), binding.TQ_EUNSUPPORTED),
+    (dict(capacity=48), binding.TQ_EINVAL),
+    (dict(capacity=0), binding.TQ_EINVAL),
+    (dict(v_format=0), binding.TQ_EUNSUPPORTED),
+    (dict(k_format=7), binding.TQ_EUNSUPPORTED),
+    (dict(v_data=0), binding.TQ_EINVAL),
+    (dict(k_norms=0), binding.TQ_EINVAL),
+    (dict(batch=0), binding.TQ_EINVAL),
+])
+def test_bad_cache_descriptors(lib, over, status):
+    d = _desc(**over)
+    a, p = _lens(0, 0)
+    q = ctypes.c_void_p(0x20000)
+    assert lib.tq_rotate_q(ctypes.byref(d), q, 0, 4, q, None) == status
+    assert _err(lib)
+    assert lib.tq_encode_append(ctypes.byref(d), p, q, q, 1, None, None) == status
+
+
+def test_f16_k_needs_no_norms(lib):
+    d = _desc(k_format=0, k_norms=0, k_signs=0, k_codebook=0)
+    a, p = _lens(0, 0)
+    # valid descriptor; the error comes from the heads check, proving the descriptor passed
+    assert lib.tq_rotate_q(ctypes.byref(d), ctypes.c_void_p(1), 0, 3, ctypes.c_void_p(1), None) == binding.TQ_EINVAL
+    assert "num_q_heads" in _err(lib)
+
+
+def test_heads_checks(lib):
+    d = _desc()
+    q = ctypes.c_void_p(0x20000)
+    assert lib.tq_rotate_q(ctypes.byref(d), q, 0, 3, q, None) == binding.TQ_EINVAL        # 3 % 2
+    assert lib.tq_rotate_q(ctypes.byref(d), q, 0, 34, q, None) == binding.TQ_EUNSUPPORTED  # group 17
+    assert lib.tq_rotate_q(ctypes.byref(d), ctypes.c_void_p(0), 0, 4, q, None) == binding.TQ_EINVAL
+
+
+def test_append_capacity_and_counts(lib):
+    d = _desc()
+    q = ctypes.c_void_p(0x20000)
+    a, p = _lens(60, 10)
+    assert lib.tq_encode_append(ctypes.byref(d), p, q, q, 5, None, None) == binding.TQ_ECAPACITY
+    assert "capacity" in _err(lib)
+    c, pc = _lens(6, 0)
+    assert lib.tq_encode_append(ctypes.byref(d), p, q, q, 5, pc, None) == binding.TQ_EINVAL      # count > t_new
+    c, pc = _lens(-1, 0)
+    assert lib.tq_encode_append(ctypes.byref(d), p, q, q, 5, pc, None) == binding.TQ_EINVAL
+    a, p = _lens(-3, 0)
+    assert lib.tq_encode_append(ctypes.byref(d), p, q, q, 0, None, None) == binding.TQ_EINVAL
+    a, p = _lens(10, 10)
+    assert lib.tq_encode_append(ctypes.byref(d), p, q, q, 0, None, None) == binding.TQ_OK          # no-op
+    assert lib.tq_encode_append(ctypes.byref(d), ctypes.c_void_p(0), q, q, 1, None, None) == binding.TQ_EINVAL
+
+
+def test_workspace_size_and_check(lib):
+    d = _desc()
+    a, p = _lens(64, 17)
+    n = lib.tq_decode_workspace_size(ctypes.byref(d), 4, p)
+    assert n > 0 and n % 4 == 0
+    # one split per (sequence, KV head) at these lengths: 2*2*1 items x group 2 x 130 floats
+    assert n == 2 * 2 * 1 * 2 * 130 * 4
+    q = ctypes.c_void_p(0x20000)
+    st = lib.tq_decode_attention(ctypes.byref(d), p, q, 4, ctypes.c_float(0.1), q, q, n - 4, None)
+    assert st == binding.TQ_EWORKSPACE
+    st = lib.tq_decode_attention_variant(ctypes.byref(d), p, q, 4, ctypes.c_float(0.1), q, q, n, 9, None)
+    assert st == binding.TQ_EINVAL
+    a, p = _lens(65, 0)
+    assert lib.tq_decode_workspace_size(ctypes.byref(d), 4, p) == 0
+    assert lib.tq_decode_attention(ctypes.byref(d), p, q, 4, ctypes.c_float(0.1), q, q, 10 ** 9, None) == \
+        binding.TQ_ECAPACITY
+
+
+def test_workspace_grows_with_context(lib):
+    d = _desc(batch=1, num_kv_heads=8, capacity=131072)
+    sizes = []
+    for L in (256, 4096, 131072):
+        a, p = _lens(L)
+        sizes.append(lib.tq_decode_workspace_size(ctypes.byref(d), 64, p))
+    assert sizes[0] <= sizes[1] <= sizes[2]
+
+
+@pytest.mark.parametrize("batch,hkv,hq,lens,bytes_per_token", [
+    (32, 8, 32, [32768] * 32, 132),                                 # batched turbo4
+    (16, 8, 64, list(np.linspace(1024, 131072, 16).astype(int)), 100),  # ragged turbo3
+])
+def test_partials_are_small_next_to_the_cache(lib, batch, hkv, hq, lens, bytes_per_token):
+    """In the bandwidth-bound regime the split partials (written once, read once) stay
+    under 5% of the packed K+V bytes a decode call streams."""
+    d = _desc(batch=batch, num_kv_heads=hkv, capacity=131072)
+    a, p = _lens(*lens)
+    ws = lib.tq_decode_workspace_size(ctypes.byref(d), hq, p)
+    kv = sum(lens) * hkv * bytes_per_token
+    assert 2 * ws < 0.05 * kv
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_LIB", None)
+    with pytest.raises(FileNotFoundError):
+        binding.load_library(str(tmp_path / "missing.so"))

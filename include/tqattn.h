@@ -133,9 +133,9 @@ tq_status tq_encode_append(const tq_cache* cache, const int32_t* seq_lens_host,
 tq_status tq_rotate_q(const tq_cache* cache, const void* q, int32_t q_is_fp32,
                       int32_t num_q_heads, float* q_rot, void* stream);
 
-/* Bytes of device workspace tq_decode_attention needs for these lengths
- * (split-K partials).  seq_lens_host: HOST int32 [B].  Returns 0 on invalid
- * arguments (see tq_last_error). */
+/* Bytes of device workspace tq_decode_attention needs for these lengths:
+ * split-K partials (fp32 o, m, l per split and query head).  seq_lens_host:
+ * HOST int32 [B].  Returns 0 on invalid arguments (see tq_last_error). */
 size_t tq_decode_workspace_size(const tq_cache* cache, int32_t num_q_heads,
                                 const int32_t* seq_lens_host);
 
@@ -151,7 +151,9 @@ size_t tq_decode_workspace_size(const tq_cache* cache, int32_t num_q_heads,
  *   q_rot          device fp32 [B][num_q_heads][128] (from tq_rotate_q).
  *   out_rot        device fp32 [B][num_q_heads][128]; a sequence of length 0
  *                  gives zeros.
- *   workspace      device, >= tq_decode_workspace_size() bytes.
+ *   workspace      device, >= tq_decode_workspace_size() bytes; no initial
+ *                  contents needed; reusable by later calls (not by two calls
+ *                  in flight at the same time).
  * The cache is not modified. */
 tq_status tq_decode_attention(const tq_cache* cache, const int32_t* seq_lens_host,
                               const float* q_rot, int32_t num_q_heads, float scale,
@@ -159,7 +161,7 @@ tq_status tq_decode_attention(const tq_cache* cache, const int32_t* seq_lens_hos
                               void* stream);
 
 /* Same as tq_decode_attention with an explicit kernel variant, for A/B
- * comparison of kernel designs: 0 = default (fastest), 1 = plain VALU
+ * comparison of kernel designs: 0 = default (the MFMA kernel), 1 = plain VALU
  * reference kernel, 2 = MFMA kernel.  Unknown variants give TQ_EINVAL. */
 tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_lens_host,
                                       const float* q_rot, int32_t num_q_heads, float scale,

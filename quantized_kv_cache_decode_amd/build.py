@@ -19,6 +19,8 @@ DEVICE_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed FP32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: no AGPR<->VGPR copies around the softmax rescale
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
 ]
 

@@ -65,8 +65,15 @@ tq_status check_lengths(const tq_cache* c, const int32_t* lens, int32_t extra) {
   return TQ_OK;
 }
 
-// Split plan shared by the workspace query and the launch.  About 2048 work
-// items over the chip (8 per CU), each a multiple of 256 tokens.  Once the call
+#ifndef TQ_PLAN_MIN_CHUNK
+#define TQ_PLAN_MIN_CHUNK 256   // shortest split, tokens (a multiple of 128)
+#endif
+#ifndef TQ_PLAN_ITEMS
+#define TQ_PLAN_ITEMS 2048      // work items the plan aims for
+#endif
+
+// Split plan shared by the workspace query and the launch.  About TQ_PLAN_ITEMS
+// work items over the chip (8 per CU), each a multiple of 128 tokens.  Once the call
 // is bandwidth-bound (>= 4M token-heads) the chunk is also kept long enough that
 // the partials (G x 130 floats, written then read) stay under ~4% of the packed
 // bytes of the chunk.
@@ -77,15 +84,16 @@ tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
     total += (long long)lens[b] * c->num_kv_heads;
     lmax = std::max(lmax, (int)lens[b]);
   }
-  long long chunk = (total + 2047) / 2048;
+  long long chunk = (total + TQ_PLAN_ITEMS - 1) / TQ_PLAN_ITEMS;
   if (total >= (4LL << 20)) chunk = std::max(chunk, 260LL * group);
-  chunk = std::max(256LL, (chunk + 255) / 256 * 256);
+  chunk = std::max((long long)TQ_PLAN_MIN_CHUNK, (chunk + 127) / 128 * 128);
   tq::DecodePlan p;
   p.chunk = (int)chunk;
   p.max_splits = std::max(1, (int)((lmax + chunk - 1) / chunk));
   return p;
 }
 
+// Workspace: split partials o [items][G][128] and (m, l) [items][G][2] (fp32).
 size_t workspace_bytes(const tq_cache* c, int32_t num_q_heads, const tq::DecodePlan& p) {
   const size_t items = (size_t)c->batch * c->num_kv_heads * p.max_splits;
   const size_t g = num_q_heads / c->num_kv_heads;
@@ -205,8 +213,10 @@ tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_
   a.part_ml = a.part_o + (size_t)cache->batch * cache->num_kv_heads * plan.max_splits * a.group * 128;
   a.out_rot = out_rot;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = (variant == 2) ? tq::launch_decode_mfma(a, cache->batch, s)
-                                : tq::launch_decode_reference(a, cache->batch, s);
+  // variant 0 (default) is the MFMA kernel, 1 the plain VALU reference kernel;
+  // both are followed by the log-sum-exp merge of their splits
+  hipError_t e = (variant == 1) ? tq::launch_decode_reference(a, cache->batch, s)
+                                : tq::launch_decode_mfma(a, cache->batch, s);
   if ((st = hip_status(e, "decode launch")) != TQ_OK) return st;
   return hip_status(tq::launch_combine(a, cache->batch, s), "combine launch");
 }

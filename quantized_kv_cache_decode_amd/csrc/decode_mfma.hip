@@ -1,10 +1,436 @@
-// MFMA split-K decode attention (variant 2).  Not built yet: the launcher
-// reports "not supported" so the API returns TQ_EHIP for this variant.
+// MFMA split-K decode attention for gfx950 (variant 2).
+//
+// One wave per work item (split s of KV head h of sequence b).  Both
+// contractions run on v_mfma_f32_16x16x32_f16 with fp32 accumulation; the VALU
+// only dequantises codes into MFMA operands and runs the online softmax.
+//
+// Column packing.  The G query heads of a KV head are padded to Gp = 4, 8 or
+// 16 and the 16 MFMA columns carry NS = 16/Gp "sets" of them: column n is
+// head n % Gp of set n / Gp, and set sigma works on its own 32-token V tile.
+// An iteration therefore consumes NS tiles (32*NS tokens) and no softmax lane
+// is spent on padding when G divides 16.
+//
+//   scores   S^T[token][col] = sum_k K[token][k] * Qhat[k][col]     (A = K, B = q)
+//            The B operand of lane group g is zero unless g belongs to the
+//            column's set, so each set only sees its own tokens; lane (g, n)
+//            ends with the 8 scores of tile slots r = 16*rb + 4*g + j of its
+//            column's tile -- the slots of V-tile chunk group g, element 4rb+j.
+//   softmax  log2-domain online max/sum (the scale * log2(e) factor is folded
+//            into q); the max is shared by the 4 lanes of a column.
+//   values   O^T[dim][col] += sum_t V^T[dim][t] * Pn[t][col]    (A = V, B = P*n_V)
+//            with one MFMA group per set, whose B operand is zero outside the set.
+//
+// Dequant (no LDS, no barrier; interleaved with the MFMA issue, which
+// turboquant_plus "SMEM Pre-Dequant Experiment", "Why It Failed", found to be
+// the point): fp16 codebook values come from byte tables held in registers via
+// v_perm_b32 -- one lookup per 4 codes for the low bytes, one for the high
+// bytes, two more to interleave them into fp16 pairs.  turbo3 looks up the full
+// signed 8-entry table; turbo4 looks up 8 magnitudes and ORs the sign bit.
+// The per-token norms multiply the fp32 scores (K) and the fp16 probabilities
+// (V), never the operands.
+#include <math.h>
+
 #include "tq_device.h"
 #include "tq_launch.h"
 
 namespace tq {
+namespace {
 
-hipError_t launch_decode_mfma(const DecodeArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Build-time tuning knobs (defaults are the measured best; see the design notes).
+#ifndef TQ_MFMA_PREFETCH
+#define TQ_MFMA_PREFETCH 1   // 1: request the next iteration's words mid-iteration
+#endif
+#ifndef TQ_MFMA_NS_SMALL_GROUP
+#define TQ_MFMA_NS_SMALL_GROUP 4   // token sets per MFMA for group sizes <= 4 (4 or 2)
+#endif
+#ifndef TQ_MFMA_LAZY_RESCALE
+#define TQ_MFMA_LAZY_RESCALE 1
+#endif
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ inline half8 pack8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(half8, v);
+}
+
+// Byte tables of 8 fp16 values: lo/hi byte of entries 0..3 (x0) and 4..7 (x1).
+struct ByteTable {
+  uint32_t lo0, lo1, hi0, hi1;
+};
+
+__device__ inline ByteTable make_table(const uint16_t* v8) {
+  ByteTable t;
+  t.lo0 = t.lo1 = t.hi0 = t.hi1 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = v8[i], b = v8[4 + i];
+    t.lo0 |= (a & 0xffu) << (8 * i);
+    t.hi0 |= (a >> 8) << (8 * i);
+    t.lo1 |= (b & 0xffu) << (8 * i);
+    t.hi1 |= (b >> 8) << (8 * i);
+  }
+  return t;
+}
+
+__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) { return __builtin_amdgcn_perm(hi, lo, sel); }
+
+// four table lookups (selector bytes 0..7) -> two dwords of fp16 pairs
+__device__ inline void lookup4(const ByteTable& t, uint32_t sel, uint32_t& d0, uint32_t& d1) {
+  const uint32_t lo = perm(t.lo1, t.lo0, sel);
+  const uint32_t hi = perm(t.hi1, t.hi0, sel);
+  d0 = perm(hi, lo, 0x05010400u);
+  d1 = perm(hi, lo, 0x07030602u);
+}
+
+// turbo3: codes 8c..8c+7 of a sub-block (words A, B, C) as 8 fp16 codebook values.
+template <int C>
+__device__ inline half8 dq_turbo3(uint32_t A, uint32_t B, uint32_t Cw, const ByteTable& t) {
+  uint32_t s0, s1;
+  if (C == 0) {
+    s0 = A & 0x07070707u;
+    s1 = (A >> 3) & 0x07070707u;
+  } else if (C == 1) {
+    s0 = B & 0x07070707u;
+    s1 = (B >> 3) & 0x07070707u;
+  } else if (C == 2) {
+    s0 = Cw & 0x07070707u;
+    s1 = (Cw >> 3) & 0x07070707u;
+  } else {
+    s0 = ((A >> 6) & 0x03030303u) | ((Cw >> 4) & 0x04040404u);
+    s1 = ((B >> 6) & 0x03030303u) | ((Cw >> 5) & 0x04040404u);
+  }
+  uint32_t d0, d1, d2, d3;
+  lookup4(t, s0, d0, d1);
+  lookup4(t, s1, d2, d3);
+  return pack8(d0, d1, d2, d3);
+}
+
+// turbo4: the 8 sign-magnitude nibbles of an octet word as 8 fp16 codebook values.
+__device__ inline half8 dq_turbo4(uint32_t w, const ByteTable& mag) {
+  const uint32_t mA = w & 0x07070707u, mB = (w >> 4) & 0x07070707u;
+  const uint32_t loA = perm(mag.lo1, mag.lo0, mA);
+  const uint32_t hiA = perm(mag.hi1, mag.hi0, mA) | ((w << 4) & 0x80808080u);
+  const uint32_t loB = perm(mag.lo1, mag.lo0, mB);
+  const uint32_t hiB = perm(mag.hi1, mag.hi0, mB) | (w & 0x80808080u);
+  return pack8(perm(hiA, loA, 0x05010400u), perm(hiA, loA, 0x07030602u), perm(hiB, loB, 0x05010400u),
+               perm(hiB, loB, 0x07030602u));
+}
+
+__device__ inline floatx4 mfma(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float xmax4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ inline float xsum4(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+template <int N>
+__device__ inline void load_words(uint32_t (&w)[N], const uint8_t* p) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const uint2 v = reinterpret_cast<const uint2*>(p)[i];
+      w[2 * i] = v.x;
+      w[2 * i + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = reinterpret_cast<const uint32_t*>(p)[i];
+  }
+}
+
+template <int N>
+__device__ inline void zero_words(uint32_t (&w)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = 0;
+}
+
+template <int KFMT, int VFMT, int NS>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int P = 4 / NS;                  // lane groups per set in the score MFMA
+  constexpr int Gp = 16 / NS;                // columns (padded heads) per set
+  constexpr int TOK = 32 * NS;               // tokens per iteration
+  constexpr int REC = KFMT == kFmtF16 ? 256 : k_record_bytes(KFMT);
+  constexpr int KW = REC / 4 / P;            // K words per lane per token
+  constexpr int NKK = 4 * NS;                // score MFMAs per 16-token row block
+  constexpr int VW = v_chunk_bytes(VFMT) / 4;  // V words per lane per tile
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = a.group;
+  const int L = min(a.seq_lens[b], a.cap);
+  const int chunk = a.plan.chunk;
+  const int nsplit = min((L + chunk - 1) / chunk, a.plan.max_splits);
+  if (s >= nsplit) return;
+  const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
+  const int t0 = s * chunk;
+  const int t1 = (s == nsplit - 1) ? L : t0 + chunk;
+
+  const int sig = g / P, part = g % P;       // score-MFMA set and part of this lane
+  const int sn = n / Gp, hn = n % Gp;        // this lane's column: set and head
+  const size_t row = size_t(b) * a.hkv + h;
+  const uint8_t* kbase = a.k_data + row * size_t(a.cap) * REC + part * (REC / P);
+  const uint8_t* vbase = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT) + lane * (VW * 4);
+  const uint16_t* knorm = KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap);
+  const uint16_t* vnorm = a.v_norms + row * size_t(a.cap);
+
+  // q in this lane's score-MFMA B slots: q[hn][part*128/P + 8kk + t] * scale*log2(e),
+  // zero unless the lane's k-slots belong to its column's set (loads are unconditional).
+  // Kept in VGPRs: staging these operands in LDS measured slower.
+  half8 qb[NKK];
+  {
+    const bool use = hn < G && sig == sn;
+    const float* qrow = a.q_rot + ((size_t(b) * a.hkv + h) * G + min(hn, G - 1)) * kDim + part * (kDim / P);
+    const float f = use ? a.scale * kLog2e : 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const float4 x0 = reinterpret_cast<const float4*>(qrow + 8 * kk)[0];
+      const float4 x1 = reinterpret_cast<const float4*>(qrow + 8 * kk)[1];
+      qb[kk] = half8{_Float16(x0.x * f), _Float16(x0.y * f), _Float16(x0.z * f), _Float16(x0.w * f),
+                     _Float16(x1.x * f), _Float16(x1.y * f), _Float16(x1.z * f), _Float16(x1.w * f)};
+    }
+  }
+  ByteTable ktab, vtab;
+  {
+    uint16_t c[8];
+    if (KFMT != kFmtF16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = a.k_cb[(KFMT == kFmtTurbo4 ? 8 : 0) + i];
+      ktab = make_table(c);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = a.v_cb[(VFMT == kFmtTurbo4 ? 8 : 0) + i];
+    vtab = make_table(c);
+  }
+
+  floatx4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Register double-buffering by rotation: the K words of iteration i+1 are
+  // requested as soon as iteration i's K has been turned into MFMA operands, and
+  // the V words and norms of i+1 as soon as i's values are accumulated, so every
+  // load has about half an iteration of this wave's own math to hide behind.
+  uint32_t kw[2][KW];
+  uint32_t vw[NS][VW];
+  uint2 nk[2], nv[2];
+  // Tiles past the split's last visible token are read from the last visible tile
+  // instead (always in bounds); their scores are masked and their probabilities are 0.
+  const int last_tile = (t1 - 1) >> 5;
+  auto load_k = [&](int base) {
+    const int tk = min((base >> 5) + sig, last_tile) << 5;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) load_words(kw[rb], kbase + size_t(tk + 16 * rb + n) * REC);
+    if (KFMT != kFmtF16) {
+      const int tn = min((base >> 5) + sn, last_tile) << 5;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) nk[rb] = *reinterpret_cast<const uint2*>(knorm + tn + 16 * rb + 4 * g);
+    }
+  };
+  auto load_v = [&](int base) {
+#pragma unroll
+    for (int sg = 0; sg < NS; ++sg)
+      load_words(vw[sg], vbase + size_t(min((base >> 5) + sg, last_tile)) * v_tile_bytes(VFMT));
+    const int tn = min((base >> 5) + sn, last_tile) << 5;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) nv[rb] = *reinterpret_cast<const uint2*>(vnorm + tn + 16 * rb + 4 * g);
+  };
+  if (TQ_MFMA_PREFETCH) {
+    load_k(t0);
+    load_v(t0);
+  }
+
+  for (int base = t0; base < t1; base += TOK) {
+    if (!TQ_MFMA_PREFETCH) {
+      load_k(base);
+      load_v(base);
+    }
+    const int tn = ((base >> 5) + sn) << 5;      // first token of this lane's column tile
+    // ---- scores (dequant of each operand right before its MFMA)
+    float z[8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = j < 2 ? nk[rb].x : nk[rb].y;
+        z[4 * rb + j] = KFMT != kFmtF16 ? half_bits_to_float(uint16_t(w >> (16 * (j & 1)))) : 1.f;
+      }
+    }
+    floatx4 S[2], S2[2];                          // two accumulator chains per row block
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      S[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      S2[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        half8 A;
+        if (KFMT == kFmtF16) {
+          A = pack8(kw[rb][4 * kk], kw[rb][4 * kk + 1], kw[rb][4 * kk + 2], kw[rb][4 * kk + 3]);
+        } else if (KFMT == kFmtTurbo4) {
+          A = dq_turbo4(kw[rb][kk], ktab);
+        } else {
+          const int sb = 3 * (kk >> 2);
+          const uint32_t wa = kw[rb][sb], wb = kw[rb][sb + 1], wc = kw[rb][sb + 2];
+          switch (kk & 3) {
+            case 0: A = dq_turbo3<0>(wa, wb, wc, ktab); break;
+            case 1: A = dq_turbo3<1>(wa, wb, wc, ktab); break;
+            case 2: A = dq_turbo3<2>(wa, wb, wc, ktab); break;
+            default: A = dq_turbo3<3>(wa, wb, wc, ktab); break;
+          }
+        }
+        if (kk & 1) S2[rb] = mfma(A, qb[kk], S2[rb]);
+        else S[rb] = mfma(A, qb[kk], S[rb]);
+      }
+      S[rb] += S2[rb];
+    }
+    if (TQ_MFMA_PREFETCH) load_k(base + TOK);     // next iteration's K words and K norms
+
+    // ---- online softmax (log2 domain) for the 8 tokens of this lane's column
+    const bool tail = base + TOK > t1;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v = S[rb][j] * z[4 * rb + j];
+        if (tail && tn + 16 * rb + 4 * g + j >= t1) v = -INFINITY;
+        z[4 * rb + j] = v;
+      }
+    }
+    float mt = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
+    mt = xmax4(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    if (!TQ_MFMA_LAZY_RESCALE || __any(m_new > m_run)) {   // rescale only when a running max grew
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+    }
+    m_run = m_new;
+    float psum = 0.f;
+    half8 pb;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * rb + j;
+        const float p = __builtin_amdgcn_exp2f(z[i] - m_use);
+        psum += p;
+        const uint32_t w = j < 2 ? nv[rb].x : nv[rb].y;
+        const float pn = p * half_bits_to_float(uint16_t(w >> (16 * (j & 1))));
+        pb[i] = _Float16(z[i] == -INFINITY ? 0.f : pn);
+      }
+    }
+    l_run += psum;
+
+    // ---- values: one MFMA group per set; B is zero outside the set
+#pragma unroll
+    for (int sg = 0; sg < NS; ++sg) {
+      const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+      const half8 bsg = (sn == sg) ? pb : zero8;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        half8 A;
+        if (VFMT == kFmtTurbo4) {
+          A = dq_turbo4(vw[sg][nb], vtab);
+        } else {
+          const int sb = 3 * (nb >> 2);
+          const uint32_t wa = vw[sg][sb], wb = vw[sg][sb + 1], wc = vw[sg][sb + 2];
+          switch (nb & 3) {
+            case 0: A = dq_turbo3<0>(wa, wb, wc, vtab); break;
+            case 1: A = dq_turbo3<1>(wa, wb, wc, vtab); break;
+            case 2: A = dq_turbo3<2>(wa, wb, wc, vtab); break;
+            default: A = dq_turbo3<3>(wa, wb, wc, vtab); break;
+          }
+        }
+        acc[nb] = mfma(A, bsg, acc[nb]);
+      }
+    }
+    if (TQ_MFMA_PREFETCH) load_v(base + TOK);     // next iteration's V words and V norms
+  }
+
+  // ---- finish: sum l over the column's 4 lanes, merge the NS sets of each head
+  float l_tot = xsum4(l_run);
+  float m_fin = m_run;
+#pragma unroll
+  for (int stp = Gp; stp < 16; stp <<= 1) {
+    const float m_o = __shfl_xor(m_fin, stp, 64);
+    const float l_o = __shfl_xor(l_tot, stp, 64);
+    const float M = fmaxf(m_fin, m_o);
+    const float fs = m_fin == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_fin - M);
+    const float fo = m_o == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_o - M);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float o = __shfl_xor(acc[i][j], stp, 64);
+        acc[i][j] = acc[i][j] * fs + o * fo;
+      }
+    }
+    l_tot = l_tot * fs + l_o * fo;
+    m_fin = M;
+  }
+  // Partial of this split (unnormalised o, natural-log m, l); the splits are merged
+  // by a separate kernel: a release/acquire hand-off between waves of this kernel
+  // would need an L2 write-back per wave, which measured far slower.
+  if (n < Gp && hn < G) {
+    const size_t pidx = (row * a.plan.max_splits + s) * G + hn;
+    float* o = a.part_o + pidx * kDim;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = 8 * (4 * g + j);
+      reinterpret_cast<float4*>(o + d0)[0] = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+      reinterpret_cast<float4*>(o + d0)[1] = make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
+    }
+    if (g == 0) {
+      a.part_ml[pidx * 2] = m_fin == -INFINITY ? -INFINITY : m_fin * kLn2;
+      a.part_ml[pidx * 2 + 1] = l_tot;
+    }
+  }
+}
+
+template <int KF, int VF>
+hipError_t launch_fmt(const DecodeArgs& a, int batch, hipStream_t stream) {
+  const dim3 grid(a.plan.max_splits, a.hkv, batch), block(64);
+  if (a.group <= 16 / TQ_MFMA_NS_SMALL_GROUP)
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, TQ_MFMA_NS_SMALL_GROUP>), grid, block, 0, stream, a);
+  else if (a.group <= 8) hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 2>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 1>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, hipStream_t stream) {
+  if (a.kfmt == kFmtTurbo3 && a.vfmt == kFmtTurbo3) return launch_fmt<kFmtTurbo3, kFmtTurbo3>(a, batch, stream);
+  if (a.kfmt == kFmtTurbo3 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtTurbo3, kFmtTurbo4>(a, batch, stream);
+  if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo3) return launch_fmt<kFmtTurbo4, kFmtTurbo3>(a, batch, stream);
+  if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtTurbo4, kFmtTurbo4>(a, batch, stream);
+  if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo3) return launch_fmt<kFmtF16, kFmtTurbo3>(a, batch, stream);
+  if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtF16, kFmtTurbo4>(a, batch, stream);
+  return hipErrorInvalidValue;
+}
 
 }  // namespace tq

@@ -2,9 +2,9 @@
 // "Change": the append is the only cache mutation).
 //
 // One workgroup per (32-token V tile touched by the append, KV head,
-// sequence).  256 threads = 64 four-lane groups: groups 0..31 encode the K row
-// of tile slot r = group, groups 32..63 the V row of slot r = group - 32.  A
-// lane holds 32 consecutive dims (lane q: dims 32q..32q+31).
+// sequence).  256 threads = 16 groups of 16 lanes; each group encodes one K or
+// V row of a new token of the tile (lane j holds dims 8j..8j+7), so a
+// one-token append keeps its dependency chains short.
 //
 // Per group x (fp16 [128]):
 //   norm  n = RNE_fp16(sqrt(sum x_i^2)) computed exactly: each |x_i| * 2^24 is
@@ -14,7 +14,7 @@
 //   y     = H (s * x) / sqrt(128): butterflies in binary64 (exact: fp16 terms
 //         are multiples of 2^-24 below 2^16), then one IEEE division.
 //   idx_i = #{j : y_i > n * beta_j}, beta_j = midpoints of adjacent fp16 codebook
-//         entries (n * beta_j is exact in binary64).
+//         entries (n * beta_j is exact in binary64), found by binary search.
 // K rows are written as token-major records; V codes are staged in LDS and
 // written as whole V-tile chunk words by one thread per chunk, merging with the
 // words of tokens already in the tile.  F16 K rows are copied unchanged.
@@ -64,6 +64,19 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
   __shared__ uint8_t vcodes[kTileTokens][kDim];
   __shared__ double beta_k[15], beta_v[15];
   const int tid = threadIdx.x;
+  const size_t row = size_t(b) * a.hkv + h;  // (sequence, KV head) row
+  // Threads 0..63 own V-tile chunk tid.  When the tile already holds other tokens,
+  // its old words are requested now so the read overlaps the encode below.
+  const bool whole = lo == tile * kTileTokens && hi == tile * kTileTokens + kTileTokens;
+  uint8_t* chunk = a.v_data + (row * (a.cap / kTileTokens) + tile) * v_tile_bytes(VFMT) + (tid & 63) * v_chunk_bytes(VFMT);
+  constexpr int kChunkWords = v_chunk_bytes(VFMT) / 4;
+  uint32_t old[kChunkWords];
+#pragma unroll
+  for (int i = 0; i < kChunkWords; ++i) old[i] = 0;
+  if (tid < 64 && !whole) {
+#pragma unroll
+    for (int i = 0; i < kChunkWords; ++i) old[i] = reinterpret_cast<const uint32_t*>(chunk)[i];
+  }
   if (tid < levels(VFMT) - 1)
     beta_v[tid] = 0.5 * (double(half_bits_to_float(a.v_cb[tid])) + double(half_bits_to_float(a.v_cb[tid + 1])));
   if (KFMT != kFmtF16 && tid >= 32 && tid - 32 < levels(KFMT) - 1)
@@ -71,106 +84,105 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
         0.5 * (double(half_bits_to_float(a.k_cb[tid - 32])) + double(half_bits_to_float(a.k_cb[tid - 31])));
   __syncthreads();
 
-  const int grp = tid >> 2, q = tid & 3;
-  const bool is_v = grp >= 32;
-  const int r = grp & 31;
-  const int t = tile * kTileTokens + r;
-  const bool active = t >= lo && t < hi;
-  const size_t row = size_t(b) * a.hkv + h;  // (sequence, KV head) row
-  const size_t src_off = (row * a.t_new + size_t(t - start)) * kDim + 32 * q;
-  const size_t slot = row * a.cap + t;
-
-  if (active) {
+  // Active rows: n_tok new tokens of this tile, each with a K row and a V row.
+  // Group gi (16 lanes) encodes K of token lo + gi for gi < n_tok, else V of token lo + gi - n_tok.
+  const int n_tok = hi - lo;
+  const int j = tid & 15;                 // lane within the group: dims 8j..8j+7
+  for (int gi = tid >> 4; gi < 2 * n_tok; gi += 16) {
+    const bool is_v = gi >= n_tok;
+    const int t = lo + (is_v ? gi - n_tok : gi);
+    const int r = t - tile * kTileTokens;
+    const size_t src_off = (row * a.t_new + size_t(t - start)) * kDim + 8 * j;
+    const size_t slot = row * a.cap + t;
     if (!is_v && KFMT == kFmtF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.k_new + src_off);
-      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.k_data) + slot * kDim + 32 * q);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.k_data) + slot * kDim + 8 * j) =
+          *reinterpret_cast<const uint4*>(a.k_new + src_off);
+      continue;
+    }
+    const uint4 raw = *reinterpret_cast<const uint4*>((is_v ? a.v_new : a.k_new) + src_off);
+    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+    const float* sg = (is_v ? a.v_signs : a.k_signs) + 8 * j;
+    double x[8];
+    uint64_t sA = 0, sB = 0, sC = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = src[i];
+    for (int e = 0; e < 8; ++e) {
+      const double xv = double(half_bits_to_float(uint16_t(w4[e >> 1] >> (16 * (e & 1)))));
+      const uint64_t m = uint64_t(fabs(xv) * 16777216.0);  // exact integer < 2^40
+      const uint64_t mh = m >> 20, ml = m & 0xfffffull;
+      sA += mh * mh;
+      sB += mh * ml;
+      sC += ml * ml;
+      x[e] = xv * double(sg[e]);
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      sA += __shfl_xor(sA, m, 16);
+      sB += __shfl_xor(sB, m, 16);
+      sC += __shfl_xor(sC, m, 16);
+    }
+    // Walsh-Hadamard in binary64: element bits 0..2 in-lane, bits 3..6 across lanes j ^ 1..8
+#pragma unroll
+    for (int hh = 1; hh < 8; hh <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!(e & hh)) {
+          const double u = x[e], v = x[e + hh];
+          x[e] = u + v;
+          x[e + hh] = u - v;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double o = __shfl_xor(x[e], m, 16);
+        x[e] = (j & m) ? (o - x[e]) : (x[e] + o);
+      }
+    }
+    const uint16_t nbits = exact_norm_fp16(sA, sB, sC);
+    const double nd = double(half_bits_to_float(nbits));
+    const double* beta = is_v ? beta_v : beta_k;
+    const int K = is_v ? levels(VFMT) : levels(KFMT);
+    uint8_t code[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double y = x[e] / kSqrtD;
+      // count of thresholds n*beta below y, by binary search over the ascending thresholds
+      int c = 0;
+      for (int st = K >> 1; st >= 1; st >>= 1)
+        if (y > nd * beta[c + st - 1]) c += st;
+      code[e] = uint8_t(c);
+    }
+    if (is_v) {
+      *reinterpret_cast<uint2*>(&vcodes[r][8 * j]) =
+          make_uint2(uint32_t(code[0]) | uint32_t(code[1]) << 8 | uint32_t(code[2]) << 16 | uint32_t(code[3]) << 24,
+                     uint32_t(code[4]) | uint32_t(code[5]) << 8 | uint32_t(code[6]) << 16 | uint32_t(code[7]) << 24);
+      if (j == 0) a.v_norms[slot] = nbits;
     } else {
-      const uint16_t* src = (is_v ? a.v_new : a.k_new) + src_off;
-      const float* sg = (is_v ? a.v_signs : a.k_signs) + 32 * q;
-      double x[32];
-      uint64_t sA = 0, sB = 0, sC = 0;
-      const uint4* s4 = reinterpret_cast<const uint4*>(src);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 raw = s4[i];
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int e = 8 * i + 2 * k2 + half;
-            const double xv = double(half_bits_to_float(uint16_t(w[k2] >> (16 * half))));
-            const uint64_t m = uint64_t(fabs(xv) * 16777216.0);  // exact integer < 2^40
-            const uint64_t mh = m >> 20, ml = m & 0xfffffull;
-            sA += mh * mh;
-            sB += mh * ml;
-            sC += ml * ml;
-            x[e] = xv * double(sg[e]);
-          }
-        }
-      }
-      // fold the four lanes' partial sums
-#pragma unroll
-      for (int m = 1; m < 4; m <<= 1) {
-        sA += __shfl_xor(sA, m, 4);
-        sB += __shfl_xor(sB, m, 4);
-        sC += __shfl_xor(sC, m, 4);
-      }
-      // Walsh-Hadamard in binary64: in-lane bits 0..4, cross-lane bits 5..6
-#pragma unroll
-      for (int hh = 1; hh < 32; hh <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          if (!(e & hh)) {
-            const double u = x[e], v = x[e + hh];
-            x[e] = u + v;
-            x[e + hh] = u - v;
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 1; m < 4; m <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          const double o = __shfl_xor(x[e], m, 4);
-          x[e] = (q & m) ? (o - x[e]) : (x[e] + o);
-        }
-      }
-      const uint16_t nbits = exact_norm_fp16(sA, sB, sC);
-      const double nd = double(half_bits_to_float(nbits));
-      const double* beta = is_v ? beta_v : beta_k;
-      const int nthr = (is_v ? levels(VFMT) : levels(KFMT)) - 1;
-      uint8_t code[32];
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const double y = x[e] / kSqrtD;
-        int c = 0;
-        for (int j = 0; j < nthr; ++j) c += (y > nd * beta[j]) ? 1 : 0;
-        code[e] = uint8_t(c);
-      }
-      if (is_v) {
-#pragma unroll
-        for (int e = 0; e < 32; ++e) vcodes[r][32 * q + e] = code[e];
-        if (q == 0) a.v_norms[slot] = nbits;
+      if (j == 0) a.k_norms[slot] = nbits;
+      uint8_t* rec = a.k_data + slot * k_record_bytes(KFMT);
+      if (KFMT == kFmtTurbo4) {
+        *reinterpret_cast<uint32_t*>(rec + 4 * j) = oct4_pack(code);
       } else {
-        if (q == 0) a.k_norms[slot] = nbits;
-        uint8_t* rec = a.k_data + slot * k_record_bytes(KFMT);
-        if (KFMT == kFmtTurbo3) {
-          uint32_t w[3];
-          sub3_pack(code, w);
-          uint32_t* dst = reinterpret_cast<uint32_t*>(rec + 12 * q);
+        // lanes 4q..4q+3 hold elements 8c..8c+7 (c = j % 4) of sub-block q; OR their fields
+        uint8_t c32[32] = {};
+        const int c0 = 8 * (j & 3);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c32[c0 + e] = code[e];
+        uint32_t w[3];
+        sub3_pack(c32, w);
+#pragma unroll
+        for (int m = 1; m < 4; m <<= 1) {
+          w[0] |= __shfl_xor(w[0], m, 16);
+          w[1] |= __shfl_xor(w[1], m, 16);
+          w[2] |= __shfl_xor(w[2], m, 16);
+        }
+        if ((j & 3) == 0) {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(rec + 12 * (j >> 2));
           dst[0] = w[0];
           dst[1] = w[1];
           dst[2] = w[2];
-        } else {
-          uint4 w;
-          w.x = oct4_pack(code);
-          w.y = oct4_pack(code + 8);
-          w.z = oct4_pack(code + 16);
-          w.w = oct4_pack(code + 24);
-          *reinterpret_cast<uint4*>(rec + 16 * q) = w;
         }
       }
     }
@@ -180,23 +192,19 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
   // V tile chunks: one thread per chunk c = 16 g + n (dims 8n..8n+7, slots r(g, i)).
   if (tid < 64) {
     const int g = tid >> 4, n = tid & 15;
-    uint8_t* chunk = a.v_data + (row * (a.cap / kTileTokens) + tile) * v_tile_bytes(VFMT) + tid * v_chunk_bytes(VFMT);
     uint8_t el[64];
-    const bool whole = lo == tile * kTileTokens && hi == tile * kTileTokens + kTileTokens;
     if (!whole) {
-      if (VFMT == kFmtTurbo3) {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(chunk);
-        uint32_t w0[3] = {w[0], w[1], w[2]}, w1[3] = {w[3], w[4], w[5]};
+      if constexpr (VFMT == kFmtTurbo3) {
+        const uint32_t w0[3] = {old[0], old[1], old[2]}, w1[3] = {old[3], old[4], old[5]};
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
           el[e] = uint8_t(sub3_get(w0, e));
           el[32 + e] = uint8_t(sub3_get(w1, e));
         }
       } else {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(chunk);
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-          const uint32_t word = w[nb];
+          const uint32_t word = old[nb];
 #pragma unroll
           for (int i = 0; i < 8; ++i) el[8 * nb + i] = uint8_t(t4_index_of_nibble(oct4_get_nibble(word, i)));
         }
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
       for (int nb = 0; nb < 8; ++nb)
         if (fresh) el[8 * nb + i] = vcodes[rr][8 * n + nb];
     }
-    if (VFMT == kFmtTurbo3) {
+    if constexpr (VFMT == kFmtTurbo3) {
       uint32_t w[6];
       sub3_pack(el, w);
       sub3_pack(el + 32, w + 3);

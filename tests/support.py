@@ -98,7 +98,7 @@ def gpu_decode(cache, q_np, variant=0, q_fp32=None):
     q_rot = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
     out_rot = torch.empty_like(q_rot)
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
-    ws = torch.empty(tq.tq_decode_workspace_size(cache, Hq), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(tq.tq_decode_workspace_size(cache, Hq), dtype=torch.uint8, device="cuda")
     tq.tq_rotate_q(cache, q, q_rot)
     tq.tq_decode_attention(cache, q_rot, SCALE, out_rot, ws, variant=variant)
     tq.tq_inverse_rotate_out(cache, out_rot, out)

@@ -19,7 +19,7 @@ from tests import support as S
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [1]
+VARIANTS = [1, 2]
 
 
 def _say(*a):
@@ -138,6 +138,40 @@ def test_sixteen_decode_steps_gqa_4_over_2(variant, codebooks):
         q = queries(w, 0, step)
         got = S.gpu_decode(cache, q, variant=variant)
         S.assert_close(got[0], S.oracle_end_to_end(w, k[0], v[0], L, q[0], codebooks), f"step {step}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_workspace_reused_across_calls(variant, codebooks):
+    """One workspace (filled with garbage first) serves successive decode calls with growing,
+    multi-split lengths."""
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    from synth import kv_slice, new_token_kv
+    w = S.scaled(get_workload(1), context=None)
+    L0 = 3000
+    k = [np.stack([kv_slice(w, 2, "k", 0, h, L0) for h in range(4)])]
+    v = [np.stack([kv_slice(w, 2, "v", 0, h, L0) for h in range(4)])]
+    cache = S.encode_on_gpu(w, k, v, [L0], 4864, seed=2)
+    ws = torch.full((tq.tq_decode_workspace_size(cache, 28, [4800]),), 0x7f, dtype=torch.uint8, device="cuda")
+    q_rot = torch.empty((1, 28, 128), dtype=torch.float32, device="cuda")
+    out_rot = torch.empty_like(q_rot)
+    out = torch.empty((1, 28, 128), dtype=torch.float16, device="cuda")
+    for step in range(3):
+        n = 300 * (step + 1)
+        kn = np.stack([new_token_kv(w, 2, "k", 0, h, step, n) for h in range(4)])
+        vn = np.stack([new_token_kv(w, 2, "v", 0, h, step, n) for h in range(4)])
+        tq.tq_encode_append(cache, S.padded_tensor([kn], n), S.padded_tensor([vn], n))
+        k[0] = np.concatenate([k[0], kn], axis=1)
+        v[0] = np.concatenate([v[0], vn], axis=1)
+        L = int(cache.lengths[0])
+        q = queries(w, 2, step)
+        tq.tq_rotate_q(cache, torch.from_numpy(q).cuda(), q_rot)
+        tq.tq_decode_attention(cache, q_rot, S.SCALE, out_rot, ws, variant=variant)
+        tq.tq_inverse_rotate_out(cache, out_rot, out)
+        torch.cuda.synchronize()
+        S.assert_close(out.cpu().numpy()[0], S.oracle_end_to_end(w, k[0], v[0], L, q[0], codebooks, seed=2),
+                       f"step {step} L={L}")
 
 
 def test_decode_does_not_mutate_cache():

@@ -1,8 +1,10 @@
 """Benchmark of one decode step of the rotated-codec KV cache on one MI355X.
 
 A step is the whole hot path for one new token per sequence:
-  tq_encode_append (1 token) -> tq_rotate_q -> tq_decode_attention -> tq_inverse_rotate_out
-on seeded synthetic inputs of the Qwen2.5-7B-shaped layer (B=1, Hq=28, Hkv=4,
+  tq_encode_append (1 token) -> tq_decode_attention_fused
+(q rotation inside the split-K decode kernel, LSE merge + inverse rotation in the
+merge kernel); --separate runs the four calls tq_encode_append -> tq_rotate_q ->
+tq_decode_attention -> tq_inverse_rotate_out instead.  Inputs are seeded synthetic inputs of the Qwen2.5-7B-shaped layer (B=1, Hq=28, Hkv=4,
 head dim 128, 8192 visible tokens, turbo3 K and V) unless --workload says
 otherwise.  The cache is replicated into distinct HBM copies (>= 1 GiB in all)
 and the steps rotate through them, so every step streams its cache from HBM
@@ -14,7 +16,8 @@ Prints ONE JSON line.  value = KV token-heads per second of whole steps
 (visible tokens x KV heads / step time).  roofline = the decode call
 (split-K kernel + LSE combine) timed by HIP events on its stream, eagerly
 enqueued behind a GPU sleep so the calls run back to back: algorithmic packed
-K+V bytes per call / average call duration, against 8 TB/s.
+K+V bytes per call / average call duration (both kernels of the call), against
+8 TB/s.
 cpu_baseline = the float64 oracle (oracle/) doing the same step on a bounded
 sample, on the host cores.
 """
@@ -41,7 +44,10 @@ def parse():
     p.add_argument("--steps", type=int, default=3200)
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--workload", type=int, default=1, help="workload index (0..4); default the 8K Qwen2.5-7B layer")
-    p.add_argument("--variant", type=int, default=0, help="decode kernel variant (0 default = MFMA, 1 VALU reference)")
+    p.add_argument("--separate", action="store_true",
+                   help="four separate calls per step instead of tq_decode_attention_fused")
+    p.add_argument("--variant", type=int, default=0,
+                   help="decode kernel variant of --separate (0 default = MFMA, 1 VALU reference)")
     p.add_argument("--copies-gib", type=float, default=1.0, help="total size of the rotated cache copies")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
@@ -49,7 +55,8 @@ def parse():
     return p.parse_args()
 
 
-KERNEL_SOURCES = ("quantized_kv_cache_decode_amd/csrc/decode_mfma.hip", "quantized_kv_cache_decode_amd/csrc/decode_ref.hip")
+KERNEL_SOURCES = tuple("quantized_kv_cache_decode_amd/csrc/" + f
+                       for f in ("decode_mfma.hip", "decode_ref.hip", "combine.hip", "tq_device.h"))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -190,12 +197,24 @@ def main():
     calib.copy_(torch.ones_like(calib))
     del calib
 
+    if args.variant and not args.separate:
+        sys.exit("--variant applies to --separate only")
+
+    def decode_call(c):
+        if args.separate:
+            tq.tq_decode_attention(c, q_rot, scale, out_rot, ws, seq_lens_host=L, variant=args.variant)
+        else:
+            tq.tq_decode_attention_fused(c, q, scale, out, ws, seq_lens_host=L)
+
     def step(i):
         c = caches[i % n_copies]
         tq.tq_encode_append(c, kn, vn, seq_lens_host=pre)
-        tq.tq_rotate_q(c, q, q_rot)
-        tq.tq_decode_attention(c, q_rot, scale, out_rot, ws, seq_lens_host=L, variant=args.variant)
-        tq.tq_inverse_rotate_out(c, out_rot, out)
+        if args.separate:
+            tq.tq_rotate_q(c, q, q_rot)
+            decode_call(c)
+            tq.tq_inverse_rotate_out(c, out_rot, out)
+        else:
+            decode_call(c)
 
     use_graph = not args.no_graph
     graph = None
@@ -237,7 +256,7 @@ def main():
     # ---- decode-call duration by HIP events on the launch stream.  Events cannot be
     # recorded inside a captured graph here, so the calls are enqueued eagerly behind a
     # GPU sleep long enough for the host to queue them all: they then run back to back
-    # and each event pair brackets exactly one call (split-K kernel + LSE combine).
+    # and each event pair brackets exactly one call (split-K kernel + LSE merge).
     call_ms = []
     n_calls = min(per_graph, 512)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
@@ -245,7 +264,7 @@ def main():
     for i in range(n_calls):
         c = caches[i % n_copies]
         ev[i][0].record()
-        tq.tq_decode_attention(c, q_rot, scale, out_rot, ws, seq_lens_host=L, variant=args.variant)
+        decode_call(c)
         ev[i][1].record()
     torch.cuda.synchronize()
     call_ms = [a.elapsed_time(b) for a, b in ev]
@@ -258,7 +277,9 @@ def main():
     achieved = alg / (dec_ms * 1e-3) / 1e9 if call_ms else None
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": recorded_traffic(w.name),
-            "kernel": "tq_decode_attention (split-K decode + LSE combine)", "call_us": dec_ms * 1e3,
+            "kernel": ("tq_decode_attention" if args.separate else "tq_decode_attention_fused")
+            + (" (decode_ref_kernel" if args.variant == 1 else " (decode_mfma_kernel") + " + combine_kernel)",
+            "call_us": dec_ms * 1e3,
             "algorithmic_bytes_per_call": alg}
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, seed, args.cpu_seconds)
     line = {
@@ -269,7 +290,8 @@ def main():
         "data": "synthetic (seeded; no model weights)",
         "config": {"workload": w.name, "batch": w.batch, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads,
                    "context_total": int(L.sum()), "k_format": w.k_format, "v_format": w.v_format,
-                   "cache_copies": n_copies, "graph": use_graph, "variant": args.variant},
+                   "cache_copies": n_copies, "graph": use_graph,
+                   "path": "separate calls" if args.separate else "fused call", "variant": args.variant},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

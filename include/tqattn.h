@@ -168,6 +168,22 @@ tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_
                                       float* out_rot, void* workspace, size_t workspace_bytes,
                                       int32_t variant, void* stream);
 
+/* The three decode calls in one: tq_rotate_q, tq_decode_attention and
+ * tq_inverse_rotate_out, with the query rotation done inside the decode kernel
+ * and the inverse rotation inside the split merge (two kernels, no q_rot or
+ * out_rot buffers; mlxcel PR #369, "Change": only the [B, Hq, D] output leaves
+ * V's rotated basis).  The result has the same bits as the three separate calls.
+ *   q    device [B][num_q_heads][128], fp32 if q_is_fp32 else fp16 bits,
+ *        unrotated (rotated into K's basis here unless k_format is F16).
+ *   out  device fp16 bits [B][num_q_heads][128], original basis; a sequence of
+ *        length 0 gives (signed) zeros.
+ * seq_lens_host, scale, workspace and the errors are as for tq_decode_attention
+ * (same workspace size).  Always the MFMA kernel. */
+tq_status tq_decode_attention_fused(const tq_cache* cache, const int32_t* seq_lens_host,
+                                    const void* q, int32_t q_is_fp32, int32_t num_q_heads,
+                                    float scale, uint16_t* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* Back to the original basis: out = s_V * H (out_rot) / sqrt(128), rounded to
  * nearest-even fp16 (mlxcel PR #369, "Change": only the small [B, Hq, D]
  * output is inverse-rotated).

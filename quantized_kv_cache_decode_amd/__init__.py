@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     codebook_bits,
     load_library,
     tq_decode_attention,
+    tq_decode_attention_fused,
     tq_decode_workspace_size,
     tq_encode_append,
     tq_inverse_rotate_out,

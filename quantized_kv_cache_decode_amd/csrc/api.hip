@@ -66,17 +66,25 @@ tq_status check_lengths(const tq_cache* c, const int32_t* lens, int32_t extra) {
 }
 
 #ifndef TQ_PLAN_MIN_CHUNK
-#define TQ_PLAN_MIN_CHUNK 256   // shortest split, tokens (a multiple of 128)
+#define TQ_PLAN_MIN_CHUNK 128   // shortest split, tokens (a multiple of 64)
+#endif
+#ifndef TQ_PLAN_ITEMS_SMALL_GROUP
+#define TQ_PLAN_ITEMS_SMALL_GROUP 2048   // work items aimed for, group size <= 4
 #endif
 #ifndef TQ_PLAN_ITEMS
-#define TQ_PLAN_ITEMS 2048      // work items the plan aims for
+#define TQ_PLAN_ITEMS 4096               // work items aimed for, group size > 4
+#endif
+#ifndef TQ_PLAN_FLOOR
+#define TQ_PLAN_FLOOR 260   // bandwidth-bound calls: chunk >= TQ_PLAN_FLOOR * group tokens
 #endif
 
-// Split plan shared by the workspace query and the launch.  About TQ_PLAN_ITEMS
-// work items over the chip (8 per CU), each a multiple of 128 tokens.  Once the call
-// is bandwidth-bound (>= 4M token-heads) the chunk is also kept long enough that
-// the partials (G x 130 floats, written then read) stay under ~4% of the packed
-// bytes of the chunk.
+// Split plan shared by the workspace query and the launch.  A fixed number of
+// work items over the chip, each a multiple of 64 tokens: 2048 (2 waves per SIMD,
+// all the decode kernel's register budget allows for group sizes <= 4) or 4096
+// (its leaner variants for larger groups fit 3-4 waves per SIMD, and smaller items
+// also even out ragged lengths).  Once the call is bandwidth-bound (>= 4M
+// token-heads) the chunk is also kept long enough that the partials (G x 130
+// floats, written then read) stay under ~4% of the packed bytes of the chunk.
 tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
   long long total = 0;
   int lmax = 0;
@@ -84,9 +92,10 @@ tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
     total += (long long)lens[b] * c->num_kv_heads;
     lmax = std::max(lmax, (int)lens[b]);
   }
-  long long chunk = (total + TQ_PLAN_ITEMS - 1) / TQ_PLAN_ITEMS;
-  if (total >= (4LL << 20)) chunk = std::max(chunk, 260LL * group);
-  chunk = std::max((long long)TQ_PLAN_MIN_CHUNK, (chunk + 127) / 128 * 128);
+  const long long items = group <= 4 ? TQ_PLAN_ITEMS_SMALL_GROUP : TQ_PLAN_ITEMS;
+  long long chunk = (total + items - 1) / items;
+  if (total >= (4LL << 20)) chunk = std::max(chunk, (long long)TQ_PLAN_FLOOR * group);
+  chunk = std::max((long long)TQ_PLAN_MIN_CHUNK, (chunk + 63) / 64 * 64);
   tq::DecodePlan p;
   p.chunk = (int)chunk;
   p.max_splits = std::max(1, (int)((lmax + chunk - 1) / chunk));
@@ -180,20 +189,20 @@ size_t tq_decode_workspace_size(const tq_cache* cache, int32_t num_q_heads, cons
   return workspace_bytes(cache, num_q_heads, make_plan(cache, seq_lens_host, num_q_heads / cache->num_kv_heads));
 }
 
-tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_lens_host, const float* q_rot,
-                                      int32_t num_q_heads, float scale, float* out_rot, void* workspace,
-                                      size_t ws_bytes, int32_t variant, void* stream) {
+namespace {
+
+// Validation and argument set-up shared by the decode entry points.
+tq_status decode_setup(const tq_cache* cache, const int32_t* seq_lens_host, int32_t num_q_heads, float scale,
+                       void* workspace, size_t ws_bytes, tq::DecodeArgs& a) {
   tq_status st = check_cache(cache);
   if (st != TQ_OK) return st;
   if ((st = check_heads(cache, num_q_heads)) != TQ_OK) return st;
   if ((st = check_lengths(cache, seq_lens_host, 0)) != TQ_OK) return st;
-  if (!q_rot || !out_rot) return fail(TQ_EINVAL, "q_rot / out_rot is NULL");
-  if (variant < 0 || variant > 2) return fail(TQ_EINVAL, "unknown decode variant %d", variant);
   const tq::DecodePlan plan = make_plan(cache, seq_lens_host, num_q_heads / cache->num_kv_heads);
   const size_t need = workspace_bytes(cache, num_q_heads, plan);
   if (!workspace || ws_bytes < need)
     return fail(TQ_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
-  tq::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
   a.hkv = cache->num_kv_heads;
   a.cap = cache->capacity;
   a.kfmt = cache->k_format;
@@ -208,9 +217,24 @@ tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_
   a.seq_lens = cache->seq_lens;
   a.k_cb = cache->k_codebook;
   a.v_cb = cache->v_codebook;
-  a.q_rot = q_rot;
+  a.k_signs = cache->k_signs;
+  a.v_signs = cache->v_signs;
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + (size_t)cache->batch * cache->num_kv_heads * plan.max_splits * a.group * 128;
+  return TQ_OK;
+}
+
+}  // namespace
+
+tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_lens_host, const float* q_rot,
+                                      int32_t num_q_heads, float scale, float* out_rot, void* workspace,
+                                      size_t ws_bytes, int32_t variant, void* stream) {
+  tq::DecodeArgs a;
+  tq_status st = decode_setup(cache, seq_lens_host, num_q_heads, scale, workspace, ws_bytes, a);
+  if (st != TQ_OK) return st;
+  if (!q_rot || !out_rot) return fail(TQ_EINVAL, "q_rot / out_rot is NULL");
+  if (variant < 0 || variant > 2) return fail(TQ_EINVAL, "unknown decode variant %d", variant);
+  a.q_rot = q_rot;
   a.out_rot = out_rot;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // variant 0 (default) is the MFMA kernel, 1 the plain VALU reference kernel;
@@ -218,6 +242,22 @@ tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_
   hipError_t e = (variant == 1) ? tq::launch_decode_reference(a, cache->batch, s)
                                 : tq::launch_decode_mfma(a, cache->batch, s);
   if ((st = hip_status(e, "decode launch")) != TQ_OK) return st;
+  return hip_status(tq::launch_combine(a, cache->batch, s), "combine launch");
+}
+
+tq_status tq_decode_attention_fused(const tq_cache* cache, const int32_t* seq_lens_host, const void* q,
+                                    int32_t q_is_fp32, int32_t num_q_heads, float scale, uint16_t* out,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  tq::DecodeArgs a;
+  tq_status st = decode_setup(cache, seq_lens_host, num_q_heads, scale, workspace, ws_bytes, a);
+  if (st != TQ_OK) return st;
+  if (!q || !out) return fail(TQ_EINVAL, "q / out is NULL");
+  a.q_in = q;
+  a.q_fp32 = q_is_fp32 != 0;
+  a.q_rotate = cache->k_format != TQ_FMT_F16;
+  a.out = out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(tq::launch_decode_mfma(a, cache->batch, s), "decode launch")) != TQ_OK) return st;
   return hip_status(tq::launch_combine(a, cache->batch, s), "combine launch");
 }
 

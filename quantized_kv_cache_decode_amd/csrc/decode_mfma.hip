@@ -30,6 +30,8 @@
 // (V), never the operands.
 #include <math.h>
 
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_launch.h"
 
@@ -41,11 +43,11 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Build-time tuning knobs (defaults are the measured best; see the design notes).
-#ifndef TQ_MFMA_PREFETCH
-#define TQ_MFMA_PREFETCH 1   // 1: request the next iteration's words mid-iteration
-#endif
 #ifndef TQ_MFMA_NS_SMALL_GROUP
 #define TQ_MFMA_NS_SMALL_GROUP 4   // token sets per MFMA for group sizes <= 4 (4 or 2)
+#endif
+#ifndef TQ_MFMA_V_FENCE
+#define TQ_MFMA_V_FENCE 0
 #endif
 #ifndef TQ_MFMA_LAZY_RESCALE
 #define TQ_MFMA_LAZY_RESCALE 1
@@ -193,40 +195,6 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const uint16_t* knorm = KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap);
   const uint16_t* vnorm = a.v_norms + row * size_t(a.cap);
 
-  // q in this lane's score-MFMA B slots: q[hn][part*128/P + 8kk + t] * scale*log2(e),
-  // zero unless the lane's k-slots belong to its column's set (loads are unconditional).
-  // Kept in VGPRs: staging these operands in LDS measured slower.
-  half8 qb[NKK];
-  {
-    const bool use = hn < G && sig == sn;
-    const float* qrow = a.q_rot + ((size_t(b) * a.hkv + h) * G + min(hn, G - 1)) * kDim + part * (kDim / P);
-    const float f = use ? a.scale * kLog2e : 0.f;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const float4 x0 = reinterpret_cast<const float4*>(qrow + 8 * kk)[0];
-      const float4 x1 = reinterpret_cast<const float4*>(qrow + 8 * kk)[1];
-      qb[kk] = half8{_Float16(x0.x * f), _Float16(x0.y * f), _Float16(x0.z * f), _Float16(x0.w * f),
-                     _Float16(x1.x * f), _Float16(x1.y * f), _Float16(x1.z * f), _Float16(x1.w * f)};
-    }
-  }
-  ByteTable ktab, vtab;
-  {
-    uint16_t c[8];
-    if (KFMT != kFmtF16) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = a.k_cb[(KFMT == kFmtTurbo4 ? 8 : 0) + i];
-      ktab = make_table(c);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = a.v_cb[(VFMT == kFmtTurbo4 ? 8 : 0) + i];
-    vtab = make_table(c);
-  }
-
-  floatx4 acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
   // Register double-buffering by rotation: the K words of iteration i+1 are
   // requested as soon as iteration i's K has been turned into MFMA operands, and
   // the V words and norms of i+1 as soon as i's values are accumulated, so every
@@ -255,16 +223,74 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) nv[rb] = *reinterpret_cast<const uint2*>(vnorm + tn + 16 * rb + 4 * g);
   };
-  if (TQ_MFMA_PREFETCH) {
-    load_k(t0);
-    load_v(t0);
+  // The first iteration's words are requested before anything else; the q
+  // staging below runs while they are in flight.
+  load_k(t0);
+  load_v(t0);
+
+  // The G query rows of this KV head go through LDS: either the fp32 rows already
+  // in K's basis, or the caller's unrotated rows, rotated here with the same
+  // 16-lane Walsh-Hadamard routine the stand-alone rotation uses (so both routes
+  // give identical bits).
+  __shared__ float qs[kMaxGroup][kDim];
+  const size_t qrow0 = row * G;  // first query row of this KV head
+  if (a.q_in) {
+    const int j = lane & 15;
+    for (int r0 = 0; r0 < G; r0 += 4) {
+      const int r = r0 + (lane >> 4);
+      if (r < G) {  // whole 16-lane segments
+        float v[8];
+        load_row8(a.q_in, a.q_fp32 != 0, (qrow0 + r) * kDim + 8 * j, v);
+        if (a.q_rotate) rotate_row_forward(v, a.k_signs, j);
+        float4* d = reinterpret_cast<float4*>(&qs[r][8 * j]);
+        d[0] = make_float4(v[0], v[1], v[2], v[3]);
+        d[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(a.q_rot + qrow0 * kDim);
+    for (int i = lane; i < G * (kDim / 4); i += 64) reinterpret_cast<float4*>(&qs[0][0])[i] = src[i];
+  }
+  __syncthreads();
+
+  // q in this lane's score-MFMA B slots: q[hn][part*128/P + 8kk + t] * scale*log2(e),
+  // zero unless the lane's k-slots belong to its column's set.
+  // Kept in VGPRs: reading these operands from LDS inside the loop measured slower.
+  half8 qb[NKK];
+  {
+    const bool use = hn < G && sig == sn;
+    const float* qrow = &qs[min(hn, G - 1)][part * (kDim / P)];
+    const float f = use ? a.scale * kLog2e : 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const float4 x0 = reinterpret_cast<const float4*>(qrow + 8 * kk)[0];
+      const float4 x1 = reinterpret_cast<const float4*>(qrow + 8 * kk)[1];
+      qb[kk] = half8{_Float16(x0.x * f), _Float16(x0.y * f), _Float16(x0.z * f), _Float16(x0.w * f),
+                     _Float16(x1.x * f), _Float16(x1.y * f), _Float16(x1.z * f), _Float16(x1.w * f)};
+    }
+  }
+  ByteTable ktab, vtab;
+  {
+    uint16_t c[8];
+    if (KFMT != kFmtF16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = a.k_cb[(KFMT == kFmtTurbo4 ? 8 : 0) + i];
+      ktab = make_table(c);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = a.v_cb[(VFMT == kFmtTurbo4 ? 8 : 0) + i];
+    vtab = make_table(c);
   }
 
-  for (int base = t0; base < t1; base += TOK) {
-    if (!TQ_MFMA_PREFETCH) {
-      load_k(base);
-      load_v(base);
-    }
+  floatx4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // One iteration over TOK tokens from `base`.  TAIL: the iteration reaches past
+  // t1 and the scores of slots >= t1 are masked (only the last one can).
+  auto step = [&](int base, auto tail_c) {
+    constexpr bool TAIL = decltype(tail_c)::value;
     const int tn = ((base >> 5) + sn) << 5;      // first token of this lane's column tile
     // ---- scores (dequant of each operand right before its MFMA)
     float z[8];
@@ -303,16 +329,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       }
       S[rb] += S2[rb];
     }
-    if (TQ_MFMA_PREFETCH) load_k(base + TOK);     // next iteration's K words and K norms
+    load_k(base + TOK);     // next iteration's K words and K norms
 
     // ---- online softmax (log2 domain) for the 8 tokens of this lane's column
-    const bool tail = base + TOK > t1;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float v = S[rb][j] * z[4 * rb + j];
-        if (tail && tn + 16 * rb + 4 * g + j >= t1) v = -INFINITY;
+        if (TAIL && tn + 16 * rb + 4 * g + j >= t1) v = -INFINITY;
         z[4 * rb + j] = v;
       }
     }
@@ -329,6 +354,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       for (int i = 0; i < 8; ++i) acc[i] *= alpha;
     }
     m_run = m_new;
+    // p = 2^(z - m); a masked slot has z = -inf and p = +0 exactly, and so does
+    // p * n_V (norms are finite), so no select is needed.
     float psum = 0.f;
     half8 pb;
 #pragma unroll
@@ -339,8 +366,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         const float p = __builtin_amdgcn_exp2f(z[i] - m_use);
         psum += p;
         const uint32_t w = j < 2 ? nv[rb].x : nv[rb].y;
-        const float pn = p * half_bits_to_float(uint16_t(w >> (16 * (j & 1))));
-        pb[i] = _Float16(z[i] == -INFINITY ? 0.f : pn);
+        pb[i] = _Float16(p * half_bits_to_float(uint16_t(w >> (16 * (j & 1)))));
       }
     }
     l_run += psum;
@@ -368,8 +394,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         acc[nb] = mfma(A, bsg, acc[nb]);
       }
     }
-    if (TQ_MFMA_PREFETCH) load_v(base + TOK);     // next iteration's V words and V norms
-  }
+#if TQ_MFMA_V_FENCE
+    __builtin_amdgcn_sched_barrier(0);  // keep the V requests after this iteration's PV
+#endif
+    load_v(base + TOK);     // next iteration's V words and V norms
+  };
+
+  int base = t0;
+  for (; base + TOK <= t1; base += TOK) step(base, std::false_type{});
+  if (base < t1) step(base, std::true_type{});
 
   // ---- finish: sum l over the column's 4 lanes, merge the NS sets of each head
   float l_tot = xsum4(l_run);

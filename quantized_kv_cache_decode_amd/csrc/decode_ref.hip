@@ -199,63 +199,6 @@ __global__ __launch_bounds__(256) void decode_ref_kernel(DecodeArgs a) {
   }
 }
 
-// Log-sum-exp merge of the splits of one (sequence, query head).  128 threads:
-// the split maxima are reduced in parallel, each chunk of up to 128 splits has its
-// weights exp(m_s - M) computed once into LDS, and thread d sums its dim over
-// the chunk with independent loads.
-__device__ inline float block128_max(float v, float* red) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const float r = fmaxf(red[0], red[1]);
-  __syncthreads();
-  return r;
-}
-
-__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
-  const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int G = a.group;
-  const int h = hq / G, g = hq % G;
-  const int L = min(a.seq_lens[b], a.cap);
-  const int nsplit = min((L + a.plan.chunk - 1) / a.plan.chunk, a.plan.max_splits);
-  const size_t row = size_t(b) * a.hkv + h;
-  const size_t p0 = row * a.plan.max_splits * G + g;   // partial index of split s: p0 + s*G
-  __shared__ float red[2];
-  __shared__ float wsh[128];
-  float M = -INFINITY;
-  for (int s = d; s < nsplit; s += 128) M = fmaxf(M, a.part_ml[(p0 + size_t(s) * G) * 2]);
-  M = block128_max(M, red);
-  float o = 0.f, lsum = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += 128) {
-    const int s = s0 + d;
-    float w = 0.f;
-    if (s < nsplit) {
-      const float ms = a.part_ml[(p0 + size_t(s) * G) * 2];
-      w = ms == -INFINITY ? 0.f : expf(ms - M);
-      lsum += w * a.part_ml[(p0 + size_t(s) * G) * 2 + 1];
-    }
-    wsh[d] = w;
-    __syncthreads();
-    const int cnt = min(128, nsplit - s0);
-    int i = 0;
-    for (; i + 4 <= cnt; i += 4) {
-      const float* q = a.part_o + (p0 + size_t(s0 + i) * G) * kDim + d;
-      const float o0 = q[0], o1 = q[size_t(G) * kDim], o2 = q[size_t(2 * G) * kDim], o3 = q[size_t(3 * G) * kDim];
-      o += wsh[i] * o0 + wsh[i + 1] * o1 + wsh[i + 2] * o2 + wsh[i + 3] * o3;
-    }
-    for (; i < cnt; ++i) o += wsh[i] * a.part_o[(p0 + size_t(s0 + i) * G) * kDim + d];
-    __syncthreads();
-  }
-  // total l: sum of the per-thread partial sums
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) lsum += __shfl_xor(lsum, m, 64);
-  if ((d & 63) == 0) red[d >> 6] = lsum;
-  __syncthreads();
-  const float ltot = red[0] + red[1];
-  a.out_rot[(size_t(b) * a.hkv * G + hq) * kDim + d] = nsplit > 0 ? o / ltot : 0.f;
-}
-
 template <int KF, int VF>
 void launch_ref(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL((decode_ref_kernel<KF, VF>), grid, dim3(256), 0, stream, a);
@@ -272,11 +215,6 @@ hipError_t launch_decode_reference(const DecodeArgs& a, int batch, hipStream_t s
   else if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo3) launch_ref<kFmtF16, kFmtTurbo3>(a, grid, stream);
   else if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo4) launch_ref<kFmtF16, kFmtTurbo4>(a, grid, stream);
   else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_combine(const DecodeArgs& a, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.hkv * a.group, batch), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,8 +1,5 @@
-// 128-point Walsh-Hadamard transform of rows, in registers: one row per 16
-// lanes, 8 elements per lane (element 8*j + i in lane j, slot i).  Stages over
-// element bits 0..2 are in-lane butterflies; stages over bits 3..6 exchange
-// with lane j ^ 1, 2, 4, 8 inside the 16-lane segment.  Natural (Sylvester)
-// order in and out; normalised by 1/sqrt(128).
+// 128-point Walsh-Hadamard rotations of rows, in registers: one row per 16
+// lanes, 8 elements per lane (fwht128_row); normalised by 1/sqrt(128).
 //
 // tq_rotate_q:          q_rot = H (s_K * q) / sqrt(128)   (fp16 or fp32 in, fp32 out)
 // tq_inverse_rotate_out: out  = s_V * H (o) / sqrt(128)   (fp32 in, fp16 RNE out)
@@ -14,30 +11,6 @@
 namespace tq {
 namespace {
 
-constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
-
-__device__ inline void fwht128_row(float v[8], int lane16) {
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (!(i & h)) {
-        const float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float o = __shfl_xor(v[i], m, 16);
-      v[i] = (lane16 & m) ? (o - v[i]) : (v[i] + o);
-    }
-  }
-}
-
 template <bool IN_FP32, bool ROTATE>
 __global__ __launch_bounds__(256) void rotate_q_kernel(const void* __restrict__ q, const float* __restrict__ signs,
                                                        float* __restrict__ q_rot, int rows) {
@@ -46,26 +19,8 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(const void* __restrict__ 
   if (row >= rows) return;  // whole 16-lane segments leave together
   float v[8];
   const size_t base = size_t(row) * kDim + 8 * lane16;
-  if (IN_FP32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q) + base);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + base);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = half_bits_to_float(uint16_t(w[i] & 0xffffu));
-      v[2 * i + 1] = half_bits_to_float(uint16_t(w[i] >> 16));
-    }
-  }
-  if (ROTATE) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] *= signs[8 * lane16 + i];
-    fwht128_row(v, lane16);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] *= kInvSqrtD;
-  }
+  load_row8(q, IN_FP32, base, v);
+  if (ROTATE) rotate_row_forward(v, signs, lane16);
   float4* o = reinterpret_cast<float4*>(q_rot + base);
   o[0] = make_float4(v[0], v[1], v[2], v[3]);
   o[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -81,14 +36,8 @@ __global__ __launch_bounds__(256) void inverse_rotate_kernel(const float* __rest
   const float4* p = reinterpret_cast<const float4*>(o_rot + base);
   const float4 a = p[0], b = p[1];
   float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  fwht128_row(v, lane16);
   uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float x0 = v[2 * i] * kInvSqrtD * signs[8 * lane16 + 2 * i];
-    const float x1 = v[2 * i + 1] * kInvSqrtD * signs[8 * lane16 + 2 * i + 1];
-    w[i] = uint32_t(__half_as_ushort(__float2half_rn(x0))) | (uint32_t(__half_as_ushort(__float2half_rn(x1))) << 16);
-  }
+  rotate_row_inverse_f16(v, signs, lane16, w);
   *reinterpret_cast<uint4*>(out + base) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 

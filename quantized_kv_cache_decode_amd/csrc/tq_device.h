@@ -71,4 +71,73 @@ __host__ __device__ inline uint32_t oct4_pack(const uint8_t* idx) {
 
 __device__ inline float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
+constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
+
+// Unnormalised 128-point Walsh-Hadamard transform of one row held by 16 lanes,
+// 8 elements per lane (element 8*j + i in lane j = lane16, slot i).  Stages over
+// element bits 0..2 are in-lane butterflies; stages over bits 3..6 exchange with
+// lane j ^ 1, 2, 4, 8 of the same aligned 16-lane segment, so all 16 lanes of a
+// segment must execute it together.  Natural (Sylvester) order in and out.  Every
+// kernel that rotates uses this one routine, so rotations done inside different
+// kernels round identically.
+__device__ inline void fwht128_row(float v[8], int lane16) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (!(i & h)) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float o = __shfl_xor(v[i], m, 16);
+      v[i] = (lane16 & m) ? (o - v[i]) : (v[i] + o);
+    }
+  }
+}
+
+// The 8 elements 8*lane16 .. 8*lane16+7 of a row of fp32 or fp16-bit values.
+__device__ inline void load_row8(const void* base, bool fp32, size_t off, float v[8]) {
+  if (fp32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = half_bits_to_float(uint16_t(w[i] & 0xffffu));
+      v[2 * i + 1] = half_bits_to_float(uint16_t(w[i] >> 16));
+    }
+  }
+}
+
+// q into K's codec basis: v = H (s * v) / sqrt(128), in place (16-lane row layout).
+__device__ inline void rotate_row_forward(float v[8], const float* signs, int lane16) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] *= signs[8 * lane16 + i];
+  fwht128_row(v, lane16);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] *= kInvSqrtD;
+}
+
+// Out of V's codec basis and into fp16: s * H (v) / sqrt(128), nearest-even fp16
+// bits packed in pairs (element 8*lane16 + 2i in the low half of w[i]).
+__device__ inline void rotate_row_inverse_f16(float v[8], const float* signs, int lane16, uint32_t w[4]) {
+  fwht128_row(v, lane16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x0 = v[2 * i] * kInvSqrtD * signs[8 * lane16 + 2 * i];
+    const float x1 = v[2 * i + 1] * kInvSqrtD * signs[8 * lane16 + 2 * i + 1];
+    w[i] = uint32_t(__half_as_ushort(__float2half_rn(x0))) | (uint32_t(__half_as_ushort(__float2half_rn(x1))) << 16);
+  }
+}
+
 }  // namespace tq

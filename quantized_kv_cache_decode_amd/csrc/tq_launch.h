@@ -58,10 +58,16 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const uint16_t* k_cb;
   const uint16_t* v_cb;
-  const float* q_rot;       // [B][Hq][128]
+  const float* q_rot;       // [B][Hq][128] fp32, already in K's basis (when q_in is NULL)
+  const void* q_in;         // [B][Hq][128] unrotated q (fp32 or fp16 bits), rotated in-kernel; or NULL
+  int q_fp32;               // q_in is fp32 (else fp16 bits)
+  int q_rotate;             // q_in goes through H(s_K * q)/sqrt(128) (quantised K formats)
+  const float* k_signs;
+  const float* v_signs;
   float* part_o;            // [B*Hkv*max_splits][group][128]
   float* part_ml;           // [B*Hkv*max_splits][group][2]
-  float* out_rot;           // [B][Hq][128]
+  float* out_rot;           // [B][Hq][128] fp32 in V's basis, or NULL when `out` is written
+  uint16_t* out;            // [B][Hq][128] fp16 bits in the original basis, or NULL
 };
 
 hipError_t launch_decode_reference(const DecodeArgs& a, int batch, hipStream_t stream);

@@ -88,20 +88,26 @@ def oracle_end_to_end(w, k16, v16, L, q_b, codebooks, seed=0):
     return reference.decode_sequence(q_b, k_hat, v_hat, L)
 
 
-def gpu_decode(cache, q_np, variant=0, q_fp32=None):
-    """Run tq_rotate_q -> tq_decode_attention -> tq_inverse_rotate_out; returns fp16 [B, Hq, 128] as numpy."""
+def gpu_decode(cache, q_np, variant=0):
+    """Decode of q [B, Hq, 128] through the C ABI; returns fp16 [B, Hq, 128] as numpy.
+
+    variant 0/1/2: tq_rotate_q -> tq_decode_attention(variant) -> tq_inverse_rotate_out;
+    "fused": tq_decode_attention_fused (rotations inside the decode and merge kernels)."""
     import torch
 
     import quantized_kv_cache_decode_amd as tq
     q = torch.from_numpy(np.ascontiguousarray(q_np)).to("cuda")
     B, Hq, _ = q.shape
-    q_rot = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
-    out_rot = torch.empty_like(q_rot)
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
     ws = torch.zeros(tq.tq_decode_workspace_size(cache, Hq), dtype=torch.uint8, device="cuda")
-    tq.tq_rotate_q(cache, q, q_rot)
-    tq.tq_decode_attention(cache, q_rot, SCALE, out_rot, ws, variant=variant)
-    tq.tq_inverse_rotate_out(cache, out_rot, out)
+    if variant == "fused":
+        tq.tq_decode_attention_fused(cache, q, SCALE, out, ws)
+    else:
+        q_rot = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+        out_rot = torch.empty_like(q_rot)
+        tq.tq_rotate_q(cache, q, q_rot)
+        tq.tq_decode_attention(cache, q_rot, SCALE, out_rot, ws, variant=variant)
+        tq.tq_inverse_rotate_out(cache, out_rot, out)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 

@@ -19,7 +19,7 @@ from tests import support as S
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [1, 2]
+VARIANTS = [1, 2, "fused"]
 
 
 def _say(*a):
@@ -166,12 +166,27 @@ def test_workspace_reused_across_calls(variant, codebooks):
         v[0] = np.concatenate([v[0], vn], axis=1)
         L = int(cache.lengths[0])
         q = queries(w, 2, step)
-        tq.tq_rotate_q(cache, torch.from_numpy(q).cuda(), q_rot)
-        tq.tq_decode_attention(cache, q_rot, S.SCALE, out_rot, ws, variant=variant)
-        tq.tq_inverse_rotate_out(cache, out_rot, out)
+        if variant == "fused":
+            tq.tq_decode_attention_fused(cache, torch.from_numpy(q).cuda(), S.SCALE, out, ws)
+        else:
+            tq.tq_rotate_q(cache, torch.from_numpy(q).cuda(), q_rot)
+            tq.tq_decode_attention(cache, q_rot, S.SCALE, out_rot, ws, variant=variant)
+            tq.tq_inverse_rotate_out(cache, out_rot, out)
         torch.cuda.synchronize()
         S.assert_close(out.cpu().numpy()[0], S.oracle_end_to_end(w, k[0], v[0], L, q[0], codebooks, seed=2),
                        f"step {step} L={L}")
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3s", "c4s"])
+def test_fused_call_matches_separate_calls_bitwise(name):
+    """tq_decode_attention_fused == tq_rotate_q + tq_decode_attention + tq_inverse_rotate_out,
+    bit for bit (the same rotation routine and merge arithmetic run inside the fused kernels);
+    the workloads cover fp32 q (c0) and fp16 q, and the unrotated fp16-K mode (c2)."""
+    w, lens = _small_workloads()[name]
+    cache, _, _, _, q = S.prefill_and_step(w, lengths=lens)
+    sep = S.gpu_decode(cache, q, variant=2)
+    fused = S.gpu_decode(cache, q, variant="fused")
+    np.testing.assert_array_equal(fused.view(np.uint16), sep.view(np.uint16))
 
 
 def test_decode_does_not_mutate_cache():

@@ -148,12 +148,20 @@ def test_workspace_grows_with_context(lib):
 ])
 def test_partials_are_small_next_to_the_cache(lib, batch, hkv, hq, lens, bytes_per_token):
     """In the bandwidth-bound regime the split partials (written once, read once) stay
-    under 5% of the packed K+V bytes a decode call streams."""
+    under 5% of the packed K+V bytes a decode call streams.  The workspace holds
+    max_splits partials per (sequence, KV head); the splits actually written are
+    bounded through the smallest chunk consistent with that max_splits."""
     d = _desc(batch=batch, num_kv_heads=hkv, capacity=131072)
     a, p = _lens(*lens)
     ws = lib.tq_decode_workspace_size(ctypes.byref(d), hq, p)
+    group = hq // hkv
+    per_item = group * 130 * 4
+    assert ws % (batch * hkv * per_item) == 0
+    max_splits = ws // (batch * hkv * per_item)
+    chunk_min = -(-max(lens) // max_splits)
+    items = sum(hkv * -(-int(L) // chunk_min) for L in lens)
     kv = sum(lens) * hkv * bytes_per_token
-    assert 2 * ws < 0.05 * kv
+    assert 2 * items * per_item < 0.05 * kv
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):

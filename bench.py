@@ -1,11 +1,16 @@
 """Benchmark of one decode step of the rotated-codec KV cache on one MI355X.
 
-A step is the whole hot path for one new token per sequence:
-  tq_encode_append (1 token) -> tq_decode_attention_fused
-(q rotation inside the split-K decode kernel, LSE merge + inverse rotation in the
-merge kernel); --separate runs the four calls tq_encode_append -> tq_rotate_q ->
-tq_decode_attention -> tq_inverse_rotate_out instead.  Inputs are seeded synthetic inputs of the Qwen2.5-7B-shaped layer (B=1, Hq=28, Hkv=4,
-head dim 128, 8192 visible tokens, turbo3 K and V) unless --workload says
+A step is the whole hot path for one new token per sequence: append it (encode
+K and V rows: rotate, norm, nearest centroid, pack), rotate q, split-K decode over
+all visible tokens, LSE merge, inverse-rotate the output.  --path picks the calls:
+  step      tq_decode_step: two kernels; the token is appended by extra work
+            groups of the decode kernel while the splits stream the older tokens
+            (default);
+  fused     tq_encode_append -> tq_decode_attention_fused (three kernels);
+  separate  tq_encode_append -> tq_rotate_q -> tq_decode_attention ->
+            tq_inverse_rotate_out (five kernels).
+Inputs are seeded synthetic ones of the Qwen2.5-7B-shaped layer (B=1, Hq=28,
+Hkv=4, head dim 128, 8192 visible tokens, turbo3 K and V) unless --workload says
 otherwise.  The cache is replicated into distinct HBM copies (>= 1 GiB in all)
 and the steps rotate through them, so every step streams its cache from HBM
 rather than from the 256 MB Infinity Cache (each copy stands for another layer
@@ -44,10 +49,10 @@ def parse():
     p.add_argument("--steps", type=int, default=3200)
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--workload", type=int, default=1, help="workload index (0..4); default the 8K Qwen2.5-7B layer")
-    p.add_argument("--separate", action="store_true",
-                   help="four separate calls per step instead of tq_decode_attention_fused")
+    p.add_argument("--path", choices=("step", "fused", "separate"), default="step",
+                   help="calls per step (see the module docstring)")
     p.add_argument("--variant", type=int, default=0,
-                   help="decode kernel variant of --separate (0 default = MFMA, 1 VALU reference)")
+                   help="decode kernel variant of --path separate (0 default = MFMA, 1 VALU reference)")
     p.add_argument("--copies-gib", type=float, default=1.0, help="total size of the rotated cache copies")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
@@ -188,7 +193,8 @@ def main():
     q_rot = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
     out_rot = torch.empty_like(q_rot)
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
-    ws = torch.zeros(tq.tq_decode_workspace_size(master, Hq, L), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(tq.tq_decode_workspace_size(master, Hq, L), tq.tq_decode_workspace_size(master, Hq, pre)),
+                     dtype=torch.uint8, device="cuda")
     scale = 1.0 / math.sqrt(128.0)
     per_graph = n_copies
     # a plain 512 MiB device copy (setup, untimed): its FETCH_SIZE / WRITE_SIZE counters
@@ -197,24 +203,30 @@ def main():
     calib.copy_(torch.ones_like(calib))
     del calib
 
-    if args.variant and not args.separate:
-        sys.exit("--variant applies to --separate only")
+    if args.variant and args.path != "separate":
+        sys.exit("--variant applies to --path separate only")
+    sep = args.path == "separate"
 
     def decode_call(c):
-        if args.separate:
+        """The timed call: append + decode for the step path, decode alone otherwise."""
+        if args.path == "step":
+            tq.tq_decode_step(c, kn, vn, q, scale, out, ws, seq_lens_host=pre)
+        elif sep:
             tq.tq_decode_attention(c, q_rot, scale, out_rot, ws, seq_lens_host=L, variant=args.variant)
         else:
             tq.tq_decode_attention_fused(c, q, scale, out, ws, seq_lens_host=L)
 
     def step(i):
+        # Every step writes the same token into slot L-1 of its cache copy and attends over
+        # L tokens, so replays are idempotent and the copies keep their length.
         c = caches[i % n_copies]
-        tq.tq_encode_append(c, kn, vn, seq_lens_host=pre)
-        if args.separate:
+        if args.path != "step":
+            tq.tq_encode_append(c, kn, vn, seq_lens_host=pre)
+        if sep:
             tq.tq_rotate_q(c, q, q_rot)
-            decode_call(c)
+        decode_call(c)
+        if sep:
             tq.tq_inverse_rotate_out(c, out_rot, out)
-        else:
-            decode_call(c)
 
     use_graph = not args.no_graph
     graph = None
@@ -277,7 +289,8 @@ def main():
     achieved = alg / (dec_ms * 1e-3) / 1e9 if call_ms else None
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": recorded_traffic(w.name),
-            "kernel": ("tq_decode_attention" if args.separate else "tq_decode_attention_fused")
+            "kernel": {"step": "tq_decode_step", "fused": "tq_decode_attention_fused",
+                       "separate": "tq_decode_attention"}[args.path]
             + (" (decode_ref_kernel" if args.variant == 1 else " (decode_mfma_kernel") + " + combine_kernel)",
             "call_us": dec_ms * 1e3,
             "algorithmic_bytes_per_call": alg}
@@ -291,7 +304,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads,
                    "context_total": int(L.sum()), "k_format": w.k_format, "v_format": w.v_format,
                    "cache_copies": n_copies, "graph": use_graph,
-                   "path": "separate calls" if args.separate else "fused call", "variant": args.variant},
+                   "path": args.path, "variant": args.variant},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -30,7 +30,8 @@
  *     thread.
  *   - Query head h attends KV head h / (num_q_heads / num_kv_heads)
  *     (contiguous GQA groups).  Group sizes 1..16 are supported.
- *   - Only tq_encode_append writes the cache; the other calls read it.
+ *   - Only tq_encode_append and tq_decode_step write the cache; the other
+ *     calls read it.
  *
  * Byte layouts (this library's own; the pages print none):
  *   turbo4 octet word: 8 codes in one little-endian u32; code e (0..3) in bits
@@ -82,8 +83,10 @@ typedef enum {
  *   k_norms  fp16 bits [B][Hkv][capacity]; NULL when k_format == TQ_FMT_F16.
  *   v_data   u8 [B][Hkv][capacity/32][1536 | 2048] V tiles.
  *   v_norms  fp16 bits [B][Hkv][capacity].
- *   seq_lens int32 [B]: visible tokens per sequence (the cache "offset");
- *            written by tq_encode_append, read by tq_decode_attention.
+ *   seq_lens int32 [B]: visible tokens per sequence (the cache "offset"),
+ *            kept up to date by tq_encode_append and tq_decode_step for callers
+ *            that read it on the device; the decode calls take the lengths from
+ *            the host.
  *   k_signs, v_signs   float [128] of +1/-1 (k_signs unused for F16 K).
  *   k_codebook, v_codebook   fp16 bits, ascending, 8 (turbo3) or 16 (turbo4)
  *            entries, symmetric (c[i] = -c[n-1-i]); k_codebook unused for F16 K.
@@ -133,9 +136,11 @@ tq_status tq_encode_append(const tq_cache* cache, const int32_t* seq_lens_host,
 tq_status tq_rotate_q(const tq_cache* cache, const void* q, int32_t q_is_fp32,
                       int32_t num_q_heads, float* q_rot, void* stream);
 
-/* Bytes of device workspace tq_decode_attention needs for these lengths:
- * split-K partials (fp32 o, m, l per split and query head).  seq_lens_host:
- * HOST int32 [B].  Returns 0 on invalid arguments (see tq_last_error). */
+/* Bytes of device workspace the decode calls need for these lengths: split-K
+ * partials (fp32 o, m, l per split and query head, plus one slot per (sequence,
+ * KV head) for tq_decode_step's new token).
+ * seq_lens_host: HOST int32 [B].  Returns 0 on invalid arguments (see
+ * tq_last_error). */
 size_t tq_decode_workspace_size(const tq_cache* cache, int32_t num_q_heads,
                                 const int32_t* seq_lens_host);
 
@@ -146,8 +151,10 @@ size_t tq_decode_workspace_size(const tq_cache* cache, int32_t num_q_heads,
  * with k_t = n_K,t * c_K[idx_K,t] (symmetric) or the fp16 K row (F16).
  * Split-K over the context with a per-sequence split count, then a
  * log-sum-exp merge of the splits.
- *   seq_lens_host  HOST int32 [B]; must equal cache->seq_lens (it sizes the
- *                  launch; the kernels read the device lengths).
+ *   seq_lens_host  HOST int32 [B]: the visible lengths to attend over (normally
+ *                  the lengths cache->seq_lens holds).  They size the launch and
+ *                  travel as kernel arguments; the decode calls never read
+ *                  cache->seq_lens.
  *   q_rot          device fp32 [B][num_q_heads][128] (from tq_rotate_q).
  *   out_rot        device fp32 [B][num_q_heads][128]; a sequence of length 0
  *                  gives zeros.
@@ -183,6 +190,34 @@ tq_status tq_decode_attention_fused(const tq_cache* cache, const int32_t* seq_le
                                     const void* q, int32_t q_is_fp32, int32_t num_q_heads,
                                     float scale, uint16_t* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/* One whole decode step: append one new token to every sequence and attend to
+ * all visible tokens, the new one included -- tq_encode_append (t_new = 1)
+ * followed by tq_decode_attention_fused on the grown cache, in two kernels
+ * (three on bandwidth-bound calls, >= 4M visible token-heads, where the
+ * append runs as a launch of its own so the splits fill the chip in one
+ * round).  The new token is encoded and written by two extra work groups per
+ * (sequence, KV head) of the decode kernel, which also take the token's own
+ * softmax partial (its score against every query head of the group, weight 1,
+ * value its reconstructed V row); the regular splits cover the older tokens
+ * in parallel and the split merge folds the extra partial in (mlxcel PR #369,
+ * "Change": the append is the only cache mutation and the rotated-basis route
+ * attends right after it).  Codes, norms and cache->seq_lens end up exactly as
+ * after tq_encode_append; the output agrees with the two-call route up to
+ * rounding (the new token's score is taken in fp32 rather than on the matrix
+ * cores).
+ *   seq_lens_host  HOST int32 [B]: lengths BEFORE the append (= cache->seq_lens);
+ *                  each must be < capacity.
+ *   k_new, v_new   device fp16 [B][Hkv][1][128], the new token's rows.
+ *   q, q_is_fp32, out   as for tq_decode_attention_fused.
+ *   workspace      >= tq_decode_workspace_size(cache, num_q_heads, seq_lens_host)
+ *                  with the lengths before the append.
+ * Errors as for tq_encode_append and tq_decode_attention.  Always the MFMA kernel. */
+tq_status tq_decode_step(const tq_cache* cache, const int32_t* seq_lens_host,
+                         const void* k_new, const void* v_new, const void* q,
+                         int32_t q_is_fp32, int32_t num_q_heads, float scale,
+                         uint16_t* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Back to the original basis: out = s_V * H (out_rot) / sqrt(128), rounded to
  * nearest-even fp16 (mlxcel PR #369, "Change": only the small [B, Hq, D]

@@ -22,8 +22,8 @@ K_RECORD_BYTES = {"turbo3": 48, "turbo4": 64}
 V_TILE_BYTES = {"turbo3": 1536, "turbo4": 2048}
 EXPORTED = (
     "tq_encode_append", "tq_rotate_q", "tq_decode_workspace_size", "tq_decode_attention",
-    "tq_decode_attention_variant", "tq_decode_attention_fused", "tq_inverse_rotate_out", "tq_last_error",
-    "tq_version",
+    "tq_decode_attention_variant", "tq_decode_attention_fused", "tq_decode_step", "tq_inverse_rotate_out",
+    "tq_last_error", "tq_version",
 )
 
 
@@ -63,11 +63,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tq_decode_attention.argtypes = [cp, P, P, I32, F32, P, P, SZ, P]
     lib.tq_decode_attention_variant.argtypes = [cp, P, P, I32, F32, P, P, SZ, I32, P]
     lib.tq_decode_attention_fused.argtypes = [cp, P, P, I32, I32, F32, P, P, SZ, P]
+    lib.tq_decode_step.argtypes = [cp, P, P, P, P, I32, I32, F32, P, P, SZ, P]
     lib.tq_inverse_rotate_out.argtypes = [cp, P, I32, P, P]
     lib.tq_last_error.restype = ctypes.c_char_p
     lib.tq_version.restype = ctypes.c_char_p
     for name in ("tq_encode_append", "tq_rotate_q", "tq_decode_attention", "tq_decode_attention_variant",
-                 "tq_decode_attention_fused",
+                 "tq_decode_attention_fused", "tq_decode_step",
                  "tq_inverse_rotate_out"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
@@ -196,6 +197,21 @@ def tq_decode_attention_fused(cache: Cache, q, scale, out, workspace, seq_lens_h
     _check(load_library().tq_decode_attention_fused(
         cache.desc, p, _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]), float(scale), _ptr(out),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream)))
+
+
+def tq_decode_step(cache: Cache, k_new, v_new, q, scale, out, workspace, seq_lens_host=None, stream=None):
+    """Append one token (k_new, v_new fp16 [B, Hkv, 1, 128]) to every sequence and attend q
+    [B, Hq, 128] over all visible tokens including it; out fp16 [B, Hq, 128].  The workspace is
+    sized with the lengths before the append."""
+    import torch
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
+    if int(k_new.shape[2]) != 1 or int(v_new.shape[2]) != 1:
+        raise ValueError("tq_decode_step appends exactly one token per sequence")
+    _check(load_library().tq_decode_step(
+        cache.desc, p, _ptr(k_new), _ptr(v_new), _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]),
+        float(scale), _ptr(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+        _stream(stream)))
+    cache.lengths = arr + 1
 
 
 def tq_inverse_rotate_out(cache: Cache, out_rot, out, stream=None):

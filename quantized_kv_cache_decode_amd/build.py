@@ -7,6 +7,7 @@ then linked into quantized_kv_cache_decode_amd/libtqattn.so.
 import concurrent.futures as cf
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -25,14 +26,34 @@ DEVICE_FLAGS = [
 ]
 
 
+RESOURCE_REPORT = os.path.join(HERE, "_build", "kernel_resources.txt")
+
+
 def _compile(src, obj):
-    cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *DEVICE_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-fno-caret-diagnostics", "-c", src,
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    noise = ("is not a recognized feature for this target", "kernel-resource-usage")
+    err = "\n".join(l for l in r.stderr.splitlines() if not any(n in l for n in noise))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
-    return err
+    return err, _resources(r.stderr)
+
+
+def _resources(remarks):
+    """(kernel, VGPRs, scratch bytes per lane) from the compiler's resource-usage remarks."""
+    out, name, vgpr = [], None, None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r" VGPRs: (\d+)", line)
+        if m:
+            vgpr = int(m.group(1))
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name:
+            out.append((name, vgpr, int(m.group(1))))
+    return out
 
 
 def build(verbose: bool = True) -> str:
@@ -40,10 +61,14 @@ def build(verbose: bool = True) -> str:
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
     objs = [os.path.join(bdir, os.path.basename(s) + ".o") for s in srcs]
+    report = []
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        for s, msg in zip(srcs, ex.map(_compile, srcs, objs)):
+        for s, (msg, res) in zip(srcs, ex.map(_compile, srcs, objs)):
             if verbose and msg.strip():
                 print(f"[{os.path.basename(s)}]\n{msg}", file=sys.stderr)
+            report += [f"{os.path.basename(s)} {k} vgpr={v} scratch={sc}" for k, v, sc in res]
+    with open(RESOURCE_REPORT, "w") as f:
+        f.write("\n".join(report) + "\n")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

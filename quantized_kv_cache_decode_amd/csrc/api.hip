@@ -94,19 +94,25 @@ tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
   }
   const long long items = group <= 4 ? TQ_PLAN_ITEMS_SMALL_GROUP : TQ_PLAN_ITEMS;
   long long chunk = (total + items - 1) / items;
-  if (total >= (4LL << 20)) chunk = std::max(chunk, (long long)TQ_PLAN_FLOOR * group);
+  const bool bandwidth_bound = total >= (4LL << 20);
+  if (bandwidth_bound) chunk = std::max(chunk, (long long)TQ_PLAN_FLOOR * group);
   chunk = std::max((long long)TQ_PLAN_MIN_CHUNK, (chunk + 63) / 64 * 64);
   tq::DecodePlan p;
   p.chunk = (int)chunk;
   p.max_splits = std::max(1, (int)((lmax + chunk - 1) / chunk));
+  p.slots = p.max_splits + 1;
+  p.bandwidth_bound = bandwidth_bound;
   return p;
 }
 
-// Workspace: split partials o [items][G][128] and (m, l) [items][G][2] (fp32).
+// Workspace: split partials o [items][G][128] and (m, l) [items][G][2] (fp32),
+// items = B * Hkv * slots.
+size_t partial_floats(const tq_cache* c, int32_t num_q_heads, const tq::DecodePlan& p) {
+  return (size_t)c->batch * c->num_kv_heads * p.slots * (num_q_heads / c->num_kv_heads);
+}
+
 size_t workspace_bytes(const tq_cache* c, int32_t num_q_heads, const tq::DecodePlan& p) {
-  const size_t items = (size_t)c->batch * c->num_kv_heads * p.max_splits;
-  const size_t g = num_q_heads / c->num_kv_heads;
-  return items * g * (128 + 2) * sizeof(float);
+  return partial_floats(c, num_q_heads, p) * (128 + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -214,13 +220,46 @@ tq_status decode_setup(const tq_cache* cache, const int32_t* seq_lens_host, int3
   a.k_norms = cache->k_norms;
   a.v_data = static_cast<const uint8_t*>(cache->v_data);
   a.v_norms = cache->v_norms;
-  a.seq_lens = cache->seq_lens;
   a.k_cb = cache->k_codebook;
   a.v_cb = cache->v_codebook;
   a.k_signs = cache->k_signs;
   a.v_signs = cache->v_signs;
   a.part_o = static_cast<float*>(workspace);
-  a.part_ml = a.part_o + (size_t)cache->batch * cache->num_kv_heads * plan.max_splits * a.group * 128;
+  a.part_ml = a.part_o + partial_floats(cache, num_q_heads, plan) * 128;
+  a.col0 = 0;
+  a.split_cols = plan.max_splits;
+  return TQ_OK;
+}
+
+// Launch the decode kernel (variant 1: the VALU reference) and the split merge for
+// every group of up to kAppendChunk sequences, with their host lengths as kernel
+// arguments (the kernels never wait on a length read from memory).
+tq_status launch_decode_and_merge(const tq_cache* cache, const int32_t* seq_lens_host, tq::DecodeArgs& a,
+                                  int variant, hipStream_t s) {
+  for (int b0 = 0; b0 < cache->batch; b0 += tq::kAppendChunk) {
+    const int nb = std::min(tq::kAppendChunk, cache->batch - b0);
+    tq::SeqLens lens;
+    memset(&lens, 0, sizeof(lens));
+    for (int i = 0; i < nb; ++i) lens.len[i] = seq_lens_host[b0 + i];
+    a.b0 = b0;
+    a.app.b0 = b0;
+    tq_status st;
+    if (a.app.k_new && a.plan.bandwidth_bound) {
+      // decode step on a bandwidth-bound call: the token's work groups go first, in a
+      // launch of their own, so the splits still fill the chip in one round
+      tq::DecodeArgs ap = a;
+      ap.col0 = 2;
+      ap.split_cols = 0;
+      if ((st = hip_status(tq::launch_decode_mfma(ap, lens, nb, s), "append launch")) != TQ_OK) return st;
+      a.col0 = 0;
+    } else {
+      a.col0 = a.app.k_new ? 2 : 0;
+    }
+    const hipError_t e = variant == 1 ? tq::launch_decode_reference(a, lens, nb, s)
+                                      : tq::launch_decode_mfma(a, lens, nb, s);
+    if ((st = hip_status(e, "decode launch")) != TQ_OK) return st;
+    if ((st = hip_status(tq::launch_combine(a, lens, nb, s), "combine launch")) != TQ_OK) return st;
+  }
   return TQ_OK;
 }
 
@@ -236,13 +275,9 @@ tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_
   if (variant < 0 || variant > 2) return fail(TQ_EINVAL, "unknown decode variant %d", variant);
   a.q_rot = q_rot;
   a.out_rot = out_rot;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   // variant 0 (default) is the MFMA kernel, 1 the plain VALU reference kernel;
   // both are followed by the log-sum-exp merge of their splits
-  hipError_t e = (variant == 1) ? tq::launch_decode_reference(a, cache->batch, s)
-                                : tq::launch_decode_mfma(a, cache->batch, s);
-  if ((st = hip_status(e, "decode launch")) != TQ_OK) return st;
-  return hip_status(tq::launch_combine(a, cache->batch, s), "combine launch");
+  return launch_decode_and_merge(cache, seq_lens_host, a, variant, static_cast<hipStream_t>(stream));
 }
 
 tq_status tq_decode_attention_fused(const tq_cache* cache, const int32_t* seq_lens_host, const void* q,
@@ -256,9 +291,40 @@ tq_status tq_decode_attention_fused(const tq_cache* cache, const int32_t* seq_le
   a.q_fp32 = q_is_fp32 != 0;
   a.q_rotate = cache->k_format != TQ_FMT_F16;
   a.out = out;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = hip_status(tq::launch_decode_mfma(a, cache->batch, s), "decode launch")) != TQ_OK) return st;
-  return hip_status(tq::launch_combine(a, cache->batch, s), "combine launch");
+  return launch_decode_and_merge(cache, seq_lens_host, a, 0, static_cast<hipStream_t>(stream));
+}
+
+tq_status tq_decode_step(const tq_cache* cache, const int32_t* seq_lens_host, const void* k_new, const void* v_new,
+                         const void* q, int32_t q_is_fp32, int32_t num_q_heads, float scale, uint16_t* out,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  tq::DecodeArgs a;
+  tq_status st = decode_setup(cache, seq_lens_host, num_q_heads, scale, workspace, ws_bytes, a);
+  if (st != TQ_OK) return st;
+  if ((st = check_lengths(cache, seq_lens_host, 1)) != TQ_OK) return st;  // room for the new token
+  if (!k_new || !v_new || !q || !out) return fail(TQ_EINVAL, "k_new / v_new / q / out is NULL");
+  a.q_in = q;
+  a.q_fp32 = q_is_fp32 != 0;
+  a.q_rotate = cache->k_format != TQ_FMT_F16;
+  a.out = out;
+  tq::EncodeArgs& e = a.app;
+  e.hkv = cache->num_kv_heads;
+  e.cap = cache->capacity;
+  e.kfmt = cache->k_format;
+  e.vfmt = cache->v_format;
+  e.t_new = 1;
+  e.b0 = 0;
+  e.k_new = static_cast<const uint16_t*>(k_new);
+  e.v_new = static_cast<const uint16_t*>(v_new);
+  e.k_data = static_cast<uint8_t*>(cache->k_data);
+  e.k_norms = cache->k_norms;
+  e.v_data = static_cast<uint8_t*>(cache->v_data);
+  e.v_norms = cache->v_norms;
+  e.seq_lens = cache->seq_lens;
+  e.k_signs = cache->k_signs;
+  e.v_signs = cache->v_signs;
+  e.k_cb = cache->k_codebook;
+  e.v_cb = cache->v_codebook;
+  return launch_decode_and_merge(cache, seq_lens_host, a, 0, static_cast<hipStream_t>(stream));
 }
 
 tq_status tq_decode_attention(const tq_cache* cache, const int32_t* seq_lens_host, const float* q_rot,

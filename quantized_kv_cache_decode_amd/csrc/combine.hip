@@ -22,38 +22,42 @@ namespace tq {
 namespace {
 
 constexpr int kSplitGroups = 16;
-constexpr int kBatch = 4;  // splits per thread per round of loads
+constexpr int kBatch = 5;  // splits per thread per round of loads (80 per round)
 
 __device__ inline float weight(float m, float M) { return m == -INFINITY ? 0.f : expf(m - M); }
 
 template <bool INVERSE>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, SeqLens lens) {
   // No multiply-add contraction here: the normalised output must round the same
   // whether it goes to memory (then to the stand-alone inverse rotation) or
   // straight into the in-register rotation below.
 #pragma clang fp contract(off)
-  const int hq = blockIdx.x, b = blockIdx.y;
+  const int hq = blockIdx.x, b = a.b0 + blockIdx.y;
   const int G = a.group;
   const int h = hq / G, g = hq % G;
-  const int L = min(a.seq_lens[b], a.cap);
+  // Decode step: the splits cover the tokens before the append and the appended
+  // token has its own slot.
+  const bool step = a.app.k_new != nullptr;
+  const int L = min(lens.len[blockIdx.y], a.cap);
   const int nsplit = min((L + a.plan.chunk - 1) / a.plan.chunk, a.plan.max_splits);
-  const size_t p0 = (size_t(b) * a.hkv + h) * a.plan.max_splits * G + g;  // partial of split s: p0 + s*G
+  const int nparts = nsplit + (step ? 1 : 0);  // partial v lives in slot v, the step's last in slot max_splits
+  const size_t p0 = partial_index(a, size_t(b) * a.hkv + h, 0, g);  // slot s: p0 + s*G
   const int j = threadIdx.x & 15, sg = threadIdx.x >> 4;
 
   float m = -INFINITY, l = 0.f, o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
-  for (int s0 = sg; s0 < nsplit; s0 += kSplitGroups * kBatch) {
+  for (int s0 = sg; s0 < nparts; s0 += kSplitGroups * kBatch) {
     float ms[kBatch], ls[kBatch];
     float4 oa[kBatch], ob[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int s = s0 + kSplitGroups * k;
+      const int v = s0 + kSplitGroups * k;
       ms[k] = -INFINITY;
       ls[k] = 0.f;
       oa[k] = ob[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (s < nsplit) {
-        const size_t p = p0 + size_t(s) * G;
+      if (v < nparts) {
+        const size_t p = p0 + size_t(v < nsplit ? v : a.plan.max_splits) * G;
         const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * p);
         ms[k] = ml.x;
         ls[k] = ml.y;
@@ -105,9 +109,11 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     v[0] += w * x.x; v[1] += w * x.y; v[2] += w * x.z; v[3] += w * x.w;
     v[4] += w * y.x; v[5] += w * y.y; v[6] += w * y.z; v[7] += w * y.w;
   }
-  const float inv = nsplit > 0 ? 1.f / lt : 0.f;
+  const float inv = nparts > 0 ? 1.f / lt : 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = nsplit > 0 ? v[i] * inv : 0.f;
+  for (int i = 0; i < 8; ++i) v[i] = nparts > 0 ? v[i] * inv : 0.f;
+  // the step's length update, once every reader of the old length has finished
+  if (step && hq == 0 && j == 0) a.app.seq_lens[b] = L + 1;
   const size_t row = size_t(b) * a.hkv * G + hq;
   if (INVERSE) {
     uint32_t w[4];
@@ -122,10 +128,10 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_combine(const DecodeArgs& a, int batch, hipStream_t stream) {
+hipError_t launch_combine(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
   const dim3 grid(a.hkv * a.group, batch), block(256);
-  if (a.out) hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream, a);
+  if (a.out) hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream, a, lens);
+  else hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream, a, lens);
   return hipGetLastError();
 }
 

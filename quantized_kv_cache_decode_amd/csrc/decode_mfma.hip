@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "tq_device.h"
+#include "tq_encode.h"
 #include "tq_launch.h"
 
 namespace tq {
@@ -45,6 +46,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Build-time tuning knobs (defaults are the measured best; see the design notes).
 #ifndef TQ_MFMA_NS_SMALL_GROUP
 #define TQ_MFMA_NS_SMALL_GROUP 4   // token sets per MFMA for group sizes <= 4 (4 or 2)
+#endif
+#ifndef TQ_MFMA_Q_LDS
+#define TQ_MFMA_Q_LDS 0   // 1: score-MFMA q operands read from LDS in the loop (frees VGPRs)
 #endif
 #ifndef TQ_MFMA_V_FENCE
 #define TQ_MFMA_V_FENCE 0
@@ -167,8 +171,145 @@ __device__ inline void zero_words(uint32_t (&w)[N]) {
   for (int i = 0; i < N; ++i) w[i] = 0;
 }
 
+// Decode step, two extra work groups of (sequence b, KV head h), at grid columns
+// 0 (K) and 1 (V) so they start first: lanes 0-15 encode the new token's K or V row
+// at slot L straight into the cache, then write that side of the token's own
+// partial for the G query heads -- K: score z_g = scale * q_g . k_hat (k_hat =
+// n_K * c_K[idx] in K's basis, or the fp16 row) as m, and l = 1; V: o = v_hat =
+// n_V * c_V[idx] in V's basis.  The regular splits cover the L earlier tokens and
+// never read slot L, so all of them run side by side; the merge kernel folds this
+// partial in like any other split.
+template <int KFMT, int VFMT>
+__device__ __forceinline__ void append_v_partial(const DecodeArgs& a, size_t row, int L, int lane) {
+  const int j = lane & 15;
+  if (lane >= 16) return;  // one 16-lane group
+  VRowInputs<VFMT> in;
+  load_v_inputs<VFMT>(a.app, row, L, a.app.v_new + row * kDim, j, in);
+  uint8_t code[8];
+  const float nv = half_bits_to_float(append_v_row<VFMT>(a.app, row, L, in, j, code));
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = nv * codebook_at<VFMT>(in.row.tab, code[e]);
+  const size_t p0 = partial_index(a, row, a.plan.max_splits, 0);
+  for (int g = 0; g < a.group; ++g) {
+    float4* o = reinterpret_cast<float4*>(a.part_o + (p0 + g) * kDim + 8 * j);
+    o[0] = make_float4(x[0], x[1], x[2], x[3]);
+    o[1] = make_float4(x[4], x[5], x[6], x[7]);
+  }
+}
+
+// K side: `kin` (quantised K) or `kraw` (F16 K) were requested before the q
+// staging, so their memory round trip overlaps it.
+template <int KFMT, int VFMT>
+__device__ __forceinline__ void append_k_partial(const DecodeArgs& a, const float (*qs)[kDim], size_t row, int L, int lane,
+                                 const RowInputs<KFMT == kFmtF16 ? kFmtTurbo3 : KFMT>& kin, const uint4& kraw) {
+  const int j = lane & 15;
+  if (lane >= 16) return;  // one 16-lane group
+  constexpr int KQ = KFMT == kFmtF16 ? kFmtTurbo3 : KFMT;
+  float x[8];
+  if (KFMT == kFmtF16) {
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.app.k_data) + (row * a.cap + L) * kDim + 8 * j) = kraw;
+    const uint32_t w[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = half_bits_to_float(uint16_t(w[e >> 1] >> (16 * (e & 1))));
+  } else {
+    uint8_t code[8];
+    const float nk = half_bits_to_float(append_k_row<KQ>(a.app, row, L, kin, j, code));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = nk * codebook_at<KQ>(kin.tab, code[e]);
+  }
+  // this lane's share of every head's dot product, then one 16-lane reduction for all
+  const int G = a.group;
+  float d[kMaxGroup];
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) {
+    float t = 0.f;
+    if (g < G) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t += qs[g][8 * j + e] * x[e];
+    }
+    d[g] = t;
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) d[g] += __shfl_xor(d[g], m, 16);
+  }
+  const size_t p0 = partial_index(a, row, a.plan.max_splits, 0);
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) {
+    if (g < G && j == g) {  // lane g stores head g
+      a.part_ml[(p0 + g) * 2] = a.scale * d[g];  // natural-log units, like the splits' m
+      a.part_ml[(p0 + g) * 2 + 1] = 1.f;
+    }
+  }
+}
+
+// The G query rows of KV head row `row` into LDS qs: either the fp32 rows already
+// in K's basis, or the caller's unrotated rows, rotated here with the same 16-lane
+// Walsh-Hadamard routine the stand-alone rotation uses (so both routes give
+// identical bits).  All 64 lanes; the caller synchronises.
+__device__ __forceinline__ void stage_q(const DecodeArgs& a, float (*qs)[kDim], size_t row, int lane) {
+  const int G = a.group;
+  const size_t qrow0 = row * G;  // first query row of this KV head
+  if (a.q_in) {
+    // rows r = 4*k + lane/16 (k < 4 covers G <= 16): every load first, then the
+    // rotations, so the rows cost one memory round trip
+    const int j = lane & 15, r0 = lane >> 4;
+    float v0[8], v1[8], v2[8], v3[8];
+    auto load = [&](int k, float (&v)[8]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      if (4 * k + r0 < G) load_row8(a.q_in, a.q_fp32 != 0, (qrow0 + 4 * k + r0) * kDim + 8 * j, v);
+    };
+    auto finish = [&](int k, float (&v)[8]) {
+      if (4 * k + r0 < G) {  // whole 16-lane segments
+        if (a.q_rotate) rotate_row_forward(v, a.k_signs, j);
+        float4* d = reinterpret_cast<float4*>(&qs[4 * k + r0][8 * j]);
+        d[0] = make_float4(v[0], v[1], v[2], v[3]);
+        d[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    };
+    load(0, v0);
+    load(1, v1);
+    load(2, v2);
+    load(3, v3);
+    finish(0, v0);
+    finish(1, v1);
+    finish(2, v2);
+    finish(3, v3);
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(a.q_rot + qrow0 * kDim);
+    for (int i = lane; i < G * (kDim / 4); i += 64) reinterpret_cast<float4*>(&qs[0][0])[i] = src[i];
+  }
+}
+
+// Decode step, K side as a whole: request the row and thresholds, stage q while
+// they arrive, then encode, store and score.
+template <int KFMT, int VFMT>
+__device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[kDim], size_t row, int L, int lane) {
+  constexpr int KQ = KFMT == kFmtF16 ? kFmtTurbo3 : KFMT;
+  RowInputs<KQ> kin;
+  uint4 kraw = make_uint4(0, 0, 0, 0);
+  if (lane < 16) {
+    const uint16_t* src = a.app.k_new + row * kDim;
+    if (KFMT == kFmtF16) kraw = *reinterpret_cast<const uint4*>(src + 8 * lane);
+    else load_row_inputs<KQ>(src, a.app.k_signs, a.app.k_cb, lane, kin);
+  }
+  stage_q(a, qs, row, lane);
+  __syncthreads();
+  append_k_partial<KFMT, VFMT>(a, qs, row, L, lane, kin, kraw);
+}
+
+#ifndef TQ_MFMA_MIN_WAVES
+#define TQ_MFMA_MIN_WAVES 0   // >0: ask the compiler for this many waves per SIMD (NS=4: minus 1)
+#endif
+template <int NS>
+constexpr int min_waves() { return TQ_MFMA_MIN_WAVES == 0 ? 1 : (NS == 4 ? TQ_MFMA_MIN_WAVES - 1 : TQ_MFMA_MIN_WAVES); }
+
 template <int KFMT, int VFMT, int NS>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(min_waves<NS>())))
+void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   constexpr int P = 4 / NS;                  // lane groups per set in the score MFMA
   constexpr int Gp = 16 / NS;                // columns (padded heads) per set
   constexpr int TOK = 32 * NS;               // tokens per iteration
@@ -177,11 +318,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NKK = 4 * NS;                // score MFMAs per 16-token row block
   constexpr int VW = v_chunk_bytes(VFMT) / 4;  // V words per lane per tile
 
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // decode step: grid columns 0 and 1 (when col0 = 2) append the new token (K, V)
+  // and attend to it alone; the splits follow
+  const int s = int(blockIdx.x) - a.col0;
+  const int h = blockIdx.y, b = a.b0 + blockIdx.z;
   const int G = a.group;
-  const int L = min(a.seq_lens[b], a.cap);
+  const int L = min(lens.len[blockIdx.z], a.cap);  // decode step: the length before the append
   const int chunk = a.plan.chunk;
   const int nsplit = min((L + chunk - 1) / chunk, a.plan.max_splits);
+  const bool append_wg = s < 0;
   if (s >= nsplit) return;
   const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
   const int t0 = s * chunk;
@@ -194,6 +339,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const uint8_t* vbase = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT) + lane * (VW * 4);
   const uint16_t* knorm = KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap);
   const uint16_t* vnorm = a.v_norms + row * size_t(a.cap);
+  __shared__ float qs[kMaxGroup][kDim];
+  if (append_wg) {
+    // The append is one long dependent chain (binary64 butterflies, exact norm,
+    // thresholds) sharing its SIMD with streaming decode waves: let it issue first.
+    __builtin_amdgcn_s_setprio(3);
+    if (s == -1) append_v_partial<KFMT, VFMT>(a, row, L, lane);  // the V side needs no q
+    else append_k_work<KFMT, VFMT>(a, qs, row, L, lane);
+    return;
+  }
 
   // Register double-buffering by rotation: the K words of iteration i+1 are
   // requested as soon as iteration i's K has been turned into MFMA operands, and
@@ -228,34 +382,30 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   load_k(t0);
   load_v(t0);
 
-  // The G query rows of this KV head go through LDS: either the fp32 rows already
-  // in K's basis, or the caller's unrotated rows, rotated here with the same
-  // 16-lane Walsh-Hadamard routine the stand-alone rotation uses (so both routes
-  // give identical bits).
-  __shared__ float qs[kMaxGroup][kDim];
-  const size_t qrow0 = row * G;  // first query row of this KV head
-  if (a.q_in) {
-    const int j = lane & 15;
-    for (int r0 = 0; r0 < G; r0 += 4) {
-      const int r = r0 + (lane >> 4);
-      if (r < G) {  // whole 16-lane segments
-        float v[8];
-        load_row8(a.q_in, a.q_fp32 != 0, (qrow0 + r) * kDim + 8 * j, v);
-        if (a.q_rotate) rotate_row_forward(v, a.k_signs, j);
-        float4* d = reinterpret_cast<float4*>(&qs[r][8 * j]);
-        d[0] = make_float4(v[0], v[1], v[2], v[3]);
-        d[1] = make_float4(v[4], v[5], v[6], v[7]);
-      }
-    }
-  } else {
-    const float4* src = reinterpret_cast<const float4*>(a.q_rot + qrow0 * kDim);
-    for (int i = lane; i < G * (kDim / 4); i += 64) reinterpret_cast<float4*>(&qs[0][0])[i] = src[i];
-  }
+  stage_q(a, qs, row, lane);
   __syncthreads();
 
   // q in this lane's score-MFMA B slots: q[hn][part*128/P + 8kk + t] * scale*log2(e),
   // zero unless the lane's k-slots belong to its column's set.
   // Kept in VGPRs: reading these operands from LDS inside the loop measured slower.
+#if TQ_MFMA_Q_LDS
+  // fp16 operands in LDS: rows 0..G-1 = q * scale*log2(e), row kMaxGroup = zeros.
+  __shared__ half8 qh[kMaxGroup + 1][kDim / 8];
+  {
+    const float f = a.scale * kLog2e;
+    for (int i = lane; i < (G + 1) * (kDim / 8); i += 64) {
+      const int r = i / (kDim / 8), c = i % (kDim / 8);
+      const bool zero = r == G;
+      const float* src = &qs[zero ? 0 : r][8 * c];
+      const float ff = zero ? 0.f : f;
+      qh[zero ? kMaxGroup : r][c] = half8{_Float16(src[0] * ff), _Float16(src[1] * ff), _Float16(src[2] * ff),
+                                          _Float16(src[3] * ff), _Float16(src[4] * ff), _Float16(src[5] * ff),
+                                          _Float16(src[6] * ff), _Float16(src[7] * ff)};
+    }
+  }
+  __syncthreads();
+  const half8* qbase = (hn < G && sig == sn) ? &qh[hn][part * (NKK)] : &qh[kMaxGroup][0];
+#else
   half8 qb[NKK];
   {
     const bool use = hn < G && sig == sn;
@@ -269,6 +419,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
                      _Float16(x1.x * f), _Float16(x1.y * f), _Float16(x1.z * f), _Float16(x1.w * f)};
     }
   }
+#endif
   ByteTable ktab, vtab;
   {
     uint16_t c[8];
@@ -292,6 +443,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   auto step = [&](int base, auto tail_c) {
     constexpr bool TAIL = decltype(tail_c)::value;
     const int tn = ((base >> 5) + sn) << 5;      // first token of this lane's column tile
+#if TQ_MFMA_Q_LDS
+    // an offset the compiler cannot see through keeps the q reads inside the loop
+    int qoff = 0;
+    asm volatile("" : "+v"(qoff));
+    const half8* qi = qbase + qoff;
+#endif
     // ---- scores (dequant of each operand right before its MFMA)
     float z[8];
 #pragma unroll
@@ -324,8 +481,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
             default: A = dq_turbo3<3>(wa, wb, wc, ktab); break;
           }
         }
-        if (kk & 1) S2[rb] = mfma(A, qb[kk], S2[rb]);
-        else S[rb] = mfma(A, qb[kk], S[rb]);
+#if TQ_MFMA_Q_LDS
+        const half8 qk = qi[kk];
+#else
+        const half8 qk = qb[kk];
+#endif
+        if (kk & 1) S2[rb] = mfma(A, qk, S2[rb]);
+        else S[rb] = mfma(A, qk, S[rb]);
       }
       S[rb] += S2[rb];
     }
@@ -429,7 +591,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   // by a separate kernel: a release/acquire hand-off between waves of this kernel
   // would need an L2 write-back per wave, which measured far slower.
   if (n < Gp && hn < G) {
-    const size_t pidx = (row * a.plan.max_splits + s) * G + hn;
+    const size_t pidx = partial_index(a, row, s, hn);
     float* o = a.part_o + pidx * kDim;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -445,24 +607,25 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 }
 
 template <int KF, int VF>
-hipError_t launch_fmt(const DecodeArgs& a, int batch, hipStream_t stream) {
-  const dim3 grid(a.plan.max_splits, a.hkv, batch), block(64);
+hipError_t launch_fmt(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
+  // decode step: the appended token's two work groups come first
+  const dim3 grid(a.col0 + a.split_cols, a.hkv, batch), block(64);
   if (a.group <= 16 / TQ_MFMA_NS_SMALL_GROUP)
-    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, TQ_MFMA_NS_SMALL_GROUP>), grid, block, 0, stream, a);
-  else if (a.group <= 8) hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 2>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 1>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, TQ_MFMA_NS_SMALL_GROUP>), grid, block, 0, stream, a, lens);
+  else if (a.group <= 8) hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 2>), grid, block, 0, stream, a, lens);
+  else hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 1>), grid, block, 0, stream, a, lens);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, hipStream_t stream) {
-  if (a.kfmt == kFmtTurbo3 && a.vfmt == kFmtTurbo3) return launch_fmt<kFmtTurbo3, kFmtTurbo3>(a, batch, stream);
-  if (a.kfmt == kFmtTurbo3 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtTurbo3, kFmtTurbo4>(a, batch, stream);
-  if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo3) return launch_fmt<kFmtTurbo4, kFmtTurbo3>(a, batch, stream);
-  if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtTurbo4, kFmtTurbo4>(a, batch, stream);
-  if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo3) return launch_fmt<kFmtF16, kFmtTurbo3>(a, batch, stream);
-  if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtF16, kFmtTurbo4>(a, batch, stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
+  if (a.kfmt == kFmtTurbo3 && a.vfmt == kFmtTurbo3) return launch_fmt<kFmtTurbo3, kFmtTurbo3>(a, lens, batch, stream);
+  if (a.kfmt == kFmtTurbo3 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtTurbo3, kFmtTurbo4>(a, lens, batch, stream);
+  if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo3) return launch_fmt<kFmtTurbo4, kFmtTurbo3>(a, lens, batch, stream);
+  if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtTurbo4, kFmtTurbo4>(a, lens, batch, stream);
+  if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo3) return launch_fmt<kFmtF16, kFmtTurbo3>(a, lens, batch, stream);
+  if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtF16, kFmtTurbo4>(a, lens, batch, stream);
   return hipErrorInvalidValue;
 }
 

@@ -57,10 +57,10 @@ __device__ inline float wave_sum(float v) {
 }
 
 template <int KFMT, int VFMT>
-__global__ __launch_bounds__(256) void decode_ref_kernel(DecodeArgs a) {
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(256) void decode_ref_kernel(DecodeArgs a, SeqLens lens) {
+  const int s = blockIdx.x, h = blockIdx.y, b = a.b0 + blockIdx.z;
   const int G = a.group;
-  const int L = min(a.seq_lens[b], a.cap);
+  const int L = min(lens.len[blockIdx.z], a.cap);
   const int chunk = a.plan.chunk;
   const int nsplit = min((L + chunk - 1) / chunk, a.plan.max_splits);
   if (s >= nsplit) return;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void decode_ref_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  const size_t pidx = (row * a.plan.max_splits + s) * G;
+  const size_t pidx = partial_index(a, row, s, 0);
   for (int i = tid; i < G * kDim; i += 256) {
     const int g = i / kDim, d = i % kDim;
     float M = -INFINITY;
@@ -200,20 +200,20 @@ __global__ __launch_bounds__(256) void decode_ref_kernel(DecodeArgs a) {
 }
 
 template <int KF, int VF>
-void launch_ref(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_ref_kernel<KF, VF>), grid, dim3(256), 0, stream, a);
+void launch_ref(const DecodeArgs& a, const SeqLens& lens, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_ref_kernel<KF, VF>), grid, dim3(256), 0, stream, a, lens);
 }
 
 }  // namespace
 
-hipError_t launch_decode_reference(const DecodeArgs& a, int batch, hipStream_t stream) {
+hipError_t launch_decode_reference(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
   const dim3 grid(a.plan.max_splits, a.hkv, batch);
-  if (a.kfmt == kFmtTurbo3 && a.vfmt == kFmtTurbo3) launch_ref<kFmtTurbo3, kFmtTurbo3>(a, grid, stream);
-  else if (a.kfmt == kFmtTurbo3 && a.vfmt == kFmtTurbo4) launch_ref<kFmtTurbo3, kFmtTurbo4>(a, grid, stream);
-  else if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo3) launch_ref<kFmtTurbo4, kFmtTurbo3>(a, grid, stream);
-  else if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo4) launch_ref<kFmtTurbo4, kFmtTurbo4>(a, grid, stream);
-  else if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo3) launch_ref<kFmtF16, kFmtTurbo3>(a, grid, stream);
-  else if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo4) launch_ref<kFmtF16, kFmtTurbo4>(a, grid, stream);
+  if (a.kfmt == kFmtTurbo3 && a.vfmt == kFmtTurbo3) launch_ref<kFmtTurbo3, kFmtTurbo3>(a, lens, grid, stream);
+  else if (a.kfmt == kFmtTurbo3 && a.vfmt == kFmtTurbo4) launch_ref<kFmtTurbo3, kFmtTurbo4>(a, lens, grid, stream);
+  else if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo3) launch_ref<kFmtTurbo4, kFmtTurbo3>(a, lens, grid, stream);
+  else if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo4) launch_ref<kFmtTurbo4, kFmtTurbo4>(a, lens, grid, stream);
+  else if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo3) launch_ref<kFmtF16, kFmtTurbo3>(a, lens, grid, stream);
+  else if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo4) launch_ref<kFmtF16, kFmtTurbo4>(a, lens, grid, stream);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -24,6 +24,12 @@ struct EncodeArgs {
   const uint16_t* v_cb;
 };
 
+// Host lengths of the sequences of one launch (at most kAppendChunk of them; the
+// host splits larger batches into several launches).
+struct SeqLens {
+  int32_t len[kAppendChunk];
+};
+
 struct AppendStarts {
   int32_t start[kAppendChunk];  // first slot written, per sequence of the launch
   int32_t count[kAppendChunk];  // rows appended, per sequence of the launch
@@ -40,11 +46,15 @@ hipError_t launch_inverse_rotate(const float* o_rot, const float* signs, uint16_
 
 // ---- decode
 // Split plan: sequence b is cut into ceil(L_b / chunk) splits of `chunk` tokens
-// (at most max_splits; the last split takes the remainder).  Partials of split
-// s of (b, kv head h) live at index ((b*hkv + h)*max_splits + s).
+// (at most max_splits; the last split takes the remainder).  Each (b, kv head h)
+// row owns `slots` = max_splits + 1 partial slots: slot s < max_splits holds split
+// s, the last one the appended token's own partial in the decode step (where the
+// token is appended and attended in one call).
 struct DecodePlan {
   int chunk;
   int max_splits;
+  int slots;
+  int bandwidth_bound;  // >= 4M token-heads: long enough that HBM, not latency, sets the time
 };
 
 struct DecodeArgs {
@@ -55,7 +65,9 @@ struct DecodeArgs {
   const uint16_t* k_norms;
   const uint8_t* v_data;
   const uint16_t* v_norms;
-  const int32_t* seq_lens;
+  int b0;                   // first sequence of the launch (blockIdx z / y counts from it)
+  int col0;                 // decode kernel grid: columns 0..col0-1 append the step's token (0 or 2)
+  int split_cols;           // decode kernel grid: split columns after them (0 or max_splits)
   const uint16_t* k_cb;
   const uint16_t* v_cb;
   const float* q_rot;       // [B][Hq][128] fp32, already in K's basis (when q_in is NULL)
@@ -64,14 +76,21 @@ struct DecodeArgs {
   int q_rotate;             // q_in goes through H(s_K * q)/sqrt(128) (quantised K formats)
   const float* k_signs;
   const float* v_signs;
-  float* part_o;            // [B*Hkv*max_splits][group][128]
-  float* part_ml;           // [B*Hkv*max_splits][group][2]
+  float* part_o;            // [B*Hkv*slots][group][128]
+  float* part_ml;           // [B*Hkv*slots][group][2]
   float* out_rot;           // [B][Hq][128] fp32 in V's basis, or NULL when `out` is written
   uint16_t* out;            // [B][Hq][128] fp16 bits in the original basis, or NULL
+  EncodeArgs app;           // decode step: the one-token append (app.k_new == NULL otherwise)
 };
 
-hipError_t launch_decode_reference(const DecodeArgs& a, int batch, hipStream_t stream);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, hipStream_t stream);
-hipError_t launch_combine(const DecodeArgs& a, int batch, hipStream_t stream);
+inline __host__ __device__ size_t partial_index(const DecodeArgs& a, size_t row, int slot, int g) {
+  return (row * a.plan.slots + slot) * a.group + g;
+}
+
+// Each launch covers sequences a.b0 .. a.b0 + nb - 1 (nb <= kAppendChunk) with
+// their visible lengths in `lens` (the decode step: the lengths before the append).
+hipError_t launch_decode_reference(const DecodeArgs& a, const SeqLens& lens, int nb, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, const SeqLens& lens, int nb, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs& a, const SeqLens& lens, int nb, hipStream_t stream);
 
 }  // namespace tq

@@ -154,6 +154,51 @@ def compare_codes(cache, b, k16, v16, L, w, codebooks, seed=0):
     return mism, margin, total
 
 
+def new_token_rows(w, seed, step=0):
+    """The step's new K and V rows as fp16 [B, Hkv, 1, 128] numpy arrays."""
+    kn = np.stack([np.stack([new_token_kv(w, seed, "k", b, h, step) for h in range(w.num_kv_heads)])
+                   for b in range(w.batch)])
+    vn = np.stack([np.stack([new_token_kv(w, seed, "v", b, h, step) for h in range(w.num_kv_heads)])
+                   for b in range(w.batch)])
+    return kn, vn
+
+
+def gpu_decode_step(cache, kn, vn, q_np):
+    """tq_decode_step: append kn, vn [B, Hkv, 1, 128] and decode q; returns fp16 [B, Hq, 128]."""
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    q = torch.from_numpy(np.ascontiguousarray(q_np)).to("cuda")
+    B, Hq, _ = q.shape
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    ws = torch.zeros(tq.tq_decode_workspace_size(cache, Hq), dtype=torch.uint8, device="cuda")
+    tq.tq_decode_step(cache, torch.from_numpy(np.ascontiguousarray(kn)).cuda(),
+                      torch.from_numpy(np.ascontiguousarray(vn)).cuda(), q, SCALE, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def prefill_then_decode_step(w, seed=0, lengths=None, capacity=None):
+    """A workload through tq_decode_step: prefill L_b - 1 rows, then one step that appends the
+    L_b-th row and decodes (sequences with L_b = 0 get their first row).
+
+    Returns (cache, k_list, v_list (full rows incl. the appended one), lengths after the step,
+    q, out fp16)."""
+    L = context_lengths(w, seed) if lengths is None else np.asarray(lengths)
+    pre = np.maximum(L - 1, 0)
+    L = pre + 1
+    k_list = gen_kv(w, seed, pre, "k")
+    v_list = gen_kv(w, seed, pre, "v")
+    cap = capacity or int(((L.max() + 31) // 32) * 32)
+    cache = encode_on_gpu(w, k_list, v_list, pre, cap, seed)
+    kn, vn = new_token_rows(w, seed)
+    q = queries(w, seed)
+    out = gpu_decode_step(cache, kn, vn, q)
+    k_list = [np.concatenate([k, kk], axis=1) for k, kk in zip(k_list, kn)]
+    v_list = [np.concatenate([v, vv], axis=1) for v, vv in zip(v_list, vn)]
+    return cache, k_list, v_list, L, q, out
+
+
 def prefill_and_step(w, seed=0, lengths=None, capacity=None):
     """Inputs and GPU cache of a workload: prefill L_b - appends rows, then one append step.
 

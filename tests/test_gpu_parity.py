@@ -189,6 +189,66 @@ def test_fused_call_matches_separate_calls_bitwise(name):
     np.testing.assert_array_equal(fused.view(np.uint16), sep.view(np.uint16))
 
 
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3s", "c4s"])
+def test_decode_step_parity(name, codebooks):
+    """tq_decode_step (append + attend in one call): the appended token's codes and norms are
+    bit-exact, the lengths advance by one, and the output matches the oracle end to end and
+    the two-call route (tq_encode_append, then the fused decode) up to rounding."""
+    w, lens = _small_workloads()[name]
+    cache, k_list, v_list, L, q, got = S.prefill_then_decode_step(w, lengths=lens)
+    np.testing.assert_array_equal(cache.seq_lens.cpu().numpy(), L)
+    np.testing.assert_array_equal(cache.lengths, L)
+    mism = margin = total = 0
+    for b in range(w.batch):
+        m, g, t = S.compare_codes(cache, b, k_list[b], v_list[b], int(L[b]), w, codebooks)
+        mism, margin, total = mism + m, margin + g, total + t
+        S.assert_close(got[b], S.oracle_end_to_end(w, k_list[b], v_list[b], int(L[b]), q[b], codebooks),
+                       f"{name} b={b}")
+    assert mism <= margin <= 1e-4 * total
+    two_call = S.gpu_decode(cache, q, variant="fused")
+    rel, mx = S.errors(got, two_call.astype(np.float64))
+    _say(f"[{name} step] vs two-call route: rel-L2 {rel:.2e} max-abs {mx:.2e}")
+    assert rel <= 2e-4 and mx <= 2e-3
+
+
+def test_decode_step_sixteen_steps_gqa_4_over_2(codebooks):
+    """Sixteen successive tq_decode_step calls (GQA 4 over 2), across a 32-token tile boundary
+    and a split boundary, each checked against the full-dequant oracle."""
+    w = get_workload(0)
+    pre = 250
+    from synth import kv_slice, new_token_kv
+    k = [np.stack([kv_slice(w, 0, "k", 0, h, pre) for h in range(2)])]
+    v = [np.stack([kv_slice(w, 0, "v", 0, h, pre) for h in range(2)])]
+    cache = S.encode_on_gpu(w, k, v, [pre], 288)
+    for step in range(16):
+        kn = np.stack([new_token_kv(w, 0, "k", 0, h, step) for h in range(2)])[None]
+        vn = np.stack([new_token_kv(w, 0, "v", 0, h, step) for h in range(2)])[None]
+        q = queries(w, 0, step)
+        got = S.gpu_decode_step(cache, kn, vn, q)
+        k[0] = np.concatenate([k[0], kn[0]], axis=1)
+        v[0] = np.concatenate([v[0], vn[0]], axis=1)
+        L = pre + step + 1
+        assert int(cache.seq_lens.cpu()[0]) == L and int(cache.lengths[0]) == L
+        S.assert_close(got[0], S.oracle_end_to_end(w, k[0], v[0], L, q[0], codebooks), f"step {step}")
+    m, _, _ = S.compare_codes(cache, 0, k[0], v[0], pre + 16, w, codebooks)
+    assert m == 0
+
+
+@pytest.mark.parametrize("group,k_format,v_format", [(1, "turbo4", "turbo3"), (16, "turbo3", "turbo4"),
+                                                     (7, "f16", "turbo4")])
+def test_decode_step_groups_formats_and_empty(group, k_format, v_format, codebooks):
+    """The step at group sizes 1, 7 and 16, mixed formats and fp16 K, with a sequence whose
+    first token the step appends (length 0 before it) and one ending on a tile boundary."""
+    w = S.scaled(get_workload(0), batch=3, num_q_heads=2 * group, num_kv_heads=2, k_format=k_format,
+                 v_format=v_format)
+    cache, k_list, v_list, L, q, got = S.prefill_then_decode_step(w, lengths=np.array([1, 300, 64]))
+    for b in range(3):
+        S.assert_close(got[b], S.oracle_end_to_end(w, k_list[b], v_list[b], int(L[b]), q[b], codebooks),
+                       f"G={group} b={b} L={int(L[b])}")
+        m, _, _ = S.compare_codes(cache, b, k_list[b], v_list[b], int(L[b]), w, codebooks)
+        assert m == 0
+
+
 def test_decode_does_not_mutate_cache():
     w = get_workload(0)
     cache, _, _, _, q = S.prefill_and_step(w)
@@ -255,13 +315,13 @@ def test_appends_merge_into_partial_tiles(codebooks):
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("index", [1, 2, 3, 4])
 def test_full_size_sampled(index, codebooks):
-    """Full-size workloads in the launch configuration the benchmark times; codes of the
-    sampled sequences are checked in full, outputs of the sampled sequences against the
-    oracle on the GPU bytes (codes equal the oracle's, so this is also end to end)."""
+    """Full-size workloads in the launch configuration the benchmark times (prefill, then one
+    tq_decode_step); codes of the sampled sequences are checked in full, outputs of the sampled
+    sequences against the oracle on the GPU bytes (codes equal the oracle's, so this is also
+    end to end)."""
     w = get_workload(index)
     _say(f"[full {w.name}] generating + encoding")
-    cache, k_list, v_list, L, q = S.prefill_and_step(w)
-    got = S.gpu_decode(cache, q, variant=VARIANTS[-1])
+    cache, k_list, v_list, L, q, got = S.prefill_then_decode_step(w)
     sample = [int(np.argmin(L)), int(np.argmax(L))] if index == 4 else sorted({0, w.batch - 1})
     for b in sample:
         m, g, t = S.compare_codes(cache, b, k_list[b], v_list[b], int(L[b]), w, codebooks)

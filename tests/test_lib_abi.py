@@ -120,8 +120,9 @@ def test_workspace_size_and_check(lib):
     a, p = _lens(64, 17)
     n = lib.tq_decode_workspace_size(ctypes.byref(d), 4, p)
     assert n > 0 and n % 4 == 0
-    # one split per (sequence, KV head) at these lengths: 2*2*1 items x group 2 x 130 floats
-    assert n == 2 * 2 * 1 * 2 * 130 * 4
+    # one split per (sequence, KV head) at these lengths, plus the decode step's slot:
+    # 2*2*(1+1) slots x group 2 x 130 floats
+    assert n == 2 * 2 * 2 * 2 * 130 * 4
     q = ctypes.c_void_p(0x20000)
     st = lib.tq_decode_attention(ctypes.byref(d), p, q, 4, ctypes.c_float(0.1), q, q, n - 4, None)
     assert st == binding.TQ_EWORKSPACE
@@ -157,7 +158,7 @@ def test_partials_are_small_next_to_the_cache(lib, batch, hkv, hq, lens, bytes_p
     group = hq // hkv
     per_item = group * 130 * 4
     assert ws % (batch * hkv * per_item) == 0
-    max_splits = ws // (batch * hkv * per_item)
+    max_splits = ws // (batch * hkv * per_item) - 1   # one slot per row is the decode step's
     chunk_min = -(-max(lens) // max_splits)
     items = sum(hkv * -(-int(L) // chunk_min) for L in lens)
     kv = sum(lens) * hkv * bytes_per_token
@@ -168,3 +169,16 @@ def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_LIB", None)
     with pytest.raises(FileNotFoundError):
         binding.load_library(str(tmp_path / "missing.so"))
+
+
+def test_no_kernel_spills_to_scratch():
+    """Every kernel of the last build keeps its state in registers/LDS: a spill to scratch
+    memory (or a private array the compiler could not promote) would put per-lane memory
+    traffic on the hot path.  Reads the compiler's resource remarks that build.py records."""
+    from quantized_kv_cache_decode_amd import build
+    if not os.path.exists(build.RESOURCE_REPORT):
+        pytest.skip("no build in this tree (build.py writes the resource report)")
+    lines = [l.split() for l in open(build.RESOURCE_REPORT).read().splitlines() if l.strip()]
+    assert lines, "empty resource report"
+    spills = [l for l in lines if l[-1] != "scratch=0"]
+    assert not spills, spills

@@ -230,11 +230,15 @@ __device__ __forceinline__ void append_k_partial(const DecodeArgs& a, const floa
     }
     d[g] = t;
   }
+  auto sum_stage = [&](auto m_c) {
+    constexpr int M = decltype(m_c)::value;
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-#pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) d[g] += __shfl_xor(d[g], m, 16);
-  }
+    for (int g = 0; g < kMaxGroup; ++g) d[g] += xor_lane16<M>(d[g]);
+  };
+  sum_stage(std::integral_constant<int, 1>{});
+  sum_stage(std::integral_constant<int, 2>{});
+  sum_stage(std::integral_constant<int, 4>{});
+  sum_stage(std::integral_constant<int, 8>{});
   const size_t p0 = partial_index(a, row, a.plan.max_splits, 0);
 #pragma unroll
   for (int g = 0; g < kMaxGroup; ++g) {
@@ -382,6 +386,21 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   load_k(t0);
   load_v(t0);
 
+  // codebook byte tables: requested before the q staging's barrier so their
+  // loads overlap it
+  ByteTable ktab, vtab;
+  {
+    uint16_t c[8];
+    if (KFMT != kFmtF16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = a.k_cb[(KFMT == kFmtTurbo4 ? 8 : 0) + i];
+      ktab = make_table(c);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = a.v_cb[(VFMT == kFmtTurbo4 ? 8 : 0) + i];
+    vtab = make_table(c);
+  }
+
   stage_q(a, qs, row, lane);
   __syncthreads();
 
@@ -420,19 +439,6 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
     }
   }
 #endif
-  ByteTable ktab, vtab;
-  {
-    uint16_t c[8];
-    if (KFMT != kFmtF16) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = a.k_cb[(KFMT == kFmtTurbo4 ? 8 : 0) + i];
-      ktab = make_table(c);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = a.v_cb[(VFMT == kFmtTurbo4 ? 8 : 0) + i];
-    vtab = make_table(c);
-  }
-
   floatx4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};

@@ -6,6 +6,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace tq {
 
 constexpr int kDim = 128;
@@ -73,11 +75,41 @@ __device__ inline float half_bits_to_float(uint16_t h) { return __half2float(__u
 
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 
+// Value of lane (lane ^ M) within the same aligned 16-lane row, M in {1, 2, 4, 8},
+// through DPP moves (VALU data paths, no LDS round trip): quad_perm covers xor 1
+// and 2; xor 4 = half-row mirror (i ^ 7) then quad reversal (i ^ 3); xor 8 = row
+// mirror (i ^ 15) then half-row mirror (i ^ 7).  All 16 lanes of the row must be
+// active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xf, 0xf, false));
+}
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane16(uint32_t v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "xor distance within a 16-lane row");
+  if constexpr (M == 1) return dpp_u32<0xb1>(v);                 // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_u32<0x4e>(v);            // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return dpp_u32<0x1b>(dpp_u32<0x141>(v));  // half mirror, quad_perm [3,2,1,0]
+  else return dpp_u32<0x141>(dpp_u32<0x140>(v));                 // row mirror, half mirror
+}
+template <int M>
+__device__ __forceinline__ float xor_lane16(float v) {
+  return __uint_as_float(xor_lane16<M>(__float_as_uint(v)));
+}
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane16(uint64_t v) {
+  return uint64_t(xor_lane16<M>(uint32_t(v))) | (uint64_t(xor_lane16<M>(uint32_t(v >> 32))) << 32);
+}
+template <int M>
+__device__ __forceinline__ double xor_lane16(double v) {
+  return __longlong_as_double(int64_t(xor_lane16<M>(uint64_t(__double_as_longlong(v)))));
+}
+
 // Unnormalised 128-point Walsh-Hadamard transform of one row held by 16 lanes,
 // 8 elements per lane (element 8*j + i in lane j = lane16, slot i).  Stages over
 // element bits 0..2 are in-lane butterflies; stages over bits 3..6 exchange with
-// lane j ^ 1, 2, 4, 8 of the same aligned 16-lane segment, so all 16 lanes of a
-// segment must execute it together.  Natural (Sylvester) order in and out.  Every
+// lane j ^ 1, 2, 4, 8 of the same aligned 16-lane segment (DPP moves), so all 16
+// lanes of a segment must execute it together.  Natural (Sylvester) order in and out.  Every
 // kernel that rotates uses this one routine, so rotations done inside different
 // kernels round identically.
 __device__ inline void fwht128_row(float v[8], int lane16) {
@@ -92,14 +124,18 @@ __device__ inline void fwht128_row(float v[8], int lane16) {
       }
     }
   }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
+  auto stage = [&](auto m_c) {
+    constexpr int M = decltype(m_c)::value;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float o = __shfl_xor(v[i], m, 16);
-      v[i] = (lane16 & m) ? (o - v[i]) : (v[i] + o);
+      const float o = xor_lane16<M>(v[i]);
+      v[i] = (lane16 & M) ? (o - v[i]) : (v[i] + o);
     }
-  }
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 8>{});
 }
 
 // The 8 elements 8*lane16 .. 8*lane16+7 of a row of fp32 or fp16-bit values.

@@ -76,12 +76,16 @@ __device__ __forceinline__ uint16_t encode_row(const uint32_t (&w4)[4], const fl
     sC += ml * ml;
     x[e] = xv * double(sg[e]);
   }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    sA += __shfl_xor(sA, m, 16);
-    sB += __shfl_xor(sB, m, 16);
-    sC += __shfl_xor(sC, m, 16);
-  }
+  auto sum_stage = [&](auto m_c) {
+    constexpr int M = decltype(m_c)::value;
+    sA += xor_lane16<M>(sA);
+    sB += xor_lane16<M>(sB);
+    sC += xor_lane16<M>(sC);
+  };
+  sum_stage(std::integral_constant<int, 1>{});
+  sum_stage(std::integral_constant<int, 2>{});
+  sum_stage(std::integral_constant<int, 4>{});
+  sum_stage(std::integral_constant<int, 8>{});
   // Walsh-Hadamard in binary64: element bits 0..2 in-lane, bits 3..6 across lanes j ^ 1..8
 #pragma unroll
   for (int hh = 1; hh < 8; hh <<= 1) {
@@ -94,14 +98,18 @@ __device__ __forceinline__ uint16_t encode_row(const uint32_t (&w4)[4], const fl
       }
     }
   }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
+  auto fwht_stage = [&](auto m_c) {
+    constexpr int M = decltype(m_c)::value;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double o = __shfl_xor(x[e], m, 16);
-      x[e] = (j & m) ? (o - x[e]) : (x[e] + o);
+      const double o = xor_lane16<M>(x[e]);
+      x[e] = (j & M) ? (o - x[e]) : (x[e] + o);
     }
-  }
+  };
+  fwht_stage(std::integral_constant<int, 1>{});
+  fwht_stage(std::integral_constant<int, 2>{});
+  fwht_stage(std::integral_constant<int, 4>{});
+  fwht_stage(std::integral_constant<int, 8>{});
   const uint16_t nbits = exact_norm_fp16(sA, sB, sC);
   const double nd = double(half_bits_to_float(nbits));
   constexpr int K = levels(FMT);
@@ -146,12 +154,12 @@ __device__ __forceinline__ void store_k_record(uint8_t* rec, const uint8_t (&cod
     for (int e = 0; e < 8; ++e) c32[c0 + e] = code[e];
     uint32_t w[3];
     sub3_pack(c32, w);
-#pragma unroll
-    for (int m = 1; m < 4; m <<= 1) {
-      w[0] |= __shfl_xor(w[0], m, 16);
-      w[1] |= __shfl_xor(w[1], m, 16);
-      w[2] |= __shfl_xor(w[2], m, 16);
-    }
+    w[0] |= xor_lane16<1>(w[0]);
+    w[1] |= xor_lane16<1>(w[1]);
+    w[2] |= xor_lane16<1>(w[2]);
+    w[0] |= xor_lane16<2>(w[0]);
+    w[1] |= xor_lane16<2>(w[1]);
+    w[2] |= xor_lane16<2>(w[2]);
     if ((j & 3) == 0) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(rec + 12 * (j >> 2));
       dst[0] = w[0];

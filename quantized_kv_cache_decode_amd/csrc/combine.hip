@@ -3,9 +3,10 @@
 // "Change": attention runs in V's rotated basis and only the [B, Hq, D] output
 // is taken back to the original basis).
 //
-// Split s left (o_s, m_s, l_s): o_s = sum_t exp(z_t - m_s) v_t, l_s = sum_t
-// exp(z_t - m_s), m_s its running max (natural log units).  The merged output is
-// sum_s exp(m_s - M) o_s / sum_s exp(m_s - M) l_s for any M; M = max_s m_s.
+// Split s left (o_s, m_s, l_s): o_s = sum_t 2^(z_t - m_s) v_t, l_s = sum_t
+// 2^(z_t - m_s), m_s its running max, with z = scale * log2(e) * q.k (log2 units,
+// so every weight is one hardware exp2).  The merged output is
+// sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s for any M; M = max_s m_s.
 //
 // 256 threads: lane j = tid % 16 owns dims 8j..8j+7 and split group sg = tid / 16
 // takes splits sg, sg + 16, ...  Every load of a batch is independent (one
@@ -24,7 +25,7 @@ namespace {
 constexpr int kSplitGroups = 16;
 constexpr int kBatch = 5;  // splits per thread per round of loads (80 per round)
 
-__device__ inline float weight(float m, float M) { return m == -INFINITY ? 0.f : expf(m - M); }
+__device__ inline float weight(float m, float M) { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M); }
 
 template <bool INVERSE>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, SeqLens lens) {
@@ -50,20 +51,26 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, SeqLens lens
   for (int s0 = sg; s0 < nparts; s0 += kSplitGroups * kBatch) {
     float ms[kBatch], ls[kBatch];
     float4 oa[kBatch], ob[kBatch];
+    // Every load of the round is issued unconditionally (a partial past the end
+    // reads slot 0, always in bounds) and masked afterwards, so the round costs one
+    // memory round trip instead of one per partial.
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int v = s0 + kSplitGroups * k;
-      ms[k] = -INFINITY;
-      ls[k] = 0.f;
-      oa[k] = ob[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (v < nparts) {
-        const size_t p = p0 + size_t(v < nsplit ? v : a.plan.max_splits) * G;
-        const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * p);
-        ms[k] = ml.x;
-        ls[k] = ml.y;
-        const float4* src = reinterpret_cast<const float4*>(a.part_o + p * kDim + 8 * j);
-        oa[k] = src[0];
-        ob[k] = src[1];
+      const size_t p = p0 + size_t(v < nsplit ? v : (v < nparts ? a.plan.max_splits : 0)) * G;
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * p);
+      const float4* src = reinterpret_cast<const float4*>(a.part_o + p * kDim + 8 * j);
+      ms[k] = ml.x;
+      ls[k] = ml.y;
+      oa[k] = src[0];
+      ob[k] = src[1];
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (s0 + kSplitGroups * k >= nparts) {
+        ms[k] = -INFINITY;
+        ls[k] = 0.f;
+        oa[k] = ob[k] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
     float mn = m;

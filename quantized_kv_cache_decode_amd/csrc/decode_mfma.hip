@@ -58,7 +58,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #endif
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ inline half8 pack8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const u32x4 v = {a, b, c, d};
@@ -243,7 +242,7 @@ __device__ __forceinline__ void append_k_partial(const DecodeArgs& a, const floa
 #pragma unroll
   for (int g = 0; g < kMaxGroup; ++g) {
     if (g < G && j == g) {  // lane g stores head g
-      a.part_ml[(p0 + g) * 2] = a.scale * d[g];  // natural-log units, like the splits' m
+      a.part_ml[(p0 + g) * 2] = a.scale * kLog2e * d[g];  // log2 units, like the splits' m
       a.part_ml[(p0 + g) * 2 + 1] = 1.f;
     }
   }
@@ -593,7 +592,7 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
     l_tot = l_tot * fs + l_o * fo;
     m_fin = M;
   }
-  // Partial of this split (unnormalised o, natural-log m, l); the splits are merged
+  // Partial of this split (unnormalised o, log2-domain m, l); the splits are merged
   // by a separate kernel: a release/acquire hand-off between waves of this kernel
   // would need an L2 write-back per wave, which measured far slower.
   if (n < Gp && hn < G) {
@@ -606,7 +605,7 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
       reinterpret_cast<float4*>(o + d0)[1] = make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
     }
     if (g == 0) {
-      a.part_ml[pidx * 2] = m_fin == -INFINITY ? -INFINITY : m_fin * kLn2;
+      a.part_ml[pidx * 2] = m_fin;  // log2 units
       a.part_ml[pidx * 2 + 1] = l_tot;
     }
   }

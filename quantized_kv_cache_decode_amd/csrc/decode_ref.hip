@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void decode_ref_kernel(DecodeArgs a, SeqLens l
     }
     a.part_o[(pidx + g) * kDim + d] = o;
     if (d == 0) {
-      a.part_ml[(pidx + g) * 2] = M;
+      a.part_ml[(pidx + g) * 2] = M * 1.4426950408889634f;  // partials keep m in log2 units
       a.part_ml[(pidx + g) * 2 + 1] = l;
     }
   }

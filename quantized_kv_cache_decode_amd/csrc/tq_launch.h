@@ -76,8 +76,8 @@ struct DecodeArgs {
   int q_rotate;             // q_in goes through H(s_K * q)/sqrt(128) (quantised K formats)
   const float* k_signs;
   const float* v_signs;
-  float* part_o;            // [B*Hkv*slots][group][128]
-  float* part_ml;           // [B*Hkv*slots][group][2]
+  float* part_o;            // [B*Hkv*slots][group][128]   unnormalised sum_t 2^(z_t - m) v_t
+  float* part_ml;           // [B*Hkv*slots][group][2]     m (log2 units: z = scale*log2(e)*q.k), l
   float* out_rot;           // [B][Hq][128] fp32 in V's basis, or NULL when `out` is written
   uint16_t* out;            // [B][Hq][128] fp16 bits in the original basis, or NULL
   EncodeArgs app;           // decode step: the one-token append (app.k_new == NULL otherwise)

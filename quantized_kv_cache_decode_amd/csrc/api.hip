@@ -222,7 +222,9 @@ tq_status decode_setup(const tq_cache* cache, const int32_t* seq_lens_host, int3
   a.v_norms = cache->v_norms;
   a.k_cb = cache->k_codebook;
   a.v_cb = cache->v_codebook;
-  a.k_signs = cache->k_signs;
+  // the decode kernel reads the K signs unconditionally (no branch around a load);
+  // F16 K has none, so it reads V's, which it then ignores
+  a.k_signs = cache->k_signs ? cache->k_signs : cache->v_signs;
   a.v_signs = cache->v_signs;
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + partial_floats(cache, num_q_heads, plan) * 128;
@@ -273,7 +275,10 @@ tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_
   if (st != TQ_OK) return st;
   if (!q_rot || !out_rot) return fail(TQ_EINVAL, "q_rot / out_rot is NULL");
   if (variant < 0 || variant > 2) return fail(TQ_EINVAL, "unknown decode variant %d", variant);
-  a.q_rot = q_rot;
+  a.q_rot = q_rot;  // (the reference kernel reads it; the MFMA kernel stages it as fp32 q, unrotated)
+  a.q_in = q_rot;
+  a.q_fp32 = 1;
+  a.q_rotate = 0;
   a.out_rot = out_rot;
   // variant 0 (default) is the MFMA kernel, 1 the plain VALU reference kernel;
   // both are followed by the log-sum-exp merge of their splits

@@ -248,42 +248,78 @@ __device__ __forceinline__ void append_k_partial(const DecodeArgs& a, const floa
   }
 }
 
-// The G query rows of KV head row `row` into LDS qs: either the fp32 rows already
-// in K's basis, or the caller's unrotated rows, rotated here with the same 16-lane
-// Walsh-Hadamard routine the stand-alone rotation uses (so both routes give
-// identical bits).  All 64 lanes; the caller synchronises.
-__device__ __forceinline__ void stage_q(const DecodeArgs& a, float (*qs)[kDim], size_t row, int lane) {
-  const int G = a.group;
-  const size_t qrow0 = row * G;  // first query row of this KV head
-  if (a.q_in) {
-    // rows r = 4*k + lane/16 (k < 4 covers G <= 16): every load first, then the
-    // rotations, so the rows cost one memory round trip
-    const int j = lane & 15, r0 = lane >> 4;
-    float v0[8], v1[8], v2[8], v3[8];
-    auto load = [&](int k, float (&v)[8]) {
+// The G query rows of KV head row `row` into LDS qs, in two phases so the rows'
+// memory round trip overlaps other requests: q_request issues every load (rows
+// r = 4k + lane/16, k < 4 covers G <= 16; rows past G re-read row G-1 and are
+// never stored; no branch around a load, so the compiler never has to drain the
+// queue early), q_pin marks the loaded words as used where it is called (so the
+// compiler cannot sink the loads into the conditional blocks that use them, behind
+// later requests), q_finish converts, rotates (the same 16-lane Walsh-Hadamard
+// routine the stand-alone rotation uses, so both routes give identical bits) and
+// stores rows 0..G-1.  q is either the caller's unrotated rows (fp16 or fp32) or fp32 rows
+// already in K's basis (q_rotate = 0).  All 64 lanes; the caller synchronises.
+struct QRaw {
+  uint4 lo[4], hi[4];
+  float4 s0, s1;  // this lane's K sign flips (elements 8j..8j+7)
+};
+
+__device__ __forceinline__ void q_request(const DecodeArgs& a, size_t row, int lane, QRaw& q) {
+  const int G = a.group, j = lane & 15, r0 = lane >> 4;
+  const bool f32 = a.q_fp32 != 0;
+  const size_t esz = f32 ? 4 : 2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
-      if (4 * k + r0 < G) load_row8(a.q_in, a.q_fp32 != 0, (qrow0 + 4 * k + r0) * kDim + 8 * j, v);
-    };
-    auto finish = [&](int k, float (&v)[8]) {
-      if (4 * k + r0 < G) {  // whole 16-lane segments
-        if (a.q_rotate) rotate_row_forward(v, a.k_signs, j);
-        float4* d = reinterpret_cast<float4*>(&qs[4 * k + r0][8 * j]);
-        d[0] = make_float4(v[0], v[1], v[2], v[3]);
-        d[1] = make_float4(v[4], v[5], v[6], v[7]);
+  for (int k = 0; k < 4; ++k) {
+    const uint8_t* rowp = static_cast<const uint8_t*>(a.q_in) + (row * G + min(4 * k + r0, G - 1)) * kDim * esz;
+    const uint8_t* p = rowp + 8 * j * esz;  // elements 8j..8j+7: 32 bytes (fp32) or 16 (fp16)
+    q.lo[k] = *reinterpret_cast<const uint4*>(p);
+    q.hi[k] = *reinterpret_cast<const uint4*>(p + (f32 ? 16 : 0));
+  }
+  q.s0 = reinterpret_cast<const float4*>(a.k_signs + 8 * j)[0];  // read even when unused: no branch
+  q.s1 = reinterpret_cast<const float4*>(a.k_signs + 8 * j)[1];
+}
+
+__device__ __forceinline__ void pin4(uint4& v) {
+  uint32_t x = v.x, y = v.y, z = v.z, w = v.w;
+  asm volatile("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
+  v = make_uint4(x, y, z, w);
+}
+__device__ __forceinline__ void pin4(float4& v) {
+  float x = v.x, y = v.y, z = v.z, w = v.w;
+  asm volatile("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
+  v = make_float4(x, y, z, w);
+}
+__device__ __forceinline__ void q_pin(QRaw& q) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    pin4(q.lo[k]);
+    pin4(q.hi[k]);
+  }
+  pin4(q.s0);
+  pin4(q.s1);
+}
+
+__device__ __forceinline__ void q_finish(const DecodeArgs& a, float (*qs)[kDim], int lane, const QRaw& q) {
+  const int G = a.group, j = lane & 15, r0 = lane >> 4;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (4 * k + r0 < G) {  // whole 16-lane segments
+      float v[8];
+      const uint32_t w[8] = {q.lo[k].x, q.lo[k].y, q.lo[k].z, q.lo[k].w, q.hi[k].x, q.hi[k].y, q.hi[k].z, q.hi[k].w};
+      if (a.q_fp32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = half_bits_to_float(uint16_t(w[i >> 1] >> (16 * (i & 1))));
       }
-    };
-    load(0, v0);
-    load(1, v1);
-    load(2, v2);
-    load(3, v3);
-    finish(0, v0);
-    finish(1, v1);
-    finish(2, v2);
-    finish(3, v3);
-  } else {
-    const float4* src = reinterpret_cast<const float4*>(a.q_rot + qrow0 * kDim);
-    for (int i = lane; i < G * (kDim / 4); i += 64) reinterpret_cast<float4*>(&qs[0][0])[i] = src[i];
+      if (a.q_rotate) {
+        const float s8[8] = {q.s0.x, q.s0.y, q.s0.z, q.s0.w, q.s1.x, q.s1.y, q.s1.z, q.s1.w};
+        rotate_row_forward8(v, s8, j);
+      }
+      float4* d = reinterpret_cast<float4*>(&qs[4 * k + r0][8 * j]);
+      d[0] = make_float4(v[0], v[1], v[2], v[3]);
+      d[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
   }
 }
 
@@ -292,6 +328,9 @@ __device__ __forceinline__ void stage_q(const DecodeArgs& a, float (*qs)[kDim], 
 template <int KFMT, int VFMT>
 __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[kDim], size_t row, int L, int lane) {
   constexpr int KQ = KFMT == kFmtF16 ? kFmtTurbo3 : KFMT;
+  QRaw q;
+  q_request(a, row, lane, q);
+  __builtin_amdgcn_sched_barrier(0);
   RowInputs<KQ> kin;
   uint4 kraw = make_uint4(0, 0, 0, 0);
   if (lane < 16) {
@@ -299,7 +338,9 @@ __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[k
     if (KFMT == kFmtF16) kraw = *reinterpret_cast<const uint4*>(src + 8 * lane);
     else load_row_inputs<KQ>(src, a.app.k_signs, a.app.k_cb, lane, kin);
   }
-  stage_q(a, qs, row, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  q_pin(q);
+  q_finish(a, qs, lane, q);
   __syncthreads();
   append_k_partial<KFMT, VFMT>(a, qs, row, L, lane, kin, kraw);
 }
@@ -380,27 +421,40 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) nv[rb] = *reinterpret_cast<const uint2*>(vnorm + tn + 16 * rb + 4 * g);
   };
-  // The first iteration's words are requested before anything else; the q
-  // staging below runs while they are in flight.
+  // q rows first, then the first iteration's words: waiting for q (the oldest
+  // requests) leaves the K/V words in flight while q is rotated and staged.
+  QRaw qraw;
+  q_request(a, row, lane, qraw);
+  // the 8 fp16 codebook entries each side's byte table needs (turbo4: the 8
+  // magnitudes, entries 8..15); F16 K reads V's, unused
+  uint4 cbraw[2];
+  cbraw[0] = *reinterpret_cast<const uint4*>(KFMT == kFmtF16 ? a.v_cb : a.k_cb + (KFMT == kFmtTurbo4 ? 8 : 0));
+  cbraw[1] = *reinterpret_cast<const uint4*>(a.v_cb + (VFMT == kFmtTurbo4 ? 8 : 0));
+  __builtin_amdgcn_sched_barrier(0);  // keep every q request ahead of the K/V requests
   load_k(t0);
   load_v(t0);
+  __builtin_amdgcn_sched_barrier(0);  // ... and every K/V request ahead of the wait for q
+  q_pin(qraw);
+  pin4(cbraw[0]);
+  pin4(cbraw[1]);
 
-  // codebook byte tables: requested before the q staging's barrier so their
-  // loads overlap it
+  // codebook byte tables from the words requested with q
   ByteTable ktab, vtab;
   {
+    const uint32_t kc[4] = {cbraw[0].x, cbraw[0].y, cbraw[0].z, cbraw[0].w};
+    const uint32_t vc[4] = {cbraw[1].x, cbraw[1].y, cbraw[1].z, cbraw[1].w};
     uint16_t c[8];
     if (KFMT != kFmtF16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = a.k_cb[(KFMT == kFmtTurbo4 ? 8 : 0) + i];
+      for (int i = 0; i < 8; ++i) c[i] = uint16_t(kc[i >> 1] >> (16 * (i & 1)));
       ktab = make_table(c);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = a.v_cb[(VFMT == kFmtTurbo4 ? 8 : 0) + i];
+    for (int i = 0; i < 8; ++i) c[i] = uint16_t(vc[i >> 1] >> (16 * (i & 1)));
     vtab = make_table(c);
   }
 
-  stage_q(a, qs, row, lane);
+  q_finish(a, qs, lane, qraw);
   __syncthreads();
 
   // q in this lane's score-MFMA B slots: q[hn][part*128/P + 8kk + t] * scale*log2(e),

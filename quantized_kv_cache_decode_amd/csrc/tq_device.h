@@ -155,13 +155,21 @@ __device__ inline void load_row8(const void* base, bool fp32, size_t off, float 
   }
 }
 
-// q into K's codec basis: v = H (s * v) / sqrt(128), in place (16-lane row layout).
-__device__ inline void rotate_row_forward(float v[8], const float* signs, int lane16) {
+// q into K's codec basis: v = H (s * v) / sqrt(128), in place (16-lane row layout);
+// s8 = this lane's 8 signs s[8*lane16 .. 8*lane16+7].
+__device__ inline void rotate_row_forward8(float v[8], const float s8[8], int lane16) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] *= signs[8 * lane16 + i];
+  for (int i = 0; i < 8; ++i) v[i] *= s8[i];
   fwht128_row(v, lane16);
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] *= kInvSqrtD;
+}
+
+__device__ inline void rotate_row_forward(float v[8], const float* signs, int lane16) {
+  float s8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s8[i] = signs[8 * lane16 + i];
+  rotate_row_forward8(v, s8, lane16);
 }
 
 // Out of V's codec basis and into fp16: s * H (v) / sqrt(128), nearest-even fp16

@@ -70,10 +70,10 @@ struct DecodeArgs {
   int split_cols;           // decode kernel grid: split columns after them (0 or max_splits)
   const uint16_t* k_cb;
   const uint16_t* v_cb;
-  const float* q_rot;       // [B][Hq][128] fp32, already in K's basis (when q_in is NULL)
-  const void* q_in;         // [B][Hq][128] unrotated q (fp32 or fp16 bits), rotated in-kernel; or NULL
+  const float* q_rot;       // [B][Hq][128] fp32 in K's basis (the reference kernel's input)
+  const void* q_in;         // [B][Hq][128] q as the MFMA kernel reads it (fp32 or fp16 bits)
   int q_fp32;               // q_in is fp32 (else fp16 bits)
-  int q_rotate;             // q_in goes through H(s_K * q)/sqrt(128) (quantised K formats)
+  int q_rotate;             // q_in goes through H(s_K * q)/sqrt(128) in-kernel (else it is in K's basis)
   const float* k_signs;
   const float* v_signs;
   float* part_o;            // [B*Hkv*slots][group][128]   unnormalised sum_t 2^(z_t - m) v_t

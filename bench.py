@@ -61,7 +61,8 @@ def parse():
 
 
 KERNEL_SOURCES = tuple("quantized_kv_cache_decode_amd/csrc/" + f
-                       for f in ("decode_mfma.hip", "decode_ref.hip", "combine.hip", "tq_device.h"))
+                       for f in ("decode_mfma.hip", "decode_ref.hip", "combine.hip", "tq_device.h", "tq_encode.h",
+                                 "tq_launch.h"))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -288,10 +289,14 @@ def main():
     dec_ms = float(np.mean(call_ms)) if call_ms else float("nan")
     achieved = alg / (dec_ms * 1e-3) / 1e9 if call_ms else None
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": recorded_traffic(w.name),
+            "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+            # counters are recorded for the default route (tq_decode_step, MFMA kernel) only
+            "traffic": recorded_traffic(w.name) if args.path == "step" else None,
             "kernel": {"step": "tq_decode_step", "fused": "tq_decode_attention_fused",
                        "separate": "tq_decode_attention"}[args.path]
-            + (" (decode_ref_kernel" if args.variant == 1 else " (decode_mfma_kernel") + " + combine_kernel)",
+            + (" (decode_ref_kernel" if args.variant == 1 else " (decode_mfma_kernel")
+            + (" + step_append_kernel" if args.path == "step" and int(L.sum()) * w.num_kv_heads >= (4 << 20) else "")
+            + " + combine_kernel)",
             "call_us": dec_ms * 1e3,
             "algorithmic_bytes_per_call": alg}
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, seed, args.cpu_seconds)

@@ -665,8 +665,25 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   }
 }
 
+// The decode step's append work groups as a launch of their own (bandwidth-bound
+// calls): column 0 the K side, column 1 the V side of (KV head y, sequence b0 + z).
+template <int KFMT, int VFMT>
+__global__ __launch_bounds__(64) void step_append_kernel(DecodeArgs a, SeqLens lens) {
+  const int h = blockIdx.y, b = a.b0 + blockIdx.z;
+  const int L = min(lens.len[blockIdx.z], a.cap);
+  const size_t row = size_t(b) * a.hkv + h;
+  const int lane = threadIdx.x;
+  __shared__ float qs[kMaxGroup][kDim];
+  if (blockIdx.x == 1) append_v_partial<KFMT, VFMT>(a, row, L, lane);
+  else append_k_work<KFMT, VFMT>(a, qs, row, L, lane);
+}
+
 template <int KF, int VF>
 hipError_t launch_fmt(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
+  if (a.split_cols == 0) {  // the decode step's append alone
+    hipLaunchKernelGGL((step_append_kernel<KF, VF>), dim3(2, a.hkv, batch), dim3(64), 0, stream, a, lens);
+    return hipGetLastError();
+  }
   // decode step: the appended token's two work groups come first
   const dim3 grid(a.col0 + a.split_cols, a.hkv, batch), block(64);
   if (a.group <= 16 / TQ_MFMA_NS_SMALL_GROUP)

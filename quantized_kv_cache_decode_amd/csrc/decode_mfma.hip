@@ -198,10 +198,13 @@ __device__ __forceinline__ void append_v_partial(const DecodeArgs& a, size_t row
 }
 
 // K side: `kin` (quantised K) or `kraw` (F16 K) were requested before the q
-// staging, so their memory round trip overlaps it.
+// staging, so their memory round trip overlaps it.  qs holds the caller's q
+// unrotated; the reconstructed K row is rotated back instead, since the rotation
+// is orthonormal (q_rot . k_hat = q . s_K H(k_hat) / sqrt(128)).
 template <int KFMT, int VFMT>
 __device__ __forceinline__ void append_k_partial(const DecodeArgs& a, const float (*qs)[kDim], size_t row, int L, int lane,
-                                 const RowInputs<KFMT == kFmtF16 ? kFmtTurbo3 : KFMT>& kin, const uint4& kraw) {
+                                 const RowInputs<KFMT == kFmtF16 ? kFmtTurbo3 : KFMT>& kin, const uint4& kraw,
+                                 const float (&ksign)[8]) {
   const int j = lane & 15;
   if (lane >= 16) return;  // one 16-lane group
   constexpr int KQ = KFMT == kFmtF16 ? kFmtTurbo3 : KFMT;
@@ -216,6 +219,10 @@ __device__ __forceinline__ void append_k_partial(const DecodeArgs& a, const floa
     const float nk = half_bits_to_float(append_k_row<KQ>(a.app, row, L, kin, j, code));
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = nk * codebook_at<KQ>(kin.tab, code[e]);
+    // back to the original basis, k = s_K * H(k_hat) / sqrt(128): then q_rot . k_hat = q . k
+    fwht128_row(x, j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * kInvSqrtD * ksign[e];
   }
   // this lane's share of every head's dot product, then one 16-lane reduction for all
   const int G = a.group;
@@ -298,7 +305,8 @@ __device__ __forceinline__ void q_pin(QRaw& q) {
   pin4(q.s1);
 }
 
-__device__ __forceinline__ void q_finish(const DecodeArgs& a, float (*qs)[kDim], int lane, const QRaw& q) {
+__device__ __forceinline__ void q_finish(const DecodeArgs& a, float (*qs)[kDim], int lane, const QRaw& q,
+                                         bool rotate) {
   const int G = a.group, j = lane & 15, r0 = lane >> 4;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -312,7 +320,7 @@ __device__ __forceinline__ void q_finish(const DecodeArgs& a, float (*qs)[kDim],
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = half_bits_to_float(uint16_t(w[i >> 1] >> (16 * (i & 1))));
       }
-      if (a.q_rotate) {
+      if (rotate) {
         const float s8[8] = {q.s0.x, q.s0.y, q.s0.z, q.s0.w, q.s1.x, q.s1.y, q.s1.z, q.s1.w};
         rotate_row_forward8(v, s8, j);
       }
@@ -340,9 +348,12 @@ __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[k
   }
   __builtin_amdgcn_sched_barrier(0);
   q_pin(q);
-  q_finish(a, qs, lane, q);
+  // q stays unrotated: the token's K row is taken back out of the codec basis
+  // instead (one transform rather than one per query row)
+  q_finish(a, qs, lane, q, false);
   __syncthreads();
-  append_k_partial<KFMT, VFMT>(a, qs, row, L, lane, kin, kraw);
+  const float s8[8] = {q.s0.x, q.s0.y, q.s0.z, q.s0.w, q.s1.x, q.s1.y, q.s1.z, q.s1.w};
+  append_k_partial<KFMT, VFMT>(a, qs, row, L, lane, kin, kraw, s8);
 }
 
 #ifndef TQ_MFMA_MIN_WAVES
@@ -454,7 +465,7 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
     vtab = make_table(c);
   }
 
-  q_finish(a, qs, lane, qraw);
+  q_finish(a, qs, lane, qraw, a.q_rotate != 0);
   __syncthreads();
 
   // q in this lane's score-MFMA B slots: q[hn][part*128/P + 8kk + t] * scale*log2(e),

@@ -147,13 +147,26 @@ __device__ __forceinline__ void store_k_record(uint8_t* rec, const uint8_t (&cod
   if (KFMT == kFmtTurbo4) {
     *reinterpret_cast<uint32_t*>(rec + 4 * j) = oct4_pack(code);
   } else {
-    // lanes 4q..4q+3 hold elements 8c..8c+7 (c = j % 4) of sub-block q; OR their fields
-    uint8_t c32[32] = {};
-    const int c0 = 8 * (j & 3);
+    // Lanes 4q..4q+3 hold elements 8c..8c+7 (c = j % 4) of sub-block q.  Lanes with
+    // c < 3 own word c outright (element 8c+i: byte i%4, bits 3*(i/4)); lane c = 3
+    // holds elements 24..31, whose low two bits go to bits 6-7 of words A (24..27)
+    // and B (28..31) and whose top bits go to bits 6 and 7 of word C.  Each lane
+    // builds its share with constant shifts and the 4 lanes OR them together.
+    const int c = j & 3;
+    uint32_t own = 0, t0 = 0, t1 = 0, t2 = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) c32[c0 + e] = code[e];
+    for (int i = 0; i < 8; ++i) own |= (uint32_t(code[i]) & 7u) << (8 * (i & 3) + 3 * (i >> 2));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t0 |= (uint32_t(code[i]) & 3u) << (8 * i + 6);
+      t1 |= (uint32_t(code[4 + i]) & 3u) << (8 * i + 6);
+      t2 |= ((uint32_t(code[i]) >> 2) & 1u) << (8 * i + 6);
+      t2 |= ((uint32_t(code[4 + i]) >> 2) & 1u) << (8 * i + 7);
+    }
     uint32_t w[3];
-    sub3_pack(c32, w);
+    w[0] = c == 0 ? own : (c == 3 ? t0 : 0u);
+    w[1] = c == 1 ? own : (c == 3 ? t1 : 0u);
+    w[2] = c == 2 ? own : (c == 3 ? t2 : 0u);
     w[0] |= xor_lane16<1>(w[0]);
     w[1] |= xor_lane16<1>(w[1]);
     w[2] |= xor_lane16<1>(w[2]);

@@ -131,13 +131,21 @@ __device__ inline floatx4 mfma(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Reductions over the 4 lanes i, i^16, i^32, i^48 of an MFMA column, with the
+// gfx950 row-swap permutes (no LDS round trip).  permlane16_swap(x, x) hands each
+// lane the value of lane i & ~16 and of lane i | 16; permlane32_swap does the
+// same for bit 5.  Every lane of the wave must be active.
 __device__ inline float xmax4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float xsum4(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int N>
@@ -639,10 +647,10 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   // ---- finish: sum l over the column's 4 lanes, merge the NS sets of each head
   float l_tot = xsum4(l_run);
   float m_fin = m_run;
-#pragma unroll
-  for (int stp = Gp; stp < 16; stp <<= 1) {
-    const float m_o = __shfl_xor(m_fin, stp, 64);
-    const float l_o = __shfl_xor(l_tot, stp, 64);
+  auto merge_sets = [&](auto dist) {  // merge with the set `dist` columns away (DPP, within the row)
+    constexpr int STP = decltype(dist)::value;
+    const float m_o = xor_lane16<STP>(m_fin);
+    const float l_o = xor_lane16<STP>(l_tot);
     const float M = fmaxf(m_fin, m_o);
     const float fs = m_fin == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_fin - M);
     const float fo = m_o == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_o - M);
@@ -650,13 +658,15 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float o = __shfl_xor(acc[i][j], stp, 64);
+        const float o = xor_lane16<STP>(acc[i][j]);
         acc[i][j] = acc[i][j] * fs + o * fo;
       }
     }
     l_tot = l_tot * fs + l_o * fo;
     m_fin = M;
-  }
+  };
+  if constexpr (Gp <= 4) merge_sets(std::integral_constant<int, 4>{});
+  if constexpr (Gp <= 8) merge_sets(std::integral_constant<int, 8>{});
   // Partial of this split (unnormalised o, log2-domain m, l); the splits are merged
   // by a separate kernel: a release/acquire hand-off between waves of this kernel
   // would need an L2 write-back per wave, which measured far slower.

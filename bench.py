@@ -295,7 +295,6 @@ def main():
             "kernel": {"step": "tq_decode_step", "fused": "tq_decode_attention_fused",
                        "separate": "tq_decode_attention"}[args.path]
             + (" (decode_ref_kernel" if args.variant == 1 else " (decode_mfma_kernel")
-            + (" + step_append_kernel" if args.path == "step" and int(L.sum()) * w.num_kv_heads >= (4 << 20) else "")
             + " + combine_kernel)",
             "call_us": dec_ms * 1e3,
             "algorithmic_bytes_per_call": alg}

@@ -90,7 +90,10 @@ typedef enum {
  *   k_signs, v_signs   float [128] of +1/-1 (k_signs unused for F16 K).
  *   k_codebook, v_codebook   fp16 bits, ascending, 8 (turbo3) or 16 (turbo4)
  *            entries, symmetric (c[i] = -c[n-1-i]); k_codebook unused for F16 K.
- * capacity must be a positive multiple of 32; head_dim must be 128. */
+ * capacity must be a positive multiple of 32; head_dim must be 128.
+ * The decode kernels read whole 32-token tiles and mask the slots at or past a
+ * sequence's length, whose V norms are multiplied by an exact zero weight: they
+ * must hold finite fp16 values (zero-fill the arrays when allocating them). */
 typedef struct tq_cache {
   int32_t batch;
   int32_t num_kv_heads;
@@ -193,14 +196,14 @@ tq_status tq_decode_attention_fused(const tq_cache* cache, const int32_t* seq_le
 
 /* One whole decode step: append one new token to every sequence and attend to
  * all visible tokens, the new one included -- tq_encode_append (t_new = 1)
- * followed by tq_decode_attention_fused on the grown cache, in two kernels
- * (three on bandwidth-bound calls, >= 4M visible token-heads, where the
- * append runs as a launch of its own so the splits fill the chip in one
- * round).  The new token is encoded and written by two extra work groups per
- * (sequence, KV head) of the decode kernel, which also take the token's own
- * softmax partial (its score against every query head of the group, weight 1,
- * value its reconstructed V row); the regular splits cover the older tokens
- * in parallel and the split merge folds the extra partial in (mlxcel PR #369,
+ * followed by tq_decode_attention_fused on the grown cache, in two kernels.
+ * The new token is encoded and written by two extra work groups per
+ * (sequence, KV head) of the decode kernel (on bandwidth-bound calls, >= 4M
+ * visible token-heads, by the row's first two splits before their own tokens,
+ * so that the splits still fill the chip in one round), which also take the
+ * token's own softmax partial (its score against every query head of the
+ * group, weight 1, value its reconstructed V row); the regular splits cover
+ * the older tokens in parallel and the split merge folds the extra partial in (mlxcel PR #369,
  * "Change": the append is the only cache mutation and the rotated-basis route
  * attends right after it).  Codes, norms and cache->seq_lens end up exactly as
  * after tq_encode_append; the output agrees with the two-call route up to

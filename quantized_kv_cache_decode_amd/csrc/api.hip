@@ -75,7 +75,7 @@ tq_status check_lengths(const tq_cache* c, const int32_t* lens, int32_t extra) {
 #define TQ_PLAN_ITEMS 4096               // work items aimed for, group size > 4
 #endif
 #ifndef TQ_PLAN_FLOOR
-#define TQ_PLAN_FLOOR 260   // bandwidth-bound calls: chunk >= TQ_PLAN_FLOOR * group tokens
+#define TQ_PLAN_FLOOR 200   // bandwidth-bound calls: chunk >= TQ_PLAN_FLOOR * group tokens
 #endif
 
 // Split plan shared by the workspace query and the launch.  A fixed number of
@@ -229,7 +229,7 @@ tq_status decode_setup(const tq_cache* cache, const int32_t* seq_lens_host, int3
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + partial_floats(cache, num_q_heads, plan) * 128;
   a.col0 = 0;
-  a.split_cols = plan.max_splits;
+  a.split_append = 0;
   return TQ_OK;
 }
 
@@ -246,17 +246,12 @@ tq_status launch_decode_and_merge(const tq_cache* cache, const int32_t* seq_lens
     a.b0 = b0;
     a.app.b0 = b0;
     tq_status st;
-    if (a.app.k_new && a.plan.bandwidth_bound) {
-      // decode step on a bandwidth-bound call: the token's work groups go first, in a
-      // launch of their own, so the splits still fill the chip in one round
-      tq::DecodeArgs ap = a;
-      ap.col0 = 2;
-      ap.split_cols = 0;
-      if ((st = hip_status(tq::launch_decode_mfma(ap, lens, nb, s), "append launch")) != TQ_OK) return st;
-      a.col0 = 0;
-    } else {
-      a.col0 = a.app.k_new ? 2 : 0;
-    }
+    // Decode step: on latency-bound calls the token gets two work groups of its own
+    // (grid columns 0 and 1), which run beside the splits; on bandwidth-bound calls
+    // the splits fill the chip in one round and the row's first two splits append it.
+    const bool step = a.app.k_new != nullptr;
+    a.col0 = step && !a.plan.bandwidth_bound ? 2 : 0;
+    a.split_append = step && a.plan.bandwidth_bound;
     const hipError_t e = variant == 1 ? tq::launch_decode_reference(a, lens, nb, s)
                                       : tq::launch_decode_mfma(a, lens, nb, s);
     if ((st = hip_status(e, "decode launch")) != TQ_OK) return st;

@@ -8,13 +8,16 @@
 // so every weight is one hardware exp2).  The merged output is
 // sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s for any M; M = max_s m_s.
 //
-// 256 threads: lane j = tid % 16 owns dims 8j..8j+7 and split group sg = tid / 16
-// takes splits sg, sg + 16, ...  Every load of a batch is independent (one
-// memory round trip for up to 64 splits); each group keeps a running (m, l, o),
-// and the 16 groups are merged through LDS by the 16 threads of group 0, which
-// hold exactly the 16-lane row layout the in-register Walsh-Hadamard transform
-// wants.
+// One wave per (sequence, query head): lane j = lane % 16 owns dims 8j..8j+7 and
+// lane group sg = lane / 16 takes splits sg, sg + 4, ...  Every load of a round
+// is independent (one memory round trip for up to 4 * kBatch splits); each group
+// keeps a running (m, l, o), and the four groups are merged with the gfx950 row
+// swaps (lane bit 4, then bit 5) -- no LDS, no barrier.  Every group then holds
+// the merged row in the 16-lane layout the in-register Walsh-Hadamard transform
+// wants; group 0 stores it.
 #include <math.h>
+
+#include <algorithm>
 
 #include "tq_device.h"
 #include "tq_launch.h"
@@ -22,13 +25,60 @@
 namespace tq {
 namespace {
 
-constexpr int kSplitGroups = 16;
-constexpr int kBatch = 5;  // splits per thread per round of loads (80 per round)
+constexpr int kGroups = 4;     // lane groups of 16 per wave
+constexpr int kMaxBatch = 17;  // splits per lane group per round (68 per round)
 
 __device__ inline float weight(float m, float M) { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M); }
 
-template <bool INVERSE>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, SeqLens lens) {
+// Running state of a lane: the merge of the splits it has seen.
+struct Acc {
+  float m, l, o[8];
+};
+
+// Two states in a fixed order (x from the lower lane), so both lanes of a swapped
+// pair compute the same bits.
+__device__ inline Acc merge(const Acc& x, const Acc& y) {
+  const float M = fmaxf(x.m, y.m);
+  Acc r;
+  r.m = M;
+  if (M == -INFINITY) {
+    r.l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.o[i] = 0.f;
+    return r;
+  }
+  const float wx = weight(x.m, M), wy = weight(y.m, M);
+  r.l = x.l * wx + y.l * wy;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.o[i] = x.o[i] * wx + y.o[i] * wy;
+  return r;
+}
+
+// permlane16_swap(v, v) gives lane i the values of lanes i & ~16 and i | 16;
+// permlane32_swap the same for bit 5.  All 64 lanes must be active.
+template <bool BIT5>
+__device__ inline void swap_pair(float v, float& lo, float& hi) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = BIT5 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                      : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+template <bool BIT5>
+__device__ inline Acc merge_across(const Acc& a) {
+  Acc lo, hi;
+  swap_pair<BIT5>(a.m, lo.m, hi.m);
+  swap_pair<BIT5>(a.l, lo.l, hi.l);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) swap_pair<BIT5>(a.o[i], lo.o[i], hi.o[i]);
+  return merge(lo, hi);
+}
+
+// kBatch: splits per lane group per round, sized at launch to the call's longest
+// sequence so that short calls do not issue loads they then mask.
+template <bool INVERSE, int kBatch>
+__global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens) {
   // No multiply-add contraction here: the normalised output must round the same
   // whether it goes to memory (then to the stand-alone inverse rotation) or
   // straight into the in-register rotation below.
@@ -43,12 +93,14 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, SeqLens lens
   const int nsplit = min((L + a.plan.chunk - 1) / a.plan.chunk, a.plan.max_splits);
   const int nparts = nsplit + (step ? 1 : 0);  // partial v lives in slot v, the step's last in slot max_splits
   const size_t p0 = partial_index(a, size_t(b) * a.hkv + h, 0, g);  // slot s: p0 + s*G
-  const int j = threadIdx.x & 15, sg = threadIdx.x >> 4;
+  const int lane = threadIdx.x, j = lane & 15, sg = lane >> 4;
 
-  float m = -INFINITY, l = 0.f, o[8];
+  Acc acc;
+  acc.m = -INFINITY;
+  acc.l = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = 0.f;
-  for (int s0 = sg; s0 < nparts; s0 += kSplitGroups * kBatch) {
+  for (int i = 0; i < 8; ++i) acc.o[i] = 0.f;
+  for (int s0 = sg; s0 < nparts; s0 += kGroups * kBatch) {
     float ms[kBatch], ls[kBatch];
     float4 oa[kBatch], ob[kBatch];
     // Every load of the round is issued unconditionally (a partial past the end
@@ -56,7 +108,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, SeqLens lens
     // memory round trip instead of one per partial.
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int v = s0 + kSplitGroups * k;
+      const int v = s0 + kGroups * k;
       const size_t p = p0 + size_t(v < nsplit ? v : (v < nparts ? a.plan.max_splits : 0)) * G;
       const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * p);
       const float4* src = reinterpret_cast<const float4*>(a.part_o + p * kDim + 8 * j);
@@ -67,78 +119,74 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, SeqLens lens
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      if (s0 + kSplitGroups * k >= nparts) {
+      if (s0 + kGroups * k >= nparts) {
         ms[k] = -INFINITY;
         ls[k] = 0.f;
         oa[k] = ob[k] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
-    float mn = m;
+    float mn = acc.m;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) mn = fmaxf(mn, ms[k]);
     if (mn == -INFINITY) continue;  // nothing seen yet (every l is 0 too)
-    const float c = weight(m, mn);
-    l *= c;
+    const float c = weight(acc.m, mn);
+    acc.l *= c;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= c;
+    for (int i = 0; i < 8; ++i) acc.o[i] *= c;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const float w = weight(ms[k], mn);
-      l += w * ls[k];
-      o[0] += w * oa[k].x; o[1] += w * oa[k].y; o[2] += w * oa[k].z; o[3] += w * oa[k].w;
-      o[4] += w * ob[k].x; o[5] += w * ob[k].y; o[6] += w * ob[k].z; o[7] += w * ob[k].w;
+      acc.l += w * ls[k];
+      acc.o[0] += w * oa[k].x; acc.o[1] += w * oa[k].y; acc.o[2] += w * oa[k].z; acc.o[3] += w * oa[k].w;
+      acc.o[4] += w * ob[k].x; acc.o[5] += w * ob[k].y; acc.o[6] += w * ob[k].z; acc.o[7] += w * ob[k].w;
     }
-    m = mn;
+    acc.m = mn;
   }
 
-  __shared__ float sm[kSplitGroups], sl[kSplitGroups];
-  __shared__ float4 so[kSplitGroups][32];
-  so[sg][2 * j] = make_float4(o[0], o[1], o[2], o[3]);
-  so[sg][2 * j + 1] = make_float4(o[4], o[5], o[6], o[7]);
-  if (j == 0) {
-    sm[sg] = m;
-    sl[sg] = l;
-  }
-  __syncthreads();
-  if (threadIdx.x >= 16) return;  // group 0 finishes (lanes 0..15 of wave 0)
-
-  float M = sm[0];
+  acc = merge_across<false>(acc);  // groups {0,1} and {2,3}
+  acc = merge_across<true>(acc);   // then the two halves: every lane holds the merged row
+  float v[8];
+  const float inv = nparts > 0 ? 1.f / acc.l : 0.f;
 #pragma unroll
-  for (int k = 1; k < kSplitGroups; ++k) M = fmaxf(M, sm[k]);
-  float lt = 0.f, v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = 0.f;
-#pragma unroll
-  for (int k = 0; k < kSplitGroups; ++k) {
-    const float w = weight(sm[k], M);
-    const float4 x = so[k][2 * j], y = so[k][2 * j + 1];
-    lt += w * sl[k];
-    v[0] += w * x.x; v[1] += w * x.y; v[2] += w * x.z; v[3] += w * x.w;
-    v[4] += w * y.x; v[5] += w * y.y; v[6] += w * y.z; v[7] += w * y.w;
-  }
-  const float inv = nparts > 0 ? 1.f / lt : 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = nparts > 0 ? v[i] * inv : 0.f;
+  for (int i = 0; i < 8; ++i) v[i] = nparts > 0 ? acc.o[i] * inv : 0.f;
   // the step's length update, once every reader of the old length has finished
-  if (step && hq == 0 && j == 0) a.app.seq_lens[b] = L + 1;
+  if (step && hq == 0 && lane == 0) a.app.seq_lens[b] = L + 1;
   const size_t row = size_t(b) * a.hkv * G + hq;
   if (INVERSE) {
     uint32_t w[4];
-    rotate_row_inverse_f16(v, a.v_signs, j, w);
-    *reinterpret_cast<uint4*>(a.out + row * kDim + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
+    rotate_row_inverse_f16(v, a.v_signs, j, w);  // every row of 16 lanes, the same bits
+    if (sg == 0) *reinterpret_cast<uint4*>(a.out + row * kDim + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if (sg == 0) {
     float4* dst = reinterpret_cast<float4*>(a.out_rot + row * kDim + 8 * j);
     dst[0] = make_float4(v[0], v[1], v[2], v[3]);
     dst[1] = make_float4(v[4], v[5], v[6], v[7]);
   }
 }
 
+template <bool INVERSE>
+void launch_batch(const DecodeArgs& a, const SeqLens& lens, int nb, int rounds, hipStream_t stream) {
+  const dim3 grid(a.hkv * a.group, nb), block(64);
+  if (rounds <= 1) hipLaunchKernelGGL((combine_kernel<INVERSE, 1>), grid, block, 0, stream, a, lens);
+  else if (rounds <= 2) hipLaunchKernelGGL((combine_kernel<INVERSE, 2>), grid, block, 0, stream, a, lens);
+  else if (rounds <= 3) hipLaunchKernelGGL((combine_kernel<INVERSE, 3>), grid, block, 0, stream, a, lens);
+  else if (rounds <= 5) hipLaunchKernelGGL((combine_kernel<INVERSE, 5>), grid, block, 0, stream, a, lens);
+  else if (rounds <= 9) hipLaunchKernelGGL((combine_kernel<INVERSE, 9>), grid, block, 0, stream, a, lens);
+  else hipLaunchKernelGGL((combine_kernel<INVERSE, kMaxBatch>), grid, block, 0, stream, a, lens);
+}
+
 }  // namespace
 
 hipError_t launch_combine(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
-  const dim3 grid(a.hkv * a.group, batch), block(256);
-  if (a.out) hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream, a, lens);
-  else hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream, a, lens);
+  // partials of the longest sequence of the launch (the step's own slot included)
+  int most = 0;
+  for (int i = 0; i < batch; ++i) {
+    const int L = std::min(lens.len[i], a.cap);
+    most = std::max(most, std::min((L + a.plan.chunk - 1) / a.plan.chunk, a.plan.max_splits));
+  }
+  most += a.app.k_new != nullptr ? 1 : 0;
+  const int rounds = (most + kGroups - 1) / kGroups;
+  if (a.out) launch_batch<true>(a, lens, batch, rounds, stream);
+  else launch_batch<false>(a, lens, batch, rounds, stream);
   return hipGetLastError();
 }
 

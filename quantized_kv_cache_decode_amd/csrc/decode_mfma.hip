@@ -390,7 +390,7 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   const int chunk = a.plan.chunk;
   const int nsplit = min((L + chunk - 1) / chunk, a.plan.max_splits);
   const bool append_wg = s < 0;
-  if (s >= nsplit) return;
+  if (s >= nsplit && !(a.split_append && s < 2)) return;
   const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
   const int t0 = s * chunk;
   const int t1 = (s == nsplit - 1) ? L : t0 + chunk;
@@ -410,6 +410,17 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
     if (s == -1) append_v_partial<KFMT, VFMT>(a, row, L, lane);  // the V side needs no q
     else append_k_work<KFMT, VFMT>(a, qs, row, L, lane);
     return;
+  }
+  if (a.split_append && s < 2) {
+    // Bandwidth-bound step: two extra work groups would not fit in the one round of
+    // splits, so the first two splits of the row append the token before their own
+    // tokens (the kernel's other waves keep streaming meanwhile).
+    __builtin_amdgcn_s_setprio(3);
+    if (s == 0) append_k_work<KFMT, VFMT>(a, qs, row, L, lane);
+    if (s == 1 || a.plan.max_splits == 1) append_v_partial<KFMT, VFMT>(a, row, L, lane);
+    __builtin_amdgcn_s_setprio(0);
+    if (s >= nsplit) return;
+    __syncthreads();  // the K side's reads of qs come before the rows staged below
   }
 
   // Register double-buffering by rotation: the K words of iteration i+1 are
@@ -686,27 +697,10 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   }
 }
 
-// The decode step's append work groups as a launch of their own (bandwidth-bound
-// calls): column 0 the K side, column 1 the V side of (KV head y, sequence b0 + z).
-template <int KFMT, int VFMT>
-__global__ __launch_bounds__(64) void step_append_kernel(DecodeArgs a, SeqLens lens) {
-  const int h = blockIdx.y, b = a.b0 + blockIdx.z;
-  const int L = min(lens.len[blockIdx.z], a.cap);
-  const size_t row = size_t(b) * a.hkv + h;
-  const int lane = threadIdx.x;
-  __shared__ float qs[kMaxGroup][kDim];
-  if (blockIdx.x == 1) append_v_partial<KFMT, VFMT>(a, row, L, lane);
-  else append_k_work<KFMT, VFMT>(a, qs, row, L, lane);
-}
-
 template <int KF, int VF>
 hipError_t launch_fmt(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
-  if (a.split_cols == 0) {  // the decode step's append alone
-    hipLaunchKernelGGL((step_append_kernel<KF, VF>), dim3(2, a.hkv, batch), dim3(64), 0, stream, a, lens);
-    return hipGetLastError();
-  }
-  // decode step: the appended token's two work groups come first
-  const dim3 grid(a.col0 + a.split_cols, a.hkv, batch), block(64);
+  // decode step: the appended token's two work groups (if any) come first
+  const dim3 grid(a.col0 + a.plan.max_splits, a.hkv, batch), block(64);
   if (a.group <= 16 / TQ_MFMA_NS_SMALL_GROUP)
     hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, TQ_MFMA_NS_SMALL_GROUP>), grid, block, 0, stream, a, lens);
   else if (a.group <= 8) hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 2>), grid, block, 0, stream, a, lens);

@@ -67,7 +67,8 @@ struct DecodeArgs {
   const uint16_t* v_norms;
   int b0;                   // first sequence of the launch (blockIdx z / y counts from it)
   int col0;                 // decode kernel grid: columns 0..col0-1 append the step's token (0 or 2)
-  int split_cols;           // decode kernel grid: split columns after them (0 or max_splits)
+  int split_append;         // decode step with col0 = 0: split 0 appends K and split 1 (split 0 when
+                            // max_splits = 1) appends V, each before its own split
   const uint16_t* k_cb;
   const uint16_t* v_cb;
   const float* q_rot;       // [B][Hq][128] fp32 in K's basis (the reference kernel's input)

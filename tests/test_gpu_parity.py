@@ -330,3 +330,24 @@ def test_full_size_sampled(index, codebooks):
         rel, mx = S.assert_close(got[b], S.oracle_on_bytes(cache, b, int(L[b]), q[b], codebooks), f"b={b}")
         _say(f"[full {w.name}] b={b} rel-L2 {rel:.2e} max-abs {mx:.2e}")
     assert np.all(np.isfinite(got.astype(np.float32)))
+
+
+@pytest.mark.timeout(600)
+def test_bandwidth_bound_step_edge_rows(codebooks):
+    """A step large enough (>= 4M token-heads) that the row's first two splits append the token,
+    with rows whose step appends their first token, whose only split is the one appending K,
+    and rows whose earlier tokens end one short of and exactly on a split boundary (splits of
+    1600 tokens here)."""
+    w = get_workload(4)
+    lens = np.array([1, 2, 33, 1600, 1601, 131072, 131072, 131072, 131072])
+    w = S.scaled(w, batch=len(lens))
+    assert int((lens - 1).sum()) * w.num_kv_heads >= 4 << 20
+    _say("[bandwidth-bound step] generating + encoding")
+    cache, k_list, v_list, L, q, got = S.prefill_then_decode_step(w, lengths=lens)
+    np.testing.assert_array_equal(cache.seq_lens.cpu().numpy(), L)
+    for b in (0, 1, 2, 3, 4, 5):
+        m, g, t = S.compare_codes(cache, b, k_list[b], v_list[b], int(L[b]), w, codebooks)
+        assert m <= g <= 1e-4 * t
+        rel, mx = S.assert_close(got[b], S.oracle_on_bytes(cache, b, int(L[b]), q[b], codebooks), f"b={b}")
+        _say(f"[bandwidth-bound step] b={b} L={int(L[b])} rel-L2 {rel:.2e} max-abs {mx:.2e}")
+    assert np.all(np.isfinite(got.astype(np.float32)))

@@ -109,3 +109,37 @@ def attention_rotated(q, k_codes, k_norms, v_codes, v_norms, lengths, scale, k_c
             p = np.exp(z - z.max())
             out_rot[b, h] = (p / p.sum()) @ vb[g, :L]
     return inverse_rotate(out_rot, v_signs)
+
+
+def sparse_v_bound(q, k_hat, v_hat, length, scale: float, tau: float):
+    """What sparse V may drop from one sequence's attention (float64).
+
+    The V-side skip (turboquant_plus "SMEM Pre-Dequant Experiment", idea 2 "Sparse K
+    attention", which names the existing SPARSE_V skip of V work for negligible
+    weights; mlxcel PR #369, commit "docs(cache): add ADR 0002 ... (sparse-V study)":
+    exact below fp16 round-off at tau = 1e-6) leaves the scores and the softmax sum
+    alone and drops only p_t v_t terms.  A decoder may drop token t of KV head g only
+    when every query head of g gives it a weight below tau relative to that head's
+    largest weight.  Returns (o, bound): o [Hq, D] the exact attention, and bound
+    [Hq, D] = sum over such tokens t of w_{h,t} |v_{g,t}| (w the normalised weights),
+    the most any choice of dropped tokens can move o.
+
+    q [Hq, D]; k_hat, v_hat [Hkv, L, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    kb = np.asarray(k_hat, dtype=np.float64)
+    vb = np.asarray(v_hat, dtype=np.float64)
+    Hq, D = q.shape
+    hkv = kb.shape[0]
+    group = Hq // hkv
+    L = int(length)
+    o = np.zeros((Hq, D))
+    bound = np.zeros((Hq, D))
+    for g in range(hkv):
+        heads = range(g * group, (g + 1) * group)
+        rel = np.stack([np.exp(scale * (kb[g, :L] @ q[h]) - (scale * (kb[g, :L] @ q[h])).max()) for h in heads])
+        droppable = np.all(rel < tau, axis=0)          # [L]
+        for i, h in enumerate(heads):
+            w = rel[i] / rel[i].sum()
+            o[h] = w @ vb[g, :L]
+            bound[h] = (w * droppable) @ np.abs(vb[g, :L])
+    return o, bound

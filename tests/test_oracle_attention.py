@@ -121,3 +121,61 @@ def test_reference_glue_round_trips_through_the_layout(codebooks):
     o_exact = att.attention(q[None], [k16.astype(np.float64)], [v16.astype(np.float64)], [256], SCALE)[0]
     # 3-bit codes: the quantised attention stays close to the unquantised one
     assert np.linalg.norm(o - o_exact) / np.linalg.norm(o_exact) < 0.5
+
+
+def test_sparse_v_bound_hand_example():
+    """Three tokens, one KV head, two query heads, D = 1: scores (scale 1) of head 0 are
+    0, -20, -1 and of head 1 are 0, -30, -40.  Relative weights: head 0 [1, e^-20, e^-1],
+    head 1 [1, e^-30, e^-40].  At tau = 1e-6 only token 1 is below tau for both heads
+    (token 2 is not, for head 0), so the bound is w_{h,1} |v_1| per head."""
+    from oracle.attention import sparse_v_bound
+    # scores are q.k: with q = 1, K holds the wanted scores, one head at a time
+    k0 = np.array([[[0.0], [-20.0], [-1.0]]])         # [Hkv=1, L=3, D=1]
+    k1 = np.array([[[0.0], [-30.0], [-40.0]]])
+    v = np.array([[[2.0], [-3.0], [5.0]]])
+    for kk, rel in ((k0, [1.0, np.exp(-20.0), np.exp(-1.0)]), (k1, [1.0, np.exp(-30.0), np.exp(-40.0)])):
+        o, b = sparse_v_bound(np.array([[1.0]]), kk, v, 3, 1.0, 1e-6)
+        w = np.array(rel) / sum(rel)
+        np.testing.assert_allclose(o[0, 0], w @ v[0, :, 0], rtol=1e-15)
+    # both heads together: head 0 on k0-scores and head 1 on k1-scores need one K per head,
+    # so use two-dimensional K with q selecting the coordinate
+    k = np.concatenate([k0, k1], axis=2)              # [1, 3, 2]
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    vv = np.repeat(v, 2, axis=2)
+    o, b = sparse_v_bound(q, k, vv, 3, 1.0, 1e-6)
+    w0 = np.array([1.0, np.exp(-20.0), np.exp(-1.0)])
+    w0 /= w0.sum()
+    w1 = np.array([1.0, np.exp(-30.0), np.exp(-40.0)])
+    w1 /= w1.sum()
+    np.testing.assert_allclose(b[0], [w0[1] * 3.0] * 2, rtol=1e-12)
+    np.testing.assert_allclose(b[1], [w1[1] * 3.0] * 2, rtol=1e-12)
+    # tau = 0 drops nothing; tau = 1 drops every token that is nobody's maximum
+    _, b0 = sparse_v_bound(q, k, vv, 3, 1.0, 0.0)
+    assert np.all(b0 == 0)
+    _, b1 = sparse_v_bound(q, k, vv, 3, 1.0, 1.0)
+    np.testing.assert_allclose(b1[0], [w0[1] * 3.0 + w0[2] * 5.0] * 2, rtol=1e-12)
+
+
+def test_sparse_v_bound_covers_any_dropped_subset():
+    """Dropping any subset of the droppable tokens from the p.v sum (the softmax sum
+    unchanged) moves o by at most the bound; o is the exact attention."""
+    from oracle.attention import attention, sparse_v_bound
+    rng = np.random.default_rng(3)
+    hkv, G, L, D = 2, 3, 200, 16
+    k = rng.standard_normal((hkv, L, D)) * 3.0
+    v = rng.standard_normal((hkv, L, D))
+    q = rng.standard_normal((hkv * G, D)) * 3.0
+    tau = 1e-3
+    o, bound = sparse_v_bound(q, k, v, L, 0.5, tau)
+    np.testing.assert_allclose(o, attention(q[None], [k], [v], [L], 0.5)[0], rtol=1e-12, atol=1e-14)
+    for h in range(hkv * G):
+        g = h // G
+        z = np.stack([0.5 * (k[g] @ q[hh]) for hh in range(g * G, (g + 1) * G)])
+        rel = np.exp(z - z.max(axis=1, keepdims=True))
+        droppable = np.all(rel < tau, axis=0)
+        assert droppable.any()
+        w = rel[h - g * G] / rel[h - g * G].sum()
+        for trial in range(5):
+            drop = droppable & (rng.random(L) < 0.5)
+            o_drop = (w * ~drop) @ v[g]
+            assert np.all(np.abs(o_drop - o[h]) <= bound[h] + 1e-15)

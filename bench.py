@@ -57,6 +57,10 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--v-skip-threshold", type=float, default=0.0,
+                   help="sparse-V weight threshold of the decode calls (0 = exact attention)")
+    p.add_argument("--q-scale", type=float, default=1.0,
+                   help="multiply the synthetic queries (e.g. 16 for peaked attention weights)")
     return p.parse_args()
 
 
@@ -109,7 +113,7 @@ def clone_cache(master):
         master.batch, master.num_kv_heads, 128, master.capacity, master._desc.k_format, master._desc.v_format,
         c.k_data.data_ptr(), 0 if c.k_norms is None else c.k_norms.data_ptr(), c.v_data.data_ptr(),
         c.v_norms.data_ptr(), c.seq_lens.data_ptr(), master.k_signs.data_ptr(), master.v_signs.data_ptr(),
-        master.k_codebook.data_ptr(), master.v_codebook.data_ptr())
+        master.k_codebook.data_ptr(), master.v_codebook.data_ptr(), master._desc.v_skip_threshold)
     return c
 
 
@@ -181,6 +185,7 @@ def main():
 
     # ---- setup (not timed): prefill L-1 tokens, append the step's token once
     master, _, _, L, q_np = S.prefill_and_step(w, seed)
+    master.v_skip_threshold = args.v_skip_threshold   # (the copies below inherit it)
     pre = (L - 1).astype(np.int32)
     per_copy = cache_bytes(master)
     n_copies = max(1, int(math.ceil(args.copies_gib * (1 << 30) / per_copy)))
@@ -189,6 +194,7 @@ def main():
                           for b in range(w.batch)], 1)
     vn = S.padded_tensor([np.stack([new_token_kv(w, seed, "v", b, h, 0) for h in range(w.num_kv_heads)])
                           for b in range(w.batch)], 1)
+    q_np = (q_np.astype(np.float32) * args.q_scale).astype(q_np.dtype)
     q = torch.from_numpy(np.ascontiguousarray(q_np)).cuda()
     B, Hq = w.batch, w.num_q_heads
     q_rot = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
@@ -308,7 +314,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads,
                    "context_total": int(L.sum()), "k_format": w.k_format, "v_format": w.v_format,
                    "cache_copies": n_copies, "graph": use_graph,
-                   "path": args.path, "variant": args.variant},
+                   "path": args.path, "variant": args.variant,
+                   "v_skip_threshold": args.v_skip_threshold, "q_scale": args.q_scale},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -90,6 +90,18 @@ typedef enum {
  *   k_signs, v_signs   float [128] of +1/-1 (k_signs unused for F16 K).
  *   k_codebook, v_codebook   fp16 bits, ascending, 8 (turbo3) or 16 (turbo4)
  *            entries, symmetric (c[i] = -c[n-1-i]); k_codebook unused for F16 K.
+ *   v_skip_threshold   sparse V, in [0, 1]; 0 turns it off.  The MFMA decode
+ *            kernel skips the V dequant and the p.v products of a 32-token V
+ *            tile for the query heads of a KV head when every weight of the tile,
+ *            relative to the running maximum (so also relative to the final one),
+ *            is below the threshold.  The score pass and the softmax sum still
+ *            see every token: the result differs from exact attention by at most
+ *            the skipped weights times |v|.  At 1e-6 the skipped weights sit below
+ *            fp16 round-off (mlxcel PR #369, commit "docs(cache): add ADR 0002 on
+ *            Turbo KV split-dequant vs fused (sparse-V study)"; turboquant_plus
+ *            "SMEM Pre-Dequant Experiment", idea 2 "Sparse K attention", names the
+ *            V-side skip).  The VALU reference variant (tq_decode_attention_variant
+ *            1) ignores it and is exact.
  * capacity must be a positive multiple of 32; head_dim must be 128.
  * The decode kernels read whole 32-token tiles and mask the slots at or past a
  * sequence's length, whose V norms are multiplied by an exact zero weight: they
@@ -110,6 +122,7 @@ typedef struct tq_cache {
   const float* v_signs;
   const uint16_t* k_codebook;
   const uint16_t* v_codebook;
+  float v_skip_threshold;
 } tq_cache;
 
 /* Encode new tokens and append them to each sequence

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "../../include/tqattn.h"
 #include "tq_device.h"
@@ -41,6 +42,8 @@ tq_status check_cache(const tq_cache* c) {
     return fail(TQ_EINVAL, "NULL cache pointer");
   if (is_turbo(c->k_format) && (!c->k_norms || !c->k_signs || !c->k_codebook))
     return fail(TQ_EINVAL, "NULL K norm/sign/codebook pointer for a quantised K format");
+  if (!(c->v_skip_threshold >= 0.f && c->v_skip_threshold <= 1.f))
+    return fail(TQ_EINVAL, "v_skip_threshold %g outside [0, 1]", (double)c->v_skip_threshold);
   const long long slots = (long long)c->batch * c->num_kv_heads * c->capacity;
   if (slots * 128 > (1LL << 46)) return fail(TQ_EINVAL, "cache too large");
   return TQ_OK;
@@ -230,6 +233,7 @@ tq_status decode_setup(const tq_cache* cache, const int32_t* seq_lens_host, int3
   a.part_ml = a.part_o + partial_floats(cache, num_q_heads, plan) * 128;
   a.col0 = 0;
   a.split_append = 0;
+  a.v_skip_log2 = cache->v_skip_threshold > 0.f ? std::log2(cache->v_skip_threshold) : -INFINITY;
   return TQ_OK;
 }
 

@@ -370,7 +370,9 @@ __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[k
 template <int NS>
 constexpr int min_waves() { return TQ_MFMA_MIN_WAVES == 0 ? 1 : (NS == 4 ? TQ_MFMA_MIN_WAVES - 1 : TQ_MFMA_MIN_WAVES); }
 
-template <int KFMT, int VFMT, int NS>
+// SPARSE: the sparse-V skip is compiled in (its per-set branches cost the exact
+// route a few percent of scheduling freedom, so that route goes without them).
+template <int KFMT, int VFMT, int NS, bool SPARSE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(min_waves<NS>())))
 void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   constexpr int P = 4 / NS;                  // lane groups per set in the score MFMA
@@ -548,11 +550,10 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
         z[4 * rb + j] = KFMT != kFmtF16 ? half_bits_to_float(uint16_t(w >> (16 * (j & 1)))) : 1.f;
       }
     }
-    floatx4 S[2], S2[2];                          // two accumulator chains per row block
+    floatx4 S[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       S[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      S2[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         half8 A;
@@ -575,10 +576,8 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
 #else
         const half8 qk = qb[kk];
 #endif
-        if (kk & 1) S2[rb] = mfma(A, qk, S2[rb]);
-        else S[rb] = mfma(A, qk, S[rb]);
+        S[rb] = mfma(A, qk, S[rb]);
       }
-      S[rb] += S2[rb];
     }
     load_k(base + TOK);     // next iteration's K words and K norms
 
@@ -622,9 +621,15 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
     }
     l_run += psum;
 
-    // ---- values: one MFMA group per set; B is zero outside the set
+    // ---- values: one MFMA group per set; B is zero outside the set.  Sparse V: a
+    // set whose real heads all have every weight of its tile below the threshold
+    // (relative to the running max) skips its tile (wave-uniform branch).
+    const uint64_t keep = SPARSE ? __ballot(hn < G && mt - m_use >= a.v_skip_log2) : ~0ull;
 #pragma unroll
     for (int sg = 0; sg < NS; ++sg) {
+      constexpr uint64_t kRow = (1ull << Gp) - 1;
+      const uint64_t set_lanes = (kRow << (sg * Gp)) * 0x0001000100010001ull;  // columns of set sg, all 4 rows
+      if (SPARSE && (keep & set_lanes) == 0) continue;
       const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
       const half8 bsg = (sn == sg) ? pb : zero8;
 #pragma unroll
@@ -697,14 +702,20 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   }
 }
 
-template <int KF, int VF>
-hipError_t launch_fmt(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
+template <int KF, int VF, bool SPARSE>
+void launch_sets(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
   // decode step: the appended token's two work groups (if any) come first
   const dim3 grid(a.col0 + a.plan.max_splits, a.hkv, batch), block(64);
   if (a.group <= 16 / TQ_MFMA_NS_SMALL_GROUP)
-    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, TQ_MFMA_NS_SMALL_GROUP>), grid, block, 0, stream, a, lens);
-  else if (a.group <= 8) hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 2>), grid, block, 0, stream, a, lens);
-  else hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 1>), grid, block, 0, stream, a, lens);
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, TQ_MFMA_NS_SMALL_GROUP, SPARSE>), grid, block, 0, stream, a, lens);
+  else if (a.group <= 8) hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 2, SPARSE>), grid, block, 0, stream, a, lens);
+  else hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 1, SPARSE>), grid, block, 0, stream, a, lens);
+}
+
+template <int KF, int VF>
+hipError_t launch_fmt(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
+  if (a.v_skip_log2 > -INFINITY) launch_sets<KF, VF, true>(a, lens, batch, stream);
+  else launch_sets<KF, VF, false>(a, lens, batch, stream);
   return hipGetLastError();
 }
 

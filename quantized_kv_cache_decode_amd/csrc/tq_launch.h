@@ -75,6 +75,7 @@ struct DecodeArgs {
   const void* q_in;         // [B][Hq][128] q as the MFMA kernel reads it (fp32 or fp16 bits)
   int q_fp32;               // q_in is fp32 (else fp16 bits)
   int q_rotate;             // q_in goes through H(s_K * q)/sqrt(128) in-kernel (else it is in K's basis)
+  float v_skip_log2;        // sparse V: log2 of the weight threshold, -inf when off
   const float* k_signs;
   const float* v_signs;
   float* part_o;            // [B*Hkv*slots][group][128]   unnormalised sum_t 2^(z_t - m) v_t

@@ -68,6 +68,12 @@ def download_sequence(cache, b):
 
 def oracle_on_bytes(cache, b, L, q_b, codebooks, seed=0):
     """Oracle attention [Hq, 128] over the GPU-written bytes of sequence b (unpacked by the oracle)."""
+    k_hat, v_hat = oracle_dequant_bytes(cache, b, L, codebooks, seed)
+    return reference.decode_sequence(q_b, k_hat, v_hat, L)
+
+
+def oracle_dequant_bytes(cache, b, L, codebooks, seed=0):
+    """K and V [Hkv, L, 128] (float64, original basis) of sequence b from the GPU-written bytes."""
     d = download_sequence(cache, b)
     kc, vc = reference.codes_from_library_layout(d.get("k_rec"), d["v_tiles"], cache.k_format, cache.v_format)
     enc = {"v_codes": vc, "v_norms": d["v_norms"]}
@@ -75,9 +81,8 @@ def oracle_on_bytes(cache, b, L, q_b, codebooks, seed=0):
         enc["k_f16"] = d["k_f16"]
     else:
         enc["k_codes"], enc["k_norms"] = kc, d["k_norms"]
-    k_hat, v_hat = reference.dequant_sequence(enc, cache.k_format, cache.v_format, sign_vector(seed, "k"),
-                                              sign_vector(seed, "v"), codebooks, L)
-    return reference.decode_sequence(q_b, k_hat, v_hat, L)
+    return reference.dequant_sequence(enc, cache.k_format, cache.v_format, sign_vector(seed, "k"),
+                                      sign_vector(seed, "v"), codebooks, L)
 
 
 def oracle_end_to_end(w, k16, v16, L, q_b, codebooks, seed=0):

@@ -351,3 +351,66 @@ def test_bandwidth_bound_step_edge_rows(codebooks):
         rel, mx = S.assert_close(got[b], S.oracle_on_bytes(cache, b, int(L[b]), q[b], codebooks), f"b={b}")
         _say(f"[bandwidth-bound step] b={b} L={int(L[b])} rel-L2 {rel:.2e} max-abs {mx:.2e}")
     assert np.all(np.isfinite(got.astype(np.float32)))
+
+
+# ----------------------------------------------------------------------------- sparse V
+
+@pytest.mark.parametrize("variant", [2, "fused"])
+def test_sparse_v_skips_nothing_on_gaussian_scores(variant, codebooks):
+    """At tau = 1e-6 the benchmark-like inputs (Gaussian keys and queries) leave no V tile
+    below the threshold, so the output is bit-identical to exact attention's."""
+    w, lens = _small_workloads()["c1"]
+    cache, _, _, _, q = S.prefill_and_step(w, lengths=lens)
+    exact = S.gpu_decode(cache, q, variant=variant)
+    cache.v_skip_threshold = 1e-6
+    np.testing.assert_array_equal(S.gpu_decode(cache, q, variant=variant), exact)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("tau", [1e-6, 1e-2])
+@pytest.mark.parametrize("variant", [2, "fused", "step"])
+def test_sparse_v_drops_only_droppable_tokens(tau, variant, codebooks):
+    """Peaked scores (queries x16, G = 4) on a call large enough (>= 4M token-heads) that the
+    splits run 16 iterations: the output with sparse V moves from the exact route's by at
+    most the oracle's bound for what may be dropped (tokens whose weight is below tau for
+    every head of the group; tau widened by 10% for the scores' fp16 rounding), and at
+    tau = 1e-2 it does drop.  (A split's first tile per token set sets its running max and
+    is never skipped, so short splits skip little.)"""
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    from oracle import attention as att
+    from synth import kv_slice
+    B, L = 64, 8200
+    w = S.scaled(get_workload(0), batch=B, num_q_heads=32, num_kv_heads=8)
+    pre = L - (1 if variant == "step" else 0)
+    assert pre * B * 8 >= 4 << 20
+    # every sequence holds the same keys and values (one generated sequence, copied on the GPU)
+    k0 = np.stack([kv_slice(w, 0, "k", 0, h, pre) for h in range(8)])
+    v0 = np.stack([kv_slice(w, 0, "v", 0, h, pre) for h in range(8)])
+    cache = S.make_cache(w, 8224)
+    tq.tq_encode_append(cache, torch.from_numpy(k0).cuda()[None].expand(B, -1, -1, -1).contiguous(),
+                        torch.from_numpy(v0).cuda()[None].expand(B, -1, -1, -1).contiguous())
+    q = (queries(w, 0) * 16).astype(np.float32)
+    kn, vn = S.new_token_rows(w, 0)
+
+    def run(threshold):
+        cache.v_skip_threshold = threshold
+        if variant == "step":
+            cache.set_lengths(np.full(B, pre, dtype=np.int32))   # the step rewrites the same slot
+            return S.gpu_decode_step(cache, kn, vn, q).astype(np.float64)
+        return S.gpu_decode(cache, q, variant=variant).astype(np.float64)
+
+    exact = run(0.0)
+    got = run(tau)
+    moved = 0.0
+    for b in (0, B - 1):
+        k_hat, v_hat = S.oracle_dequant_bytes(cache, b, L, codebooks)
+        _, bound = att.sparse_v_bound(q[b], k_hat, v_hat, L, S.SCALE, 1.1 * tau)
+        diff = np.abs(got[b] - exact[b])
+        slack = np.abs(exact[b]) * 2.0 ** -9 + 1e-5   # the two routes' fp16 output rounding
+        assert np.all(diff <= bound + slack), f"b={b}: {np.max(diff - bound - slack)}"
+        moved = max(moved, float(diff.max()))
+        _say(f"[sparse V {variant} tau={tau}] b={b} max move {diff.max():.2e}, max bound {bound.max():.2e}")
+    if tau >= 1e-2:
+        assert moved > 0.0

@@ -143,3 +143,25 @@ def sparse_v_bound(q, k_hat, v_hat, length, scale: float, tau: float):
             o[h] = w @ vb[g, :L]
             bound[h] = (w * droppable) @ np.abs(vb[g, :L])
     return o, bound
+
+
+def attention_chunk(q, k_hat, v_hat, lengths, scale: float) -> np.ndarray:
+    """Decode attention of a chunk of Tq query positions per sequence (float64).
+
+    SURVEY's next step "Tq > 1 decode attention" (the pages' decode output is
+    [B, Hq, Tq, D], mlxcel PR #369 "Change"; the chunk's own tokens are the last Tq
+    of the cache and are causal among themselves): query position tau of sequence b
+    (0 <= tau < Tq) sits at absolute position L_b - Tq + tau and attends to tokens
+    t <= L_b - Tq + tau, i.e. to the first L_b - Tq + 1 + tau tokens.
+
+    q [B, Hq, Tq, D]; k_hat, v_hat as for `attention`; lengths[b] >= Tq.
+    Returns [B, Hq, Tq, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, Tq, D = q.shape
+    out = np.zeros((B, Hq, Tq, D))
+    for b in range(B):
+        L = int(lengths[b])
+        assert L >= Tq, "the chunk's tokens must be in the cache"
+        for tau in range(Tq):
+            out[b, :, tau] = attention(q[b:b + 1, :, tau], [k_hat[b]], [v_hat[b]], [L - Tq + 1 + tau], scale)[0]
+    return out

@@ -179,3 +179,33 @@ def test_sparse_v_bound_covers_any_dropped_subset():
             drop = droppable & (rng.random(L) < 0.5)
             o_drop = (w * ~drop) @ v[g]
             assert np.all(np.abs(o_drop - o[h]) <= bound[h] + 1e-15)
+
+
+def test_chunk_attention_is_causal_and_reduces_to_single_token():
+    """Tq = 1 is the single-token decode; position tau of a chunk depends on exactly the first
+    L - Tq + 1 + tau tokens (changing a later token leaves it unchanged, changing that token
+    does not); brute force with Python loops on a tiny chunk."""
+    from oracle.attention import attention, attention_chunk, attention_naive
+    rng = np.random.default_rng(11)
+    B, hkv, G, L, D, Tq = 2, 2, 3, 9, 8, 4
+    k = [rng.standard_normal((hkv, L, D)) for _ in range(B)]
+    v = [rng.standard_normal((hkv, L, D)) for _ in range(B)]
+    q = rng.standard_normal((B, hkv * G, Tq, D))
+    lens = [L, L - 2]
+    o = attention_chunk(q, k, v, lens, 0.3)
+    np.testing.assert_allclose(attention_chunk(q[:, :, :1], k, v, lens, 0.3)[:, :, 0],
+                               attention(q[:, :, 0], k, v, lens, 0.3), rtol=0, atol=0)
+    for b in range(B):
+        for tau in range(Tq):
+            n = lens[b] - Tq + 1 + tau
+            ref = attention_naive(q[b:b + 1, :, tau].tolist(), [k[b].tolist()], [v[b].tolist()], [n], 0.3)[0]
+            np.testing.assert_allclose(o[b, :, tau], ref, rtol=1e-12, atol=1e-14)
+            k2 = [x.copy() for x in k]
+            v2 = [x.copy() for x in v]
+            if n < L:
+                k2[b][:, n:] += 5.0
+                v2[b][:, n:] -= 3.0
+                np.testing.assert_allclose(attention_chunk(q, k2, v2, lens, 0.3)[b, :, tau], o[b, :, tau],
+                                           rtol=0, atol=0)
+            v2[b][:, n - 1] += 1.0
+            assert np.all(np.abs(attention_chunk(q, k2, v2, lens, 0.3)[b, :, tau] - o[b, :, tau]) > 0)

@@ -207,6 +207,26 @@ tq_status tq_decode_attention_fused(const tq_cache* cache, const int32_t* seq_le
                                     float scale, uint16_t* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* Decode attention of a chunk of q_len query positions per sequence (speculative
+ * verification, chunked decode): the chunk's tokens are the last q_len of each
+ * sequence, already appended with tq_encode_append, and are causal among
+ * themselves -- position tau (0 <= tau < q_len) attends to the first
+ * seq_lens_host[b] - q_len + 1 + tau tokens.  The pages' decode output is
+ * [B, Hq, Tq, D] (mlxcel PR #369, "Change"); q_len = 1 is
+ * tq_decode_attention_fused.  Each (query head, position) pair is one column of
+ * its KV head's decode, so group * q_len must be <= 16 (TQ_EUNSUPPORTED
+ * otherwise); rotations as in tq_decode_attention_fused.
+ *   seq_lens_host  HOST int32 [B]: lengths including the chunk; each >= q_len.
+ *   q     device [B][num_q_heads][q_len][128], fp32 if q_is_fp32 else fp16 bits.
+ *   out   device fp16 bits [B][num_q_heads][q_len][128], original basis.
+ *   workspace  >= tq_decode_workspace_size(cache, num_q_heads * q_len,
+ *                  seq_lens_host) bytes.
+ * Other errors as for tq_decode_attention.  Always the MFMA kernel. */
+tq_status tq_decode_chunk_fused(const tq_cache* cache, const int32_t* seq_lens_host,
+                                const void* q, int32_t q_is_fp32, int32_t num_q_heads,
+                                int32_t q_len, float scale, uint16_t* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* One whole decode step: append one new token to every sequence and attend to
  * all visible tokens, the new one included -- tq_encode_append (t_new = 1)
  * followed by tq_decode_attention_fused on the grown cache, in two kernels.

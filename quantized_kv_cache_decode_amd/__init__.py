@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     load_library,
     tq_decode_attention,
     tq_decode_attention_fused,
+    tq_decode_chunk_fused,
     tq_decode_step,
     tq_decode_workspace_size,
     tq_encode_append,

@@ -22,7 +22,8 @@ K_RECORD_BYTES = {"turbo3": 48, "turbo4": 64}
 V_TILE_BYTES = {"turbo3": 1536, "turbo4": 2048}
 EXPORTED = (
     "tq_encode_append", "tq_rotate_q", "tq_decode_workspace_size", "tq_decode_attention",
-    "tq_decode_attention_variant", "tq_decode_attention_fused", "tq_decode_step", "tq_inverse_rotate_out",
+    "tq_decode_attention_variant", "tq_decode_attention_fused", "tq_decode_chunk_fused", "tq_decode_step",
+    "tq_inverse_rotate_out",
     "tq_last_error", "tq_version",
 )
 
@@ -65,11 +66,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tq_decode_attention_variant.argtypes = [cp, P, P, I32, F32, P, P, SZ, I32, P]
     lib.tq_decode_attention_fused.argtypes = [cp, P, P, I32, I32, F32, P, P, SZ, P]
     lib.tq_decode_step.argtypes = [cp, P, P, P, P, I32, I32, F32, P, P, SZ, P]
+    lib.tq_decode_chunk_fused.argtypes = [cp, P, P, I32, I32, I32, F32, P, P, SZ, P]
     lib.tq_inverse_rotate_out.argtypes = [cp, P, I32, P, P]
     lib.tq_last_error.restype = ctypes.c_char_p
     lib.tq_version.restype = ctypes.c_char_p
     for name in ("tq_encode_append", "tq_rotate_q", "tq_decode_attention", "tq_decode_attention_variant",
-                 "tq_decode_attention_fused", "tq_decode_step",
+                 "tq_decode_attention_fused", "tq_decode_chunk_fused", "tq_decode_step",
                  "tq_inverse_rotate_out"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
@@ -207,6 +209,17 @@ def tq_decode_attention_fused(cache: Cache, q, scale, out, workspace, seq_lens_h
     _check(load_library().tq_decode_attention_fused(
         cache.desc, p, _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]), float(scale), _ptr(out),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream)))
+
+
+def tq_decode_chunk_fused(cache: Cache, q, scale, out, workspace, seq_lens_host=None, stream=None):
+    """out fp16 [B, Hq, Tq, 128] = causal decode attention of a chunk of Tq query positions
+    q [B, Hq, Tq, 128] (fp16 or fp32, unrotated) over each sequence's visible tokens, the
+    chunk's own Tq tokens last.  Workspace: tq_decode_workspace_size(cache, Hq * Tq)."""
+    import torch
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
+    _check(load_library().tq_decode_chunk_fused(
+        cache.desc, p, _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]), int(q.shape[2]), float(scale),
+        _ptr(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream)))
 
 
 def tq_decode_step(cache: Cache, k_new, v_new, q, scale, out, workspace, seq_lens_host=None, stream=None):

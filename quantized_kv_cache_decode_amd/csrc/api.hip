@@ -234,6 +234,7 @@ tq_status decode_setup(const tq_cache* cache, const int32_t* seq_lens_host, int3
   a.col0 = 0;
   a.split_append = 0;
   a.v_skip_log2 = cache->v_skip_threshold > 0.f ? std::log2(cache->v_skip_threshold) : -INFINITY;
+  a.q_len = 1;
   return TQ_OK;
 }
 
@@ -291,6 +292,34 @@ tq_status tq_decode_attention_fused(const tq_cache* cache, const int32_t* seq_le
   tq_status st = decode_setup(cache, seq_lens_host, num_q_heads, scale, workspace, ws_bytes, a);
   if (st != TQ_OK) return st;
   if (!q || !out) return fail(TQ_EINVAL, "q / out is NULL");
+  a.q_in = q;
+  a.q_fp32 = q_is_fp32 != 0;
+  a.q_rotate = cache->k_format != TQ_FMT_F16;
+  a.out = out;
+  return launch_decode_and_merge(cache, seq_lens_host, a, 0, static_cast<hipStream_t>(stream));
+}
+
+tq_status tq_decode_chunk_fused(const tq_cache* cache, const int32_t* seq_lens_host, const void* q,
+                                int32_t q_is_fp32, int32_t num_q_heads, int32_t q_len, float scale, uint16_t* out,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  tq_status st = check_cache(cache);
+  if (st != TQ_OK) return st;
+  if (q_len < 1) return fail(TQ_EINVAL, "q_len %d must be positive", q_len);
+  if ((st = check_heads(cache, num_q_heads)) != TQ_OK) return st;
+  const int group = num_q_heads / cache->num_kv_heads;
+  if ((long long)group * q_len > tq::kMaxGroup)
+    return fail(TQ_EUNSUPPORTED, "group size %d x q_len %d exceeds %d columns", group, q_len, tq::kMaxGroup);
+  if ((st = check_lengths(cache, seq_lens_host, 0)) != TQ_OK) return st;
+  for (int b = 0; b < cache->batch; ++b)
+    if (seq_lens_host[b] < q_len)
+      return fail(TQ_EINVAL, "sequence %d holds %d tokens, fewer than the chunk's %d", b, seq_lens_host[b], q_len);
+  // every (head, position) pair is a column of its KV head: q [B][Hq][q_len][128] is
+  // [B][Hkv][group * q_len][128], and so is out
+  tq::DecodeArgs a;
+  if ((st = decode_setup(cache, seq_lens_host, num_q_heads * q_len, scale, workspace, ws_bytes, a)) != TQ_OK)
+    return st;
+  if (!q || !out) return fail(TQ_EINVAL, "q / out is NULL");
+  a.q_len = q_len;
   a.q_in = q;
   a.q_fp32 = q_is_fp32 != 0;
   a.q_rotate = cache->k_format != TQ_FMT_F16;

@@ -400,6 +400,12 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   const int sig = g / P, part = g % P;       // score-MFMA set and part of this lane
   const int sn = n / Gp, hn = n % Gp;        // this lane's column: set and head
   const size_t row = size_t(b) * a.hkv + h;
+  // Chunk of q_len query positions (column hn is query position hn % q_len of its
+  // head): the sequence's last q_len tokens are causal among themselves, so column
+  // hn sees tokens < L - (q_len - 1 - hn % q_len) (in whichever splits they fall);
+  // every column sees the tokens before t_all.
+  const int t_all = min(t1, L - (a.q_len - 1));
+  const int t_col = min(t1, L - (a.q_len - 1 - hn % a.q_len));
   const uint8_t* kbase = a.k_data + row * size_t(a.cap) * REC + part * (REC / P);
   const uint8_t* vbase = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT) + lane * (VW * 4);
   const uint16_t* knorm = KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap);
@@ -587,7 +593,7 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float v = S[rb][j] * z[4 * rb + j];
-        if (TAIL && tn + 16 * rb + 4 * g + j >= t1) v = -INFINITY;
+        if (TAIL && tn + 16 * rb + 4 * g + j >= t_col) v = -INFINITY;
         z[4 * rb + j] = v;
       }
     }
@@ -657,8 +663,8 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   };
 
   int base = t0;
-  for (; base + TOK <= t1; base += TOK) step(base, std::false_type{});
-  if (base < t1) step(base, std::true_type{});
+  for (; base + TOK <= t_all; base += TOK) step(base, std::false_type{});
+  for (; base < t1; base += TOK) step(base, std::true_type{});  // at most two: t1 - t_all < 16 <= TOK
 
   // ---- finish: sum l over the column's 4 lanes, merge the NS sets of each head
   float l_tot = xsum4(l_run);

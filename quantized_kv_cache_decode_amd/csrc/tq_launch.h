@@ -76,6 +76,8 @@ struct DecodeArgs {
   int q_fp32;               // q_in is fp32 (else fp16 bits)
   int q_rotate;             // q_in goes through H(s_K * q)/sqrt(128) in-kernel (else it is in K's basis)
   float v_skip_log2;        // sparse V: log2 of the weight threshold, -inf when off
+  int q_len;                // query positions per head (>= 1): a causal chunk of the last q_len tokens;
+                            // `group` then counts (head, position) columns, head-major
   const float* k_signs;
   const float* v_signs;
   float* part_o;            // [B*Hkv*slots][group][128]   unnormalised sum_t 2^(z_t - m) v_t

@@ -414,3 +414,44 @@ def test_sparse_v_drops_only_droppable_tokens(tau, variant, codebooks):
         _say(f"[sparse V {variant} tau={tau}] b={b} max move {diff.max():.2e}, max bound {bound.max():.2e}")
     if tau >= 1e-2:
         assert moved > 0.0
+
+
+# ----------------------------------------------------------------------------- chunk (Tq > 1)
+
+def _gpu_chunk(cache, q_np):
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    q = torch.from_numpy(np.ascontiguousarray(q_np)).cuda()
+    B, Hq, Tq, _ = q.shape
+    out = torch.empty((B, Hq, Tq, 128), dtype=torch.float16, device="cuda")
+    ws = torch.zeros(tq.tq_decode_workspace_size(cache, Hq * Tq), dtype=torch.uint8, device="cuda")
+    tq.tq_decode_chunk_fused(cache, q, S.SCALE, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("group,q_len,k_format,v_format", [
+    (2, 3, "turbo3", "turbo3"), (4, 4, "turbo4", "turbo4"), (7, 2, "f16", "turbo4"), (1, 16, "turbo3", "turbo4"),
+    (8, 2, "turbo3", "turbo3")])
+def test_chunk_decode_parity(group, q_len, k_format, v_format, codebooks):
+    """Causal decode of a chunk of q_len positions per sequence against the oracle, with a
+    sequence exactly q_len long, one whose chunk straddles a split boundary (129 tokens,
+    128-token splits), a tile-aligned and a ragged one."""
+    from oracle import attention as att
+    w = S.scaled(get_workload(0), batch=4, num_q_heads=2 * group, num_kv_heads=2, k_format=k_format,
+                 v_format=v_format)
+    lens = np.array([q_len, 129, 256, 1000])
+    cache, _, _, L, _ = S.prefill_and_step(w, lengths=lens)
+    q = np.stack([queries(w, 0, step=t) for t in range(q_len)], axis=2)     # [B, Hq, Tq, 128]
+    got = _gpu_chunk(cache, q)
+    for b in range(4):
+        k_hat, v_hat = S.oracle_dequant_bytes(cache, b, int(L[b]), codebooks)
+        ref = att.attention_chunk(q[b:b + 1], [k_hat], [v_hat], [int(L[b])], S.SCALE)[0]
+        S.assert_close(got[b], ref, f"G={group} q_len={q_len} b={b} L={int(L[b])}")
+
+
+def test_chunk_of_one_is_the_fused_decode():
+    w, lens = _small_workloads()["c1"]
+    cache, _, _, _, q = S.prefill_and_step(w, lengths=lens)
+    np.testing.assert_array_equal(_gpu_chunk(cache, q[:, :, None])[:, :, 0], S.gpu_decode(cache, q, "fused"))

@@ -182,3 +182,31 @@ def test_no_kernel_spills_to_scratch():
     assert lines, "empty resource report"
     spills = [l for l in lines if l[-1] != "scratch=0"]
     assert not spills, spills
+
+
+def test_chunk_decode_checks(lib):
+    """tq_decode_chunk_fused: q_len >= 1, group * q_len <= 16 columns, every sequence holds the
+    chunk, and the workspace is sized for group * q_len columns."""
+    d = _desc()                       # 2 KV heads
+    q = ctypes.c_void_p(0x20000)
+    a, p = _lens(40, 9)
+    big = 10 ** 9
+
+    def call(heads, q_len, ws=big):
+        return lib.tq_decode_chunk_fused(ctypes.byref(d), p, q, 0, heads, q_len, ctypes.c_float(0.1), q, q, ws, None)
+
+    assert call(4, 0) == binding.TQ_EINVAL
+    assert call(4, 9) == binding.TQ_EUNSUPPORTED and "q_len" in _err(lib)     # group 2 x 9 > 16
+    assert call(4, 10) == binding.TQ_EUNSUPPORTED
+    assert call(2, 10) == binding.TQ_EINVAL and "fewer" in _err(lib)          # sequence 1 holds 9 < 10
+    n = lib.tq_decode_workspace_size(ctypes.byref(d), 4 * 8, p)
+    assert n > 0
+    assert call(4, 8, n - 4) == binding.TQ_EWORKSPACE
+
+
+def test_sparse_v_threshold_range(lib):
+    q = ctypes.c_void_p(0x20000)
+    for tau, status in ((-0.5, binding.TQ_EINVAL), (1.5, binding.TQ_EINVAL), (float("nan"), binding.TQ_EINVAL)):
+        d = _desc(v_skip_threshold=tau)
+        assert lib.tq_rotate_q(ctypes.byref(d), q, 0, 4, q, None) == status
+        assert "v_skip_threshold" in _err(lib)

@@ -8,7 +8,11 @@ all visible tokens, LSE merge, inverse-rotate the output.  --path picks the call
             (default);
   fused     tq_encode_append -> tq_decode_attention_fused (three kernels);
   separate  tq_encode_append -> tq_rotate_q -> tq_decode_attention ->
-            tq_inverse_rotate_out (five kernels).
+            tq_inverse_rotate_out (five kernels);
+  chunk     tq_encode_append of the last --q-len tokens -> tq_decode_chunk_fused
+            (--q-len query positions per head, causal within the chunk).
+--v-skip-threshold turns on sparse V; --q-scale multiplies the queries (peaked
+weights, where sparse V has tiles to skip).
 Inputs are seeded synthetic ones of the Qwen2.5-7B-shaped layer (B=1, Hq=28,
 Hkv=4, head dim 128, 8192 visible tokens, turbo3 K and V) unless --workload says
 otherwise.  The cache is replicated into distinct HBM copies (>= 1 GiB in all)
@@ -49,7 +53,7 @@ def parse():
     p.add_argument("--steps", type=int, default=3200)
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--workload", type=int, default=1, help="workload index (0..4); default the 8K Qwen2.5-7B layer")
-    p.add_argument("--path", choices=("step", "fused", "separate"), default="step",
+    p.add_argument("--path", choices=("step", "fused", "separate", "chunk"), default="step",
                    help="calls per step (see the module docstring)")
     p.add_argument("--variant", type=int, default=0,
                    help="decode kernel variant of --path separate (0 default = MFMA, 1 VALU reference)")
@@ -59,6 +63,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--v-skip-threshold", type=float, default=0.0,
                    help="sparse-V weight threshold of the decode calls (0 = exact attention)")
+    p.add_argument("--q-len", type=int, default=4,
+                   help="query positions per sequence of --path chunk (a causal chunk of the last tokens)")
     p.add_argument("--q-scale", type=float, default=1.0,
                    help="multiply the synthetic queries (e.g. 16 for peaked attention weights)")
     return p.parse_args()
@@ -176,7 +182,7 @@ def main():
     import torch
 
     import quantized_kv_cache_decode_amd as tq
-    from synth import get_workload, new_token_kv
+    from synth import get_workload, new_token_kv, queries
     from tests import support as S
     tq.load_library()
     torch.cuda.set_device(0)
@@ -184,7 +190,7 @@ def main():
     seed = 0
 
     # ---- setup (not timed): prefill L-1 tokens, append the step's token once
-    master, _, _, L, q_np = S.prefill_and_step(w, seed)
+    master, k_list, v_list, L, q_np = S.prefill_and_step(w, seed)
     master.v_skip_threshold = args.v_skip_threshold   # (the copies below inherit it)
     pre = (L - 1).astype(np.int32)
     per_copy = cache_bytes(master)
@@ -203,6 +209,18 @@ def main():
     ws = torch.zeros(max(tq.tq_decode_workspace_size(master, Hq, L), tq.tq_decode_workspace_size(master, Hq, pre)),
                      dtype=torch.uint8, device="cuda")
     scale = 1.0 / math.sqrt(128.0)
+    if args.path == "chunk":
+        # the chunk: the last q_len tokens of every sequence, re-appended each step, and
+        # q_len query positions per head attending causally
+        Tq = args.q_len
+        chunk_pre = (L - Tq).astype(np.int32)
+        kc = S.padded_tensor([k[:, int(L[b]) - Tq:int(L[b])] for b, k in enumerate(k_list)], Tq)
+        vc = S.padded_tensor([v[:, int(L[b]) - Tq:int(L[b])] for b, v in enumerate(v_list)], Tq)
+        qc_np = np.stack([queries(w, seed, step=t) for t in range(Tq)], axis=2)
+        qc = torch.from_numpy(np.ascontiguousarray((qc_np.astype(np.float32) * args.q_scale).astype(qc_np.dtype))).cuda()
+        out_c = torch.empty((B, Hq, Tq, 128), dtype=torch.float16, device="cuda")
+        ws = torch.zeros(tq.tq_decode_workspace_size(master, Hq * Tq, L), dtype=torch.uint8, device="cuda")
+    del k_list, v_list
     per_graph = n_copies
     # a plain 512 MiB device copy (setup, untimed): its FETCH_SIZE / WRITE_SIZE counters
     # calibrate the HBM traffic figures read for the decode kernel in the same profile
@@ -218,6 +236,8 @@ def main():
         """The timed call: append + decode for the step path, decode alone otherwise."""
         if args.path == "step":
             tq.tq_decode_step(c, kn, vn, q, scale, out, ws, seq_lens_host=pre)
+        elif args.path == "chunk":
+            tq.tq_decode_chunk_fused(c, qc, scale, out_c, ws, seq_lens_host=L)
         elif sep:
             tq.tq_decode_attention(c, q_rot, scale, out_rot, ws, seq_lens_host=L, variant=args.variant)
         else:
@@ -227,7 +247,9 @@ def main():
         # Every step writes the same token into slot L-1 of its cache copy and attends over
         # L tokens, so replays are idempotent and the copies keep their length.
         c = caches[i % n_copies]
-        if args.path != "step":
+        if args.path == "chunk":
+            tq.tq_encode_append(c, kc, vc, seq_lens_host=chunk_pre)
+        elif args.path != "step":
             tq.tq_encode_append(c, kn, vn, seq_lens_host=pre)
         if sep:
             tq.tq_rotate_q(c, q, q_rot)
@@ -299,7 +321,7 @@ def main():
             # counters are recorded for the default route (tq_decode_step, MFMA kernel) only
             "traffic": recorded_traffic(w.name) if args.path == "step" else None,
             "kernel": {"step": "tq_decode_step", "fused": "tq_decode_attention_fused",
-                       "separate": "tq_decode_attention"}[args.path]
+                       "separate": "tq_decode_attention", "chunk": "tq_decode_chunk_fused"}[args.path]
             + (" (decode_ref_kernel" if args.variant == 1 else " (decode_mfma_kernel")
             + " + combine_kernel)",
             "call_us": dec_ms * 1e3,
@@ -315,7 +337,8 @@ def main():
                    "context_total": int(L.sum()), "k_format": w.k_format, "v_format": w.v_format,
                    "cache_copies": n_copies, "graph": use_graph,
                    "path": args.path, "variant": args.variant,
-                   "v_skip_threshold": args.v_skip_threshold, "q_scale": args.q_scale},
+                   "v_skip_threshold": args.v_skip_threshold, "q_scale": args.q_scale,
+                   "q_len": args.q_len if args.path == "chunk" else 1},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

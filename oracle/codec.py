@@ -48,7 +48,7 @@ from .lloyd_max import decision_boundaries
 BITS = {"turbo3": 3, "turbo4": 4}
 K_RECORD_BYTES = {"turbo3": 48, "turbo4": 64}
 V_TILE_TOKENS = 32
-V_CHUNK_BYTES = {"turbo3": 24, "turbo4": 32}
+V_CHUNK_BYTES = {"turbo3": 24, "turbo4": 32, "f16": 128}
 V_TILE_BYTES = {f: 64 * b for f, b in V_CHUNK_BYTES.items()}
 FP16_MAX = 65504.0
 
@@ -238,9 +238,9 @@ def v_tile_slot(g: int, i: int) -> int:
 
 
 def _v_chunk_elements(codes_tile):
-    """codes_tile [..., 32, 128] -> chunk elements [..., 64 chunks, 64 elements]."""
+    """codes_tile [..., 32, 128] -> chunk elements [..., 64 chunks, 64 elements] (same dtype)."""
     c = np.asarray(codes_tile)
-    out = np.zeros(c.shape[:-2] + (64, 64), dtype=np.uint8)
+    out = np.zeros(c.shape[:-2] + (64, 64), dtype=c.dtype)
     for g in range(4):
         for n in range(16):
             for nb in range(8):
@@ -251,7 +251,7 @@ def _v_chunk_elements(codes_tile):
 
 def _v_chunk_elements_inverse(elems):
     e = np.asarray(elems)
-    out = np.zeros(e.shape[:-2] + (32, 128), dtype=np.uint8)
+    out = np.zeros(e.shape[:-2] + (32, 128), dtype=e.dtype)
     for g in range(4):
         for n in range(16):
             for nb in range(8):
@@ -261,7 +261,10 @@ def _v_chunk_elements_inverse(elems):
 
 
 def pack_v_tiles(codes, fmt: str) -> np.ndarray:
-    """Token-tiled V: codes [T, 128] (T a multiple of 32) -> bytes [T/32, 1536 | 2048]."""
+    """Token-tiled V: codes [T, 128] (T a multiple of 32) -> bytes [T/32, 1536 | 2048].
+
+    fmt "f16": the uncompressed comparison layout -- the same chunk element order
+    with fp16 values for codes (128-byte chunks, 8192-byte tiles)."""
     c = np.asarray(codes)
     if c.shape[-2] % V_TILE_TOKENS:
         raise ValueError("token count must be a multiple of 32")
@@ -271,6 +274,8 @@ def pack_v_tiles(codes, fmt: str) -> np.ndarray:
         chunk = np.concatenate([pack_sub3(el[..., :32]), pack_sub3(el[..., 32:])], axis=-1)
     elif fmt == "turbo4":
         chunk = np.concatenate([pack_oct4(el[..., 8 * nb:8 * nb + 8]) for nb in range(8)], axis=-1)
+    elif fmt == "f16":
+        chunk = np.ascontiguousarray(el).view(np.uint8)                # 64 little-endian fp16 values
     else:
         raise ValueError(fmt)
     return chunk.reshape(chunk.shape[:-2] + (-1,))
@@ -283,6 +288,8 @@ def unpack_v_tiles(tiles, fmt: str) -> np.ndarray:
     ch = t.reshape(t.shape[:-1] + (64, cb))
     if fmt == "turbo3":
         el = np.concatenate([unpack_sub3(ch[..., :12]), unpack_sub3(ch[..., 12:])], axis=-1)
+    elif fmt == "f16":
+        el = np.ascontiguousarray(ch).view(np.float16)                  # [..., 64, 64]
     else:
         el = np.concatenate([unpack_oct4(ch[..., 4 * nb:4 * nb + 4]) for nb in range(8)], axis=-1)
     codes = _v_chunk_elements_inverse(el)                            # [..., nt, 32, 128]

@@ -35,6 +35,12 @@ def encode_sequence(k16, v16, k_format, v_format, k_signs, v_signs, codebooks, c
         norms[:, :L] = kn
         out["k_codes"], out["k_norms"] = codes, norms
         out["k_rec"] = codec.pack_k_record(codes, k_format)
+    if v_format == "f16":   # the uncompressed comparison cache: values stored as they come
+        vf = np.zeros((hkv, cap, 128), dtype=np.float16)
+        vf[:, :L] = v16
+        out["v_f16"] = vf
+        out["v_tiles"] = codec.pack_v_tiles(vf, "f16")
+        return out
     vc, vn = codec.encode(v16, v_signs, codebooks[v_format])
     codes = np.zeros((hkv, cap, 128), dtype=np.uint8)
     codes[:, :L] = vc
@@ -51,6 +57,8 @@ def dequant_sequence(enc, k_format, v_format, k_signs, v_signs, codebooks, lengt
         k = enc["k_f16"][:, :length].astype(np.float64)
     else:
         k = codec.dequant(enc["k_codes"][:, :length], enc["k_norms"][:, :length], codebooks[k_format], k_signs)
+    if v_format == "f16":
+        return k, enc["v_f16"][:, :length].astype(np.float64)
     v = codec.dequant(enc["v_codes"][:, :length], enc["v_norms"][:, :length], codebooks[v_format], v_signs)
     return k, v
 
@@ -61,7 +69,8 @@ def decode_sequence(q, k_hat, v_hat, length, scale=SCALE):
 
 
 def codes_from_library_layout(k_rec, v_tiles, k_format, v_format):
-    """Unpack the library's byte layout back to codes [Hkv, cap, 128] (K may be None for f16)."""
+    """Unpack the library's byte layout back to codes [Hkv, cap, 128] (K may be None for f16;
+    for f16 V the values come back, fp16)."""
     kc = None if k_rec is None else codec.unpack_k_record(k_rec, k_format)
     vc = codec.unpack_v_tiles(v_tiles, v_format)
     return kc, vc

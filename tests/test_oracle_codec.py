@@ -246,3 +246,35 @@ def test_pack_round_trip_every_value_every_position(fmt, k):
     np.testing.assert_array_equal(codec.unpack_v_tiles(codec.pack_v_tiles(tiles, fmt), fmt), tiles)
     assert codec.pack_k_record(codes[:1], fmt).shape[-1] == codec.K_RECORD_BYTES[fmt]
     assert codec.pack_v_tiles(codes[:32], fmt).shape[-1] == codec.V_TILE_BYTES[fmt]
+
+
+def test_f16_v_tile_hand_worked_bytes_and_round_trip():
+    """The uncompressed comparison layout: token slot 21 = (g=1, i=5), dim 42 = (n=5, nb=2)
+    -> chunk 21, element 8*2 + 5 = 21 -> bytes 21*128 + 2*21 = 2730..2731, little-endian fp16.
+    Every value at every position round-trips bit for bit (NaN payloads and -0 included)."""
+    v = np.zeros((32, 128), dtype=np.float16)
+    v[21, 42] = np.float16(-1.5)                     # 0xBE00
+    t = codec.pack_v_tiles(v, "f16")[0]
+    assert t.shape == (8192,) and codec.V_TILE_BYTES["f16"] == 8192
+    nz = np.nonzero(t)[0]
+    assert list(nz) == [2731] and t[2731] == 0xBE and t[2730] == 0x00
+    rng = np.random.default_rng(9)
+    bits = rng.integers(0, 1 << 16, (2, 64, 128), dtype=np.uint16)
+    vals = bits.view(np.float16)
+    back = codec.unpack_v_tiles(codec.pack_v_tiles(vals, "f16"), "f16")
+    np.testing.assert_array_equal(back.view(np.uint16), bits)
+
+
+def test_reference_f16_cache_dequantises_to_its_values(codebooks):
+    """fp16 K and V: the reference keeps both as given, and the bytes unpack to them."""
+    from oracle import reference
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((2, 40, 128)).astype(np.float16)
+    v = rng.standard_normal((2, 40, 128)).astype(np.float16)
+    enc = reference.encode_sequence(k, v, "f16", "f16", None, None, codebooks)
+    kh, vh = reference.dequant_sequence(enc, "f16", "f16", None, None, codebooks, 40)
+    np.testing.assert_array_equal(kh, k.astype(np.float64))
+    np.testing.assert_array_equal(vh, v.astype(np.float64))
+    _, vv = reference.codes_from_library_layout(None, enc["v_tiles"], "f16", "f16")
+    np.testing.assert_array_equal(vv[:, :40], v)
+    assert np.all(vv[:, 40:] == 0)

@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--v-skip-threshold", type=float, default=0.0,
                    help="sparse-V weight threshold of the decode calls (0 = exact attention)")
+    p.add_argument("--formats", default=None,
+                   help="K/V formats instead of the workload's, e.g. f16/f16 (the uncompressed comparison cache)")
     p.add_argument("--q-len", type=int, default=4,
                    help="query positions per sequence of --path chunk (a causal chunk of the last tokens)")
     p.add_argument("--q-scale", type=float, default=1.0,
@@ -118,7 +120,8 @@ def clone_cache(master):
     c._desc = tq.binding.tq_cache(
         master.batch, master.num_kv_heads, 128, master.capacity, master._desc.k_format, master._desc.v_format,
         c.k_data.data_ptr(), 0 if c.k_norms is None else c.k_norms.data_ptr(), c.v_data.data_ptr(),
-        c.v_norms.data_ptr(), c.seq_lens.data_ptr(), master.k_signs.data_ptr(), master.v_signs.data_ptr(),
+        0 if c.v_norms is None else c.v_norms.data_ptr(), c.seq_lens.data_ptr(), master.k_signs.data_ptr(),
+        master.v_signs.data_ptr(),
         master.k_codebook.data_ptr(), master.v_codebook.data_ptr(), master._desc.v_skip_threshold)
     return c
 
@@ -187,6 +190,10 @@ def main():
     tq.load_library()
     torch.cuda.set_device(0)
     w = get_workload(args.workload)
+    if args.formats:
+        from dataclasses import replace
+        kf, vf = args.formats.split("/")
+        w = replace(w, k_format=kf, v_format=vf)
     seed = 0
 
     # ---- setup (not timed): prefill L-1 tokens, append the step's token once
@@ -319,7 +326,7 @@ def main():
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
             # counters are recorded for the default route (tq_decode_step, MFMA kernel) only
-            "traffic": recorded_traffic(w.name) if args.path == "step" else None,
+            "traffic": recorded_traffic(w.name) if args.path == "step" and not args.formats else None,
             "kernel": {"step": "tq_decode_step", "fused": "tq_decode_attention_fused",
                        "separate": "tq_decode_attention", "chunk": "tq_decode_chunk_fused"}[args.path]
             + (" (decode_ref_kernel" if args.variant == 1 else " (decode_mfma_kernel")

@@ -19,7 +19,7 @@ TABLE_PATH = os.path.join(HERE, "tables", "codebooks.json")
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_ECAPACITY, TQ_EWORKSPACE, TQ_EHIP = range(6)
 TQ_FMT = {"f16": 0, "turbo3": 3, "turbo4": 4}
 K_RECORD_BYTES = {"turbo3": 48, "turbo4": 64}
-V_TILE_BYTES = {"turbo3": 1536, "turbo4": 2048}
+V_TILE_BYTES = {"turbo3": 1536, "turbo4": 2048, "f16": 8192}
 EXPORTED = (
     "tq_encode_append", "tq_rotate_q", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_decode_attention_variant", "tq_decode_attention_fused", "tq_decode_chunk_fused", "tq_decode_step",
@@ -108,7 +108,8 @@ def _host_i32(lengths):
 class Cache:
     """Device buffers of one layer's KV cache (torch tensors) and their C descriptor.
 
-    k_format: "turbo3" | "turbo4" | "f16"; v_format: "turbo3" | "turbo4".
+    k_format: "turbo3" | "turbo4" | "f16"; v_format: "turbo3" | "turbo4", or "f16" with
+    k_format "f16" (the uncompressed comparison cache).
     `lengths` is the host copy of the visible length per sequence; it is advanced
     by tq_encode_append together with the device copy."""
 
@@ -128,18 +129,19 @@ class Cache:
             self.k_norms = torch.zeros(slots, dtype=torch.int16, device=dev)
         self.v_data = torch.zeros((batch, num_kv_heads, capacity // 32, V_TILE_BYTES[v_format]),
                                   dtype=torch.uint8, device=dev)
-        self.v_norms = torch.zeros(slots, dtype=torch.int16, device=dev)
+        self.v_norms = None if v_format == "f16" else torch.zeros(slots, dtype=torch.int16, device=dev)
         self.seq_lens = torch.zeros(batch, dtype=torch.int32, device=dev)
         self.k_signs = torch.as_tensor(np.asarray(k_signs, dtype=np.float32)).to(dev)
         self.v_signs = torch.as_tensor(np.asarray(v_signs, dtype=np.float32)).to(dev)
         cbk = codebook_bits(k_format) if k_format != "f16" else np.zeros(16, np.uint16)
         self.k_codebook = torch.as_tensor(cbk.view(np.int16).copy()).to(dev)
-        self.v_codebook = torch.as_tensor(codebook_bits(v_format).view(np.int16).copy()).to(dev)
+        cbv = codebook_bits(v_format) if v_format != "f16" else np.zeros(16, np.uint16)
+        self.v_codebook = torch.as_tensor(cbv.view(np.int16).copy()).to(dev)
         self.lengths = np.zeros(batch, dtype=np.int32)
         self._desc = tq_cache(
             batch, num_kv_heads, 128, capacity, TQ_FMT[k_format], TQ_FMT[v_format],
             self.k_data.data_ptr(), 0 if self.k_norms is None else self.k_norms.data_ptr(),
-            self.v_data.data_ptr(), self.v_norms.data_ptr(), self.seq_lens.data_ptr(),
+            self.v_data.data_ptr(), 0 if self.v_norms is None else self.v_norms.data_ptr(), self.seq_lens.data_ptr(),
             self.k_signs.data_ptr(), self.v_signs.data_ptr(), self.k_codebook.data_ptr(),
             self.v_codebook.data_ptr(), 0.0)
 

@@ -35,11 +35,13 @@ tq_status check_cache(const tq_cache* c) {
   if (c->head_dim != 128) return fail(TQ_EUNSUPPORTED, "head_dim %d: only 128 is supported", c->head_dim);
   if (c->batch <= 0 || c->num_kv_heads <= 0) return fail(TQ_EINVAL, "batch and num_kv_heads must be positive");
   if (c->capacity <= 0 || c->capacity % 32) return fail(TQ_EINVAL, "capacity %d must be a positive multiple of 32", c->capacity);
-  if (!is_turbo(c->v_format)) return fail(TQ_EUNSUPPORTED, "v_format %d: must be TURBO3 or TURBO4", c->v_format);
   if (!is_turbo(c->k_format) && c->k_format != TQ_FMT_F16)
     return fail(TQ_EUNSUPPORTED, "k_format %d: must be F16, TURBO3 or TURBO4", c->k_format);
-  if (!c->k_data || !c->v_data || !c->v_norms || !c->seq_lens || !c->v_signs || !c->v_codebook)
-    return fail(TQ_EINVAL, "NULL cache pointer");
+  if (!is_turbo(c->v_format) && !(c->v_format == TQ_FMT_F16 && c->k_format == TQ_FMT_F16))
+    return fail(TQ_EUNSUPPORTED, "v_format %d: must be TURBO3 or TURBO4 (F16 only with F16 K)", c->v_format);
+  if (!c->k_data || !c->v_data || !c->seq_lens) return fail(TQ_EINVAL, "NULL cache pointer");
+  if (is_turbo(c->v_format) && (!c->v_norms || !c->v_signs || !c->v_codebook))
+    return fail(TQ_EINVAL, "NULL V norm/sign/codebook pointer for a quantised V format");
   if (is_turbo(c->k_format) && (!c->k_norms || !c->k_signs || !c->k_codebook))
     return fail(TQ_EINVAL, "NULL K norm/sign/codebook pointer for a quantised K format");
   if (!(c->v_skip_threshold >= 0.f && c->v_skip_threshold <= 1.f))
@@ -225,10 +227,9 @@ tq_status decode_setup(const tq_cache* cache, const int32_t* seq_lens_host, int3
   a.v_norms = cache->v_norms;
   a.k_cb = cache->k_codebook;
   a.v_cb = cache->v_codebook;
-  // the decode kernel reads the K signs unconditionally (no branch around a load);
-  // F16 K has none, so it reads V's, which it then ignores
-  a.k_signs = cache->k_signs ? cache->k_signs : cache->v_signs;
-  a.v_signs = cache->v_signs;
+  a.k_signs = cache->k_signs;  // read only for a quantised K format
+  a.v_signs = cache->v_signs;  // read only for a quantised V format
+  a.v_rotated = cache->v_format != TQ_FMT_F16;
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + partial_floats(cache, num_q_heads, plan) * 128;
   a.col0 = 0;
@@ -275,6 +276,8 @@ tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_
   if (st != TQ_OK) return st;
   if (!q_rot || !out_rot) return fail(TQ_EINVAL, "q_rot / out_rot is NULL");
   if (variant < 0 || variant > 2) return fail(TQ_EINVAL, "unknown decode variant %d", variant);
+  if (variant == 1 && cache->v_format == TQ_FMT_F16)
+    return fail(TQ_EUNSUPPORTED, "the VALU reference variant reads quantised V only");
   a.q_rot = q_rot;  // (the reference kernel reads it; the MFMA kernel stages it as fp32 q, unrotated)
   a.q_in = q_rot;
   a.q_fp32 = 1;
@@ -373,8 +376,8 @@ tq_status tq_inverse_rotate_out(const tq_cache* cache, const float* out_rot, int
   if (st != TQ_OK) return st;
   if ((st = check_heads(cache, num_q_heads)) != TQ_OK) return st;
   if (!out_rot || !out) return fail(TQ_EINVAL, "out_rot / out is NULL");
-  return hip_status(tq::launch_inverse_rotate(out_rot, cache->v_signs, out, cache->batch * num_q_heads,
-                                              static_cast<hipStream_t>(stream)),
+  return hip_status(tq::launch_inverse_rotate(out_rot, cache->v_format != TQ_FMT_F16, cache->v_signs, out,
+                                              cache->batch * num_q_heads, static_cast<hipStream_t>(stream)),
                     "inverse_rotate launch");
 }
 

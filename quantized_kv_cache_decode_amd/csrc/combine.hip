@@ -154,7 +154,8 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens)
   const size_t row = size_t(b) * a.hkv * G + hq;
   if (INVERSE) {
     uint32_t w[4];
-    rotate_row_inverse_f16(v, a.v_signs, j, w);  // every row of 16 lanes, the same bits
+    if (a.v_rotated) rotate_row_inverse_f16(v, a.v_signs, j, w);  // every row of 16 lanes, the same bits
+    else round_row_f16(v, w);                                      // fp16 V: already the original basis
     if (sg == 0) *reinterpret_cast<uint4*>(a.out + row * kDim + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
   } else if (sg == 0) {
     float4* dst = reinterpret_cast<float4*>(a.out_rot + row * kDim + 8 * j);

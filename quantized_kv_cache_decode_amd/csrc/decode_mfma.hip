@@ -190,13 +190,21 @@ template <int KFMT, int VFMT>
 __device__ __forceinline__ void append_v_partial(const DecodeArgs& a, size_t row, int L, int lane) {
   const int j = lane & 15;
   if (lane >= 16) return;  // one 16-lane group
-  VRowInputs<VFMT> in;
-  load_v_inputs<VFMT>(a.app, row, L, a.app.v_new + row * kDim, j, in);
-  uint8_t code[8];
-  const float nv = half_bits_to_float(append_v_row<VFMT>(a.app, row, L, in, j, code));
   float x[8];
+  if constexpr (VFMT == kFmtF16) {  // stored as it comes; the partial is the row itself
+    const uint4 v = *reinterpret_cast<const uint4*>(a.app.v_new + row * kDim + 8 * j);
+    store_f16_v_row(a.app, row, L, v, j);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = nv * codebook_at<VFMT>(in.row.tab, code[e]);
+    for (int e = 0; e < 8; ++e) x[e] = half_bits_to_float(uint16_t(w[e >> 1] >> (16 * (e & 1))));
+  } else {
+    VRowInputs<VFMT> in;
+    load_v_inputs<VFMT>(a.app, row, L, a.app.v_new + row * kDim, j, in);
+    uint8_t code[8];
+    const float nv = half_bits_to_float(append_v_row<VFMT>(a.app, row, L, in, j, code));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = nv * codebook_at<VFMT>(in.row.tab, code[e]);
+  }
   const size_t p0 = partial_index(a, row, a.plan.max_splits, 0);
   for (int g = 0; g < a.group; ++g) {
     float4* o = reinterpret_cast<float4*>(a.part_o + (p0 + g) * kDim + 8 * j);
@@ -278,6 +286,7 @@ struct QRaw {
   float4 s0, s1;  // this lane's K sign flips (elements 8j..8j+7)
 };
 
+template <bool SIGNS>
 __device__ __forceinline__ void q_request(const DecodeArgs& a, size_t row, int lane, QRaw& q) {
   const int G = a.group, j = lane & 15, r0 = lane >> 4;
   const bool f32 = a.q_fp32 != 0;
@@ -289,8 +298,12 @@ __device__ __forceinline__ void q_request(const DecodeArgs& a, size_t row, int l
     q.lo[k] = *reinterpret_cast<const uint4*>(p);
     q.hi[k] = *reinterpret_cast<const uint4*>(p + (f32 ? 16 : 0));
   }
-  q.s0 = reinterpret_cast<const float4*>(a.k_signs + 8 * j)[0];  // read even when unused: no branch
-  q.s1 = reinterpret_cast<const float4*>(a.k_signs + 8 * j)[1];
+  if constexpr (SIGNS) {  // K's sign flips (a quantised K format): q rotates into its basis
+    q.s0 = reinterpret_cast<const float4*>(a.k_signs + 8 * j)[0];
+    q.s1 = reinterpret_cast<const float4*>(a.k_signs + 8 * j)[1];
+  } else {
+    q.s0 = q.s1 = make_float4(1.f, 1.f, 1.f, 1.f);
+  }
 }
 
 __device__ __forceinline__ void pin4(uint4& v) {
@@ -345,7 +358,7 @@ template <int KFMT, int VFMT>
 __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[kDim], size_t row, int L, int lane) {
   constexpr int KQ = KFMT == kFmtF16 ? kFmtTurbo3 : KFMT;
   QRaw q;
-  q_request(a, row, lane, q);
+  q_request<KFMT != kFmtF16>(a, row, lane, q);
   __builtin_amdgcn_sched_barrier(0);
   RowInputs<KQ> kin;
   uint4 kraw = make_uint4(0, 0, 0, 0);
@@ -409,7 +422,7 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   const uint8_t* kbase = a.k_data + row * size_t(a.cap) * REC + part * (REC / P);
   const uint8_t* vbase = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT) + lane * (VW * 4);
   const uint16_t* knorm = KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap);
-  const uint16_t* vnorm = a.v_norms + row * size_t(a.cap);
+  const uint16_t* vnorm = VFMT == kFmtF16 ? nullptr : a.v_norms + row * size_t(a.cap);
   __shared__ float qs[kMaxGroup][kDim];
   if (append_wg) {
     // The append is one long dependent chain (binary64 butterflies, exact norm,
@@ -456,18 +469,20 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
     for (int sg = 0; sg < NS; ++sg)
       load_words(vw[sg], vbase + size_t(min((base >> 5) + sg, last_tile)) * v_tile_bytes(VFMT));
     const int tn = min((base >> 5) + sn, last_tile) << 5;
+    if (VFMT != kFmtF16) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) nv[rb] = *reinterpret_cast<const uint2*>(vnorm + tn + 16 * rb + 4 * g);
+      for (int rb = 0; rb < 2; ++rb) nv[rb] = *reinterpret_cast<const uint2*>(vnorm + tn + 16 * rb + 4 * g);
+    }
   };
   // q rows first, then the first iteration's words: waiting for q (the oldest
   // requests) leaves the K/V words in flight while q is rotated and staged.
   QRaw qraw;
-  q_request(a, row, lane, qraw);
+  q_request<KFMT != kFmtF16>(a, row, lane, qraw);
   // the 8 fp16 codebook entries each side's byte table needs (turbo4: the 8
-  // magnitudes, entries 8..15); F16 K reads V's, unused
-  uint4 cbraw[2];
-  cbraw[0] = *reinterpret_cast<const uint4*>(KFMT == kFmtF16 ? a.v_cb : a.k_cb + (KFMT == kFmtTurbo4 ? 8 : 0));
-  cbraw[1] = *reinterpret_cast<const uint4*>(a.v_cb + (VFMT == kFmtTurbo4 ? 8 : 0));
+  // magnitudes, entries 8..15); none for an fp16 side
+  uint4 cbraw[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  if constexpr (KFMT != kFmtF16) cbraw[0] = *reinterpret_cast<const uint4*>(a.k_cb + (KFMT == kFmtTurbo4 ? 8 : 0));
+  if constexpr (VFMT != kFmtF16) cbraw[1] = *reinterpret_cast<const uint4*>(a.v_cb + (VFMT == kFmtTurbo4 ? 8 : 0));
   __builtin_amdgcn_sched_barrier(0);  // keep every q request ahead of the K/V requests
   load_k(t0);
   load_v(t0);
@@ -621,8 +636,12 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
         const int i = 4 * rb + j;
         const float p = __builtin_amdgcn_exp2f(z[i] - m_use);
         psum += p;
-        const uint32_t w = j < 2 ? nv[rb].x : nv[rb].y;
-        pb[i] = _Float16(p * half_bits_to_float(uint16_t(w >> (16 * (j & 1)))));
+        if constexpr (VFMT == kFmtF16) {
+          pb[i] = _Float16(p);
+        } else {
+          const uint32_t w = j < 2 ? nv[rb].x : nv[rb].y;
+          pb[i] = _Float16(p * half_bits_to_float(uint16_t(w >> (16 * (j & 1)))));
+        }
       }
     }
     l_run += psum;
@@ -641,7 +660,9 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         half8 A;
-        if (VFMT == kFmtTurbo4) {
+        if constexpr (VFMT == kFmtF16) {
+          A = pack8(vw[sg][4 * nb], vw[sg][4 * nb + 1], vw[sg][4 * nb + 2], vw[sg][4 * nb + 3]);
+        } else if constexpr (VFMT == kFmtTurbo4) {
           A = dq_turbo4(vw[sg][nb], vtab);
         } else {
           const int sb = 3 * (nb >> 2);
@@ -712,7 +733,9 @@ template <int KF, int VF, bool SPARSE>
 void launch_sets(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
   // decode step: the appended token's two work groups (if any) come first
   const dim3 grid(a.col0 + a.plan.max_splits, a.hkv, batch), block(64);
-  if (a.group <= 16 / TQ_MFMA_NS_SMALL_GROUP)
+  if constexpr (VF == kFmtF16)  // 128-byte V chunks: one token set keeps the registers in bounds
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 1, SPARSE>), grid, block, 0, stream, a, lens);
+  else if (a.group <= 16 / TQ_MFMA_NS_SMALL_GROUP)
     hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, TQ_MFMA_NS_SMALL_GROUP, SPARSE>), grid, block, 0, stream, a, lens);
   else if (a.group <= 8) hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 2, SPARSE>), grid, block, 0, stream, a, lens);
   else hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 1, SPARSE>), grid, block, 0, stream, a, lens);
@@ -734,6 +757,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const SeqLens& lens, int batc
   if (a.kfmt == kFmtTurbo4 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtTurbo4, kFmtTurbo4>(a, lens, batch, stream);
   if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo3) return launch_fmt<kFmtF16, kFmtTurbo3>(a, lens, batch, stream);
   if (a.kfmt == kFmtF16 && a.vfmt == kFmtTurbo4) return launch_fmt<kFmtF16, kFmtTurbo4>(a, lens, batch, stream);
+  if (a.kfmt == kFmtF16 && a.vfmt == kFmtF16) return launch_fmt<kFmtF16, kFmtF16>(a, lens, batch, stream);
   return hipErrorInvalidValue;
 }
 

@@ -37,11 +37,11 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
   // its old words are requested now so the read overlaps the encode below.
   const bool whole = lo == tile * kTileTokens && hi == tile * kTileTokens + kTileTokens;
   uint8_t* chunk = a.v_data + (row * (a.cap / kTileTokens) + tile) * v_tile_bytes(VFMT) + (tid & 63) * v_chunk_bytes(VFMT);
-  constexpr int kChunkWords = v_chunk_bytes(VFMT) / 4;
+  constexpr int kChunkWords = VFMT == kFmtF16 ? 1 : v_chunk_bytes(VFMT) / 4;  // (F16 V: rows stored directly)
   uint32_t old[kChunkWords];
 #pragma unroll
   for (int i = 0; i < kChunkWords; ++i) old[i] = 0;
-  if (tid < 64 && !whole) {
+  if (VFMT != kFmtF16 && tid < 64 && !whole) {
 #pragma unroll
     for (int i = 0; i < kChunkWords; ++i) old[i] = reinterpret_cast<const uint32_t*>(chunk)[i];
   }
@@ -59,11 +59,14 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
     uint32_t w4[4];
     float sg[8];
     uint8_t code[8];
-    if (is_v) {
-      double beta[levels(VFMT) - 1];
+    if (is_v && VFMT == kFmtF16) {
+      store_f16_v_row(a, row, t, *reinterpret_cast<const uint4*>(a.v_new + src_off), j);
+    } else if (is_v) {
+      constexpr int VQ = VFMT == kFmtF16 ? kFmtTurbo3 : VFMT;  // (F16 V handled above)
+      double beta[levels(VQ) - 1];
       load_row_and_signs(a.v_new + src_off, a.v_signs, j, w4, sg);
-      load_thresholds<VFMT>(a.v_cb, beta);
-      const uint16_t nbits = encode_row<VFMT>(w4, sg, beta, j, code);
+      load_thresholds<VQ>(a.v_cb, beta);
+      const uint16_t nbits = encode_row<VQ>(w4, sg, beta, j, code);
       *reinterpret_cast<uint2*>(&vcodes[r][8 * j]) =
           make_uint2(uint32_t(code[0]) | uint32_t(code[1]) << 8 | uint32_t(code[2]) << 16 | uint32_t(code[3]) << 24,
                      uint32_t(code[4]) | uint32_t(code[5]) << 8 | uint32_t(code[6]) << 16 | uint32_t(code[7]) << 24);
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
   __syncthreads();
 
   // V tile chunks: one thread per chunk c = 16 g + n (dims 8n..8n+7, slots r(g, i)).
-  if (tid < 64) {
+  if constexpr (VFMT != kFmtF16) if (tid < 64) {
     const int g = tid >> 4, n = tid & 15;
     uint8_t el[64];
     if (!whole) {
@@ -171,6 +174,7 @@ hipError_t launch_encode_append(const EncodeArgs& a, const AppendStarts& starts,
   else if (k == kFmtTurbo4 && v == kFmtTurbo4) launch_one<kFmtTurbo4, kFmtTurbo4>(a, starts, nb, max_tiles, single, stream);
   else if (k == kFmtF16 && v == kFmtTurbo3) launch_one<kFmtF16, kFmtTurbo3>(a, starts, nb, max_tiles, single, stream);
   else if (k == kFmtF16 && v == kFmtTurbo4) launch_one<kFmtF16, kFmtTurbo4>(a, starts, nb, max_tiles, single, stream);
+  else if (k == kFmtF16 && v == kFmtF16) launch_one<kFmtF16, kFmtF16>(a, starts, nb, max_tiles, single, stream);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -26,6 +26,8 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(const void* __restrict__ 
   o[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// ROTATE = false (fp16 V, stored unrotated): the fp16 rounding alone.
+template <bool ROTATE>
 __global__ __launch_bounds__(256) void inverse_rotate_kernel(const float* __restrict__ o_rot,
                                                              const float* __restrict__ signs,
                                                              uint16_t* __restrict__ out, int rows) {
@@ -37,7 +39,8 @@ __global__ __launch_bounds__(256) void inverse_rotate_kernel(const float* __rest
   const float4 a = p[0], b = p[1];
   float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t w[4];
-  rotate_row_inverse_f16(v, signs, lane16, w);
+  if (ROTATE) rotate_row_inverse_f16(v, signs, lane16, w);
+  else round_row_f16(v, w);
   *reinterpret_cast<uint4*>(out + base) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -57,10 +60,12 @@ hipError_t launch_rotate_q(const void* q, bool q_fp32, bool rotate, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_inverse_rotate(const float* o_rot, const float* signs, uint16_t* out, int rows,
+hipError_t launch_inverse_rotate(const float* o_rot, bool rotate, const float* signs, uint16_t* out, int rows,
                                  hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(inverse_rotate_kernel, dim3((rows + 15) / 16), dim3(256), 0, stream, o_rot, signs, out, rows);
+  const dim3 grid((rows + 15) / 16), block(256);
+  if (rotate) hipLaunchKernelGGL((inverse_rotate_kernel<true>), grid, block, 0, stream, o_rot, signs, out, rows);
+  else hipLaunchKernelGGL((inverse_rotate_kernel<false>), grid, block, 0, stream, o_rot, signs, out, rows);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ constexpr int kFmtTurbo3 = 3;
 constexpr int kFmtTurbo4 = 4;
 
 __host__ __device__ constexpr int k_record_bytes(int fmt) { return fmt == kFmtTurbo3 ? 48 : 64; }
-__host__ __device__ constexpr int v_chunk_bytes(int fmt) { return fmt == kFmtTurbo3 ? 24 : 32; }
+__host__ __device__ constexpr int v_chunk_bytes(int fmt) { return fmt == kFmtTurbo3 ? 24 : fmt == kFmtF16 ? 128 : 32; }
 __host__ __device__ constexpr int v_tile_bytes(int fmt) { return 64 * v_chunk_bytes(fmt); }
 __host__ __device__ constexpr int levels(int fmt) { return fmt == kFmtTurbo3 ? 8 : 16; }
 
@@ -174,6 +174,14 @@ __device__ inline void rotate_row_forward(float v[8], const float* signs, int la
 
 // Out of V's codec basis and into fp16: s * H (v) / sqrt(128), nearest-even fp16
 // bits packed in pairs (element 8*lane16 + 2i in the low half of w[i]).
+// 8 fp32 values rounded to nearest-even fp16, packed in pairs.
+__device__ inline void round_row_f16(const float v[8], uint32_t w[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = uint32_t(__half_as_ushort(__float2half_rn(v[2 * i]))) |
+           (uint32_t(__half_as_ushort(__float2half_rn(v[2 * i + 1]))) << 16);
+}
+
 __device__ inline void rotate_row_inverse_f16(float v[8], const float* signs, int lane16, uint32_t w[4]) {
   fwht128_row(v, lane16);
 #pragma unroll

@@ -333,14 +333,31 @@ __device__ __forceinline__ void append_f16_k_row(const EncodeArgs& a, size_t row
       *reinterpret_cast<const uint4*>(src + 8 * j);
 }
 
+// Store an F16 V row (lane j: dims 8j..8j+7) into its tile: chunk 16g + j, element
+// 8*nb + i (i the token's element index in slot group g) is dim 8j + nb.
+__device__ __forceinline__ void store_f16_v_row(const EncodeArgs& a, size_t row, int t, uint4 v, int j) {
+  const int r = t % kTileTokens;
+  uint16_t* chunk = reinterpret_cast<uint16_t*>(a.v_data + (row * (a.cap / kTileTokens) + t / kTileTokens) *
+                                                              v_tile_bytes(kFmtF16)) +
+                    (16 * slot_group(r) + j) * (v_chunk_bytes(kFmtF16) / 2) + slot_elem(r);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) chunk[8 * nb] = uint16_t(w[nb >> 1] >> (16 * (nb & 1)));
+}
+
 // Both sides in one call (loads, then encode and store).
 template <int KFMT, int VFMT>
 __device__ __forceinline__ uint16_t append_row(const EncodeArgs& a, size_t row, int t, bool is_v, const uint16_t* src,
                                       int j, uint8_t (&code)[8]) {
   if (is_v) {
-    VRowInputs<VFMT> in;
-    load_v_inputs<VFMT>(a, row, t, src, j, in);
-    return append_v_row<VFMT>(a, row, t, in, j, code);
+    if constexpr (VFMT == kFmtF16) {
+      store_f16_v_row(a, row, t, *reinterpret_cast<const uint4*>(src + 8 * j), j);
+      return 0;
+    } else {
+      VRowInputs<VFMT> in;
+      load_v_inputs<VFMT>(a, row, t, src, j, in);
+      return append_v_row<VFMT>(a, row, t, in, j, code);
+    }
   }
   if (KFMT == kFmtF16) {
     append_f16_k_row(a, row, t, src, j);

@@ -41,7 +41,7 @@ hipError_t launch_encode_append(const EncodeArgs& a, const AppendStarts& starts,
 // ---- rotations
 hipError_t launch_rotate_q(const void* q, bool q_fp32, bool rotate, const float* signs, float* q_rot, int rows,
                            hipStream_t stream);
-hipError_t launch_inverse_rotate(const float* o_rot, const float* signs, uint16_t* out, int rows,
+hipError_t launch_inverse_rotate(const float* o_rot, bool rotate, const float* signs, uint16_t* out, int rows,
                                  hipStream_t stream);
 
 // ---- decode
@@ -76,6 +76,7 @@ struct DecodeArgs {
   int q_fp32;               // q_in is fp32 (else fp16 bits)
   int q_rotate;             // q_in goes through H(s_K * q)/sqrt(128) in-kernel (else it is in K's basis)
   float v_skip_log2;        // sparse V: log2 of the weight threshold, -inf when off
+  int v_rotated;            // V is stored in its rotated basis (the output is taken back); 0 for fp16 V
   int q_len;                // query positions per head (>= 1): a causal chunk of the last q_len tokens;
                             // `group` then counts (head, position) columns, head-major
   const float* k_signs;

@@ -62,7 +62,8 @@ def download_sequence(cache, b):
         out["k_rec"] = cache.k_data[b].cpu().numpy()
         out["k_norms"] = cache.k_norms[b].cpu().numpy().view(np.float16)
     out["v_tiles"] = cache.v_data[b].cpu().numpy()
-    out["v_norms"] = cache.v_norms[b].cpu().numpy().view(np.float16)
+    if cache.v_norms is not None:
+        out["v_norms"] = cache.v_norms[b].cpu().numpy().view(np.float16)
     return out
 
 
@@ -76,7 +77,7 @@ def oracle_dequant_bytes(cache, b, L, codebooks, seed=0):
     """K and V [Hkv, L, 128] (float64, original basis) of sequence b from the GPU-written bytes."""
     d = download_sequence(cache, b)
     kc, vc = reference.codes_from_library_layout(d.get("k_rec"), d["v_tiles"], cache.k_format, cache.v_format)
-    enc = {"v_codes": vc, "v_norms": d["v_norms"]}
+    enc = {"v_f16": vc} if cache.v_format == "f16" else {"v_codes": vc, "v_norms": d["v_norms"]}
     if cache.k_format == "f16":
         enc["k_f16"] = d["k_f16"]
     else:
@@ -139,7 +140,12 @@ def compare_codes(cache, b, k16, v16, L, w, codebooks, seed=0):
     d = download_sequence(cache, b)
     kc, vc = reference.codes_from_library_layout(d.get("k_rec"), d["v_tiles"], w.k_format, w.v_format)
     mism = margin = total = 0
-    parts = [("v", v16, vc, d["v_norms"], sv, w.v_format)]
+    parts = []
+    if w.v_format != "f16":
+        parts.append(("v", v16, vc, d["v_norms"], sv, w.v_format))
+    else:   # the uncompressed comparison cache holds the rows bit for bit; slots past L stay zero
+        np.testing.assert_array_equal(vc[:, :L].view(np.uint16), v16[:, :L].view(np.uint16))
+        assert np.all(vc[:, L:].view(np.uint16) == 0)
     if w.k_format != "f16":
         parts.append(("k", k16, kc, d["k_norms"], sk, w.k_format))
     else:

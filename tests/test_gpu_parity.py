@@ -455,3 +455,36 @@ def test_chunk_of_one_is_the_fused_decode():
     w, lens = _small_workloads()["c1"]
     cache, _, _, _, q = S.prefill_and_step(w, lengths=lens)
     np.testing.assert_array_equal(_gpu_chunk(cache, q[:, :, None])[:, :, 0], S.gpu_decode(cache, q, "fused"))
+
+
+# ----------------------------------------------------------------------------- fp16 comparison cache
+
+@pytest.mark.parametrize("group", [1, 7, 16])
+@pytest.mark.parametrize("variant", [2, "fused", "step", "chunk"])
+def test_f16_cache_parity(group, variant, codebooks):
+    """The uncompressed fp16 K and V cache (the pages' '× fp16' comparison point) through the
+    same MFMA decode: rows stored bit for bit, outputs against the oracle's plain attention on
+    them, through the separate, fused, step and chunk calls."""
+    from oracle import attention as att
+    w = S.scaled(get_workload(0), batch=3, num_q_heads=2 * group, num_kv_heads=2, k_format="f16",
+                 v_format="f16")
+    lens = np.array([2, 300, 64])
+    if variant == "step":
+        cache, k_list, v_list, L, q, got = S.prefill_then_decode_step(w, lengths=lens)
+    else:
+        cache, k_list, v_list, L, q = S.prefill_and_step(w, lengths=lens)
+    if variant == "chunk":
+        q_len = 2 if group <= 8 else 1
+        qc = np.stack([queries(w, 0, step=t) for t in range(q_len)], axis=2)
+        got = _gpu_chunk(cache, qc)
+    elif variant != "step":
+        got = S.gpu_decode(cache, q, variant=variant)
+    for b in range(3):
+        m, _, _ = S.compare_codes(cache, b, k_list[b], v_list[b], int(L[b]), w, codebooks)
+        assert m == 0
+        if variant == "chunk":
+            k_hat, v_hat = S.oracle_dequant_bytes(cache, b, int(L[b]), codebooks)
+            want = att.attention_chunk(qc[b:b + 1], [k_hat], [v_hat], [int(L[b])], S.SCALE)[0]
+        else:
+            want = S.oracle_end_to_end(w, k_list[b], v_list[b], int(L[b]), q[b], codebooks)
+        S.assert_close(got[b], want, f"fp16 cache {variant} G={group} b={b} L={int(L[b])}")

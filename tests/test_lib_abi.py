@@ -210,3 +210,16 @@ def test_sparse_v_threshold_range(lib):
         d = _desc(v_skip_threshold=tau)
         assert lib.tq_rotate_q(ctypes.byref(d), q, 0, 4, q, None) == status
         assert "v_skip_threshold" in _err(lib)
+
+
+def test_f16_v_only_with_f16_k(lib):
+    q = ctypes.c_void_p(0x20000)
+    ok = _desc(k_format=0, v_format=0, k_norms=0, k_signs=0, k_codebook=0, v_norms=0, v_signs=0, v_codebook=0)
+    # valid descriptor (the heads check fails next, proving it passed)
+    assert lib.tq_rotate_q(ctypes.byref(ok), q, 0, 3, q, None) == binding.TQ_EINVAL
+    assert "num_q_heads" in _err(lib)
+    bad = _desc(k_format=3, v_format=0, v_norms=0)
+    assert lib.tq_rotate_q(ctypes.byref(bad), q, 0, 4, q, None) == binding.TQ_EUNSUPPORTED
+    a, p = _lens(10, 10)
+    st = lib.tq_decode_attention_variant(ctypes.byref(ok), p, q, 4, ctypes.c_float(0.1), q, q, 10 ** 9, 1, None)
+    assert st == binding.TQ_EUNSUPPORTED and "reference" in _err(lib)

@@ -50,7 +50,8 @@
  *     8n..8n+7 of the 8 tokens in tile slots r = 16(i/4) + 4g + (i%4),
  *     i = 0..7; chunk element 8*nb + i is dim 8n+nb of token slot r(g, i).
  *     turbo3 chunk = 2 sub-blocks (24 bytes); turbo4 chunk = 8 octet words,
- *     word nb = elements 8nb..8nb+7 (32 bytes).  Tile: 1536 / 2048 bytes.
+ *     word nb = elements 8nb..8nb+7 (32 bytes); F16 chunk = the 64 elements
+ *     as fp16 values (128 bytes).  Tile: 1536 / 2048 / 8192 bytes.
  */
 #ifndef TQATTN_H
 #define TQATTN_H
@@ -72,7 +73,8 @@ typedef enum {
 } tq_status;
 
 typedef enum {
-  TQ_FMT_F16 = 0,       /* raw half-precision K (asymmetric mode only) */
+  TQ_FMT_F16 = 0,       /* raw half precision: K (asymmetric mode), or K and V together
+                           (the uncompressed cache the pages compare every mode against) */
   TQ_FMT_TURBO3 = 3,    /* 3-bit codes + fp16 norm, 50 bytes per 128-group */
   TQ_FMT_TURBO4 = 4     /* 4-bit codes + fp16 norm, 66 bytes per 128-group */
 } tq_format;
@@ -82,7 +84,9 @@ typedef enum {
  *            F16: fp16 [B][Hkv][capacity][128].
  *   k_norms  fp16 bits [B][Hkv][capacity]; NULL when k_format == TQ_FMT_F16.
  *   v_data   u8 [B][Hkv][capacity/32][1536 | 2048] V tiles.
- *   v_norms  fp16 bits [B][Hkv][capacity].
+ *   v_norms  fp16 bits [B][Hkv][capacity]; NULL when v_format == TQ_FMT_F16
+ *            (allowed only with k_format == TQ_FMT_F16; V is then stored
+ *            unrotated and v_signs / v_codebook are unused).
  *   seq_lens int32 [B]: visible tokens per sequence (the cache "offset"),
  *            kept up to date by tq_encode_append and tq_decode_step for callers
  *            that read it on the device; the decode calls take the lengths from

@@ -79,9 +79,18 @@ tq_status check_lengths(const tq_cache* c, const int32_t* lens, int32_t extra) {
 #ifndef TQ_PLAN_ITEMS
 #define TQ_PLAN_ITEMS 4096               // work items aimed for, group size > 4
 #endif
+#ifndef TQ_PLAN_LATENCY_ITEMS
+#define TQ_PLAN_LATENCY_ITEMS 256            // small calls: work items aimed for (one per compute unit)
+#endif
+#ifndef TQ_PLAN_LATENCY_BYTES
+#define TQ_PLAN_LATENCY_BYTES (32LL << 20)   // small calls: packed K + V bytes up to this
+#endif
 #ifndef TQ_PLAN_FLOOR
 #define TQ_PLAN_FLOOR 200   // bandwidth-bound calls: chunk >= TQ_PLAN_FLOOR * group tokens
 #endif
+
+// packed bytes per (token, KV head) of one side
+long long token_bytes(int fmt) { return fmt == TQ_FMT_TURBO3 ? 50 : fmt == TQ_FMT_TURBO4 ? 66 : 256; }
 
 // Split plan shared by the workspace query and the launch.  A fixed number of
 // work items over the chip, each a multiple of 64 tokens: 2048 (2 waves per SIMD,
@@ -90,6 +99,7 @@ tq_status check_lengths(const tq_cache* c, const int32_t* lens, int32_t extra) {
 // also even out ragged lengths).  Once the call is bandwidth-bound (>= 4M
 // token-heads) the chunk is also kept long enough that the partials (G x 130
 // floats, written then read) stay under ~4% of the packed bytes of the chunk.
+// Small calls (up to 32 MB of packed K and V) aim at one split per compute unit.
 tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
   long long total = 0;
   int lmax = 0;
@@ -101,6 +111,11 @@ tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
   long long chunk = (total + items - 1) / items;
   const bool bandwidth_bound = total >= (4LL << 20);
   if (bandwidth_bound) chunk = std::max(chunk, (long long)TQ_PLAN_FLOOR * group);
+  // small calls (a few tens of MB): about one work group per compute unit -- more
+  // splits only add waves that compete for the same units' load pipes
+  const long long bytes = total * (token_bytes(c->k_format) + token_bytes(c->v_format));
+  if (!bandwidth_bound && bytes <= TQ_PLAN_LATENCY_BYTES)
+    chunk = std::max(chunk, (total + TQ_PLAN_LATENCY_ITEMS - 1) / TQ_PLAN_LATENCY_ITEMS);
   chunk = std::max((long long)TQ_PLAN_MIN_CHUNK, (chunk + 63) / 64 * 64);
   tq::DecodePlan p;
   p.chunk = (int)chunk;

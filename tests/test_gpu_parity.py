@@ -488,3 +488,24 @@ def test_f16_cache_parity(group, variant, codebooks):
         else:
             want = S.oracle_end_to_end(w, k_list[b], v_list[b], int(L[b]), q[b], codebooks)
         S.assert_close(got[b], want, f"fp16 cache {variant} G={group} b={b} L={int(L[b])}")
+
+
+# ----------------------------------------------------------------------------- many sequences
+
+@pytest.mark.parametrize("variant", ["fused", "step"])
+def test_more_sequences_than_one_launch(variant, codebooks):
+    """300 sequences: the calls split them into launches of 256 (host lengths ride in the
+    kernel arguments); sequences on both sides of the seam, and the last, are checked."""
+    w = S.scaled(get_workload(0), batch=300)
+    lens = 1 + np.random.default_rng(7).integers(0, 80, 300)
+    if variant == "step":
+        cache, k_list, v_list, L, q, got = S.prefill_then_decode_step(w, lengths=lens)
+        np.testing.assert_array_equal(cache.seq_lens.cpu().numpy(), L)
+    else:
+        cache, k_list, v_list, L, q = S.prefill_and_step(w, lengths=lens)
+        got = S.gpu_decode(cache, q, variant="fused")
+    for b in (0, 255, 256, 299):
+        m, _, _ = S.compare_codes(cache, b, k_list[b], v_list[b], int(L[b]), w, codebooks)
+        assert m == 0
+        S.assert_close(got[b], S.oracle_end_to_end(w, k_list[b], v_list[b], int(L[b]), q[b], codebooks),
+                       f"{variant} b={b} L={int(L[b])}")

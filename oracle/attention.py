@@ -145,6 +145,58 @@ def sparse_v_bound(q, k_hat, v_hat, length, scale: float, tau: float):
     return o, bound
 
 
+def sparse_k_bound(q, k_hat, v_hat, length, scale: float, tau: float):
+    """What a K-side skip may drop from one sequence's attention (float64).
+
+    turboquant_plus "SMEM Pre-Dequant Experiment", idea 2 "Sparse K attention": skip
+    the K work of positions whose attention contribution is negligible, decided from
+    a cheap estimate such as the stored norm (here: score_upper_bound, an upper
+    bound, so the estimate never lets a significant token go).  Unlike sparse V a
+    skipped token leaves the scores, the softmax sum and the p.v sum alike.  A decoder
+    may drop token t of KV head g only when every query head of g gives it a weight
+    below tau relative to that head's largest weight (the same tokens sparse_v_bound
+    calls droppable).  With w the weights normalised over all tokens, D = sum of w over
+    the dropped tokens and o the exact output, the output of the kept tokens is
+    o' = (o - sum_drop w v) / (1 - D), so |o' - o| <= (D |o| + sum_drop w |v|) / (1 - D),
+    which only grows with the dropped set.  Returns (o, bound): o [Hq, D] the exact
+    attention, bound [Hq, D] that expression with every droppable token dropped.
+
+    q [Hq, D]; k_hat, v_hat [Hkv, L, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    kb = np.asarray(k_hat, dtype=np.float64)
+    vb = np.asarray(v_hat, dtype=np.float64)
+    Hq, D = q.shape
+    hkv = kb.shape[0]
+    group = Hq // hkv
+    L = int(length)
+    o = np.zeros((Hq, D))
+    bound = np.zeros((Hq, D))
+    for g in range(hkv):
+        heads = range(g * group, (g + 1) * group)
+        rel = np.stack([np.exp(scale * (kb[g, :L] @ q[h]) - (scale * (kb[g, :L] @ q[h])).max()) for h in heads])
+        droppable = np.all(rel < tau, axis=0)          # [L]
+        for i, h in enumerate(heads):
+            w = rel[i] / rel[i].sum()
+            o[h] = w @ vb[g, :L]
+            d = float(w[droppable].sum())
+            bound[h] = (d * np.abs(o[h]) + (w * droppable) @ np.abs(vb[g, :L])) / (1.0 - d)
+    return o, bound
+
+
+def score_upper_bound(q_row, k_norm, codebook, scale: float) -> float:
+    """An upper bound on the score of one query row against any token whose stored
+    norm is k_norm, whatever its codes: the token's dequantised K row in the rotated
+    basis is k_norm * c[idx], every entry at most max|c| in magnitude, so by
+    Cauchy-Schwarz (the rotation keeps q's length)
+    scale * q . k_hat <= scale * |q| * k_norm * sqrt(D) * max|c|.
+    This is the norm-only estimate turboquant_plus "SMEM Pre-Dequant Experiment",
+    idea 2, asks for, made one-sided: a token whose bound is already below
+    (running max + ln tau) for every head of its KV head has a weight below tau."""
+    q = np.asarray(q_row, dtype=np.float64)
+    c = np.asarray(codebook, dtype=np.float64)
+    return float(scale * np.sqrt(q @ q) * float(k_norm) * np.sqrt(q.shape[0]) * np.abs(c).max())
+
+
 def attention_chunk(q, k_hat, v_hat, lengths, scale: float) -> np.ndarray:
     """Decode attention of a chunk of Tq query positions per sequence (float64).
 

@@ -6,6 +6,7 @@ import torch
 from oracle import attention as att
 from oracle import codec
 from synth import sign_vector
+from tests.conftest import load_codebook
 
 SCALE = 1 / np.sqrt(128)
 
@@ -179,6 +180,79 @@ def test_sparse_v_bound_covers_any_dropped_subset():
             drop = droppable & (rng.random(L) < 0.5)
             o_drop = (w * ~drop) @ v[g]
             assert np.all(np.abs(o_drop - o[h]) <= bound[h] + 1e-15)
+
+
+def test_sparse_k_bound_hand_example():
+    """Three tokens, one KV head, one query head, D = 1, scale 1: scores 0, -20, -1,
+    values 2, -3, 5.  At tau = 1e-6 token 1 is droppable (weight ratio e^-20) and token 2
+    is not.  Dropping token 1 gives o' = (2 + 5 e^-1) / (1 + e^-1) exactly; the bound is
+    (D |o| + w_1 |v_1|) / (1 - D) with D = w_1, and it is attained up to rounding by that
+    drop when o and -v_1 have the same sign (here o > 0, v_1 = -3)."""
+    from oracle.attention import sparse_k_bound
+    k = np.array([[[0.0], [-20.0], [-1.0]]])
+    v = np.array([[[2.0], [-3.0], [5.0]]])
+    o, b = sparse_k_bound(np.array([[1.0]]), k, v, 3, 1.0, 1e-6)
+    rel = np.array([1.0, np.exp(-20.0), np.exp(-1.0)])
+    w = rel / rel.sum()
+    np.testing.assert_allclose(o[0, 0], w @ v[0, :, 0], rtol=1e-15)
+    d = w[1]
+    np.testing.assert_allclose(b[0, 0], (d * abs(o[0, 0]) + d * 3.0) / (1 - d), rtol=1e-12)
+    o_drop = (2.0 + 5.0 * np.exp(-1.0)) / (1.0 + np.exp(-1.0))
+    np.testing.assert_allclose(abs(o_drop - o[0, 0]), b[0, 0], rtol=1e-6)
+    # tau = 0: nothing droppable; tau = 1: everything but the maximum
+    _, b0 = sparse_k_bound(np.array([[1.0]]), k, v, 3, 1.0, 0.0)
+    assert np.all(b0 == 0)
+    _, b1 = sparse_k_bound(np.array([[1.0]]), k, v, 3, 1.0, 1.0)
+    d1 = w[1] + w[2]
+    np.testing.assert_allclose(b1[0, 0], (d1 * abs(o[0, 0]) + w[1] * 3.0 + w[2] * 5.0) / (1 - d1), rtol=1e-12)
+    assert abs(2.0 - o[0, 0]) <= b1[0, 0]   # o' = v_0 (not attained: v_2 has o's sign)
+
+
+def test_sparse_k_bound_covers_any_dropped_subset():
+    """Removing any subset of the droppable tokens from the whole softmax (scores, sum and
+    p.v) moves o by at most the bound."""
+    from oracle.attention import attention, sparse_k_bound
+    rng = np.random.default_rng(5)
+    hkv, G, L, D = 2, 3, 200, 16
+    k = rng.standard_normal((hkv, L, D)) * 3.0
+    v = rng.standard_normal((hkv, L, D))
+    q = rng.standard_normal((hkv * G, D)) * 3.0
+    tau = 1e-3
+    o, bound = sparse_k_bound(q, k, v, L, 0.5, tau)
+    np.testing.assert_allclose(o, attention(q[None], [k], [v], [L], 0.5)[0], rtol=1e-12, atol=1e-14)
+    for h in range(hkv * G):
+        g = h // G
+        z = np.stack([0.5 * (k[g] @ q[hh]) for hh in range(g * G, (g + 1) * G)])
+        rel = np.exp(z - z.max(axis=1, keepdims=True))
+        droppable = np.all(rel < tau, axis=0)
+        assert droppable.any()
+        zh = z[h - g * G]
+        for trial in range(5):
+            keep = ~(droppable & (rng.random(L) < 0.5))
+            wk = np.exp(zh[keep] - zh.max())
+            o_drop = (wk / wk.sum()) @ v[g][keep]
+            assert np.all(np.abs(o_drop - o[h]) <= bound[h] * (1 + 1e-12) + 1e-15)
+
+
+def test_score_upper_bound_holds_and_is_attained():
+    """Cauchy-Schwarz: every score over random codes stays below the norm-only bound, and
+    the bound is reached by the code that puts the largest-magnitude entry, with q's sign,
+    on every coordinate of a q whose entries all have one magnitude."""
+    from oracle.attention import score_upper_bound
+    from oracle.hadamard import rotate
+    rng = np.random.default_rng(6)
+    for name in ("turbo3", "turbo4"):
+        cb = load_codebook(name).astype(np.float64)
+        for trial in range(50):
+            q = rng.standard_normal(128) * rng.uniform(0.1, 10.0)
+            n = rng.uniform(0.0, 50.0)
+            idx = rng.integers(0, len(cb), 128)
+            qr = rotate(q, sign_vector(0, "k"))
+            z = SCALE * n * (qr @ cb[idx])
+            assert z <= score_upper_bound(q, n, cb, SCALE) * (1 + 1e-12)
+        qe = np.where(rng.random(128) < 0.5, -2.5, 2.5)
+        best = np.where(qe > 0, np.argmax(cb), np.argmin(cb))
+        np.testing.assert_allclose(SCALE * 3.0 * (qe @ cb[best]), score_upper_bound(qe, 3.0, cb, SCALE), rtol=1e-12)
 
 
 def test_chunk_attention_is_causal_and_reduces_to_single_token():

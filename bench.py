@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--v-skip-threshold", type=float, default=0.0,
                    help="sparse-V weight threshold of the decode calls (0 = exact attention)")
+    p.add_argument("--k-skip-threshold", type=float, default=0.0,
+                   help="sparse-K weight threshold of the decode calls (0 = exact attention)")
     p.add_argument("--formats", default=None,
                    help="K/V formats instead of the workload's, e.g. f16/f16 (the uncompressed comparison cache)")
     p.add_argument("--q-len", type=int, default=4,
@@ -122,7 +124,8 @@ def clone_cache(master):
         c.k_data.data_ptr(), 0 if c.k_norms is None else c.k_norms.data_ptr(), c.v_data.data_ptr(),
         0 if c.v_norms is None else c.v_norms.data_ptr(), c.seq_lens.data_ptr(), master.k_signs.data_ptr(),
         master.v_signs.data_ptr(),
-        master.k_codebook.data_ptr(), master.v_codebook.data_ptr(), master._desc.v_skip_threshold)
+        master.k_codebook.data_ptr(), master.v_codebook.data_ptr(), master._desc.v_skip_threshold,
+        master._desc.k_skip_threshold)
     return c
 
 
@@ -198,7 +201,8 @@ def main():
 
     # ---- setup (not timed): prefill L-1 tokens, append the step's token once
     master, k_list, v_list, L, q_np = S.prefill_and_step(w, seed)
-    master.v_skip_threshold = args.v_skip_threshold   # (the copies below inherit it)
+    master.v_skip_threshold = args.v_skip_threshold   # (the copies below inherit them)
+    master.k_skip_threshold = args.k_skip_threshold
     pre = (L - 1).astype(np.int32)
     per_copy = cache_bytes(master)
     n_copies = max(1, int(math.ceil(args.copies_gib * (1 << 30) / per_copy)))
@@ -344,7 +348,8 @@ def main():
                    "context_total": int(L.sum()), "k_format": w.k_format, "v_format": w.v_format,
                    "cache_copies": n_copies, "graph": use_graph,
                    "path": args.path, "variant": args.variant,
-                   "v_skip_threshold": args.v_skip_threshold, "q_scale": args.q_scale,
+                   "v_skip_threshold": args.v_skip_threshold, "k_skip_threshold": args.k_skip_threshold,
+                   "q_scale": args.q_scale,
                    "q_len": args.q_len if args.path == "chunk" else 1},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -106,6 +106,22 @@ typedef enum {
  *            "SMEM Pre-Dequant Experiment", idea 2 "Sparse K attention", names the
  *            V-side skip).  The VALU reference variant (tq_decode_attention_variant
  *            1) ignores it and is exact.
+ *   k_skip_threshold   sparse K, in [0, 1]; 0 turns it off (turboquant_plus
+ *            "SMEM Pre-Dequant Experiment", idea 2 "Sparse K attention": skip the
+ *            K work of positions whose contribution is negligible, judged from the
+ *            norm alone).  The MFMA decode kernel skips a whole iteration (32 to 128
+ *            tokens: K dequant, scores, softmax and values) when, for every query
+ *            head of the KV head, the Cauchy-Schwarz bound
+ *            scale * |q| * n * sqrt(128) * max|c| on the scores of the iteration's
+ *            tokens (n their largest stored K norm) is below that head's running
+ *            maximum score + ln(threshold): every skipped token's weight is below
+ *            the threshold relative to a maximum already seen.  Unlike sparse V the
+ *            skipped tokens also leave the softmax sum, so the result differs from
+ *            exact attention by at most (D |o| + sum of the skipped weights times
+ *            |v|) / (1 - D), D the skipped weight.  The words of a skipped iteration
+ *            are still read (bandwidth is not saved, VALU and MFMA work is).  It has
+ *            no effect with F16 K (no stored norms) or in the VALU reference
+ *            variant; the first iteration of every split is never skipped.
  * capacity must be a positive multiple of 32; head_dim must be 128.
  * The decode kernels read whole 32-token tiles and mask the slots at or past a
  * sequence's length, whose V norms are multiplied by an exact zero weight: they
@@ -127,6 +143,7 @@ typedef struct tq_cache {
   const uint16_t* k_codebook;
   const uint16_t* v_codebook;
   float v_skip_threshold;
+  float k_skip_threshold;
 } tq_cache;
 
 /* Encode new tokens and append them to each sequence

@@ -41,7 +41,7 @@ class tq_cache(ctypes.Structure):
         ("k_data", ctypes.c_void_p), ("k_norms", ctypes.c_void_p), ("v_data", ctypes.c_void_p),
         ("v_norms", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p), ("k_signs", ctypes.c_void_p),
         ("v_signs", ctypes.c_void_p), ("k_codebook", ctypes.c_void_p), ("v_codebook", ctypes.c_void_p),
-        ("v_skip_threshold", ctypes.c_float),
+        ("v_skip_threshold", ctypes.c_float), ("k_skip_threshold", ctypes.c_float),
     ]
 
 
@@ -143,7 +143,7 @@ class Cache:
             self.k_data.data_ptr(), 0 if self.k_norms is None else self.k_norms.data_ptr(),
             self.v_data.data_ptr(), 0 if self.v_norms is None else self.v_norms.data_ptr(), self.seq_lens.data_ptr(),
             self.k_signs.data_ptr(), self.v_signs.data_ptr(), self.k_codebook.data_ptr(),
-            self.v_codebook.data_ptr(), 0.0)
+            self.v_codebook.data_ptr(), 0.0, 0.0)
 
     @property
     def v_skip_threshold(self) -> float:
@@ -153,6 +153,15 @@ class Cache:
     @v_skip_threshold.setter
     def v_skip_threshold(self, tau: float):
         self._desc.v_skip_threshold = float(tau)
+
+    @property
+    def k_skip_threshold(self) -> float:
+        """Sparse-K weight threshold of the decode calls (0 = exact attention)."""
+        return float(self._desc.k_skip_threshold)
+
+    @k_skip_threshold.setter
+    def k_skip_threshold(self, tau: float):
+        self._desc.k_skip_threshold = float(tau)
 
     @property
     def desc(self):

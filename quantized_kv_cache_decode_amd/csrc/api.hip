@@ -46,6 +46,8 @@ tq_status check_cache(const tq_cache* c) {
     return fail(TQ_EINVAL, "NULL K norm/sign/codebook pointer for a quantised K format");
   if (!(c->v_skip_threshold >= 0.f && c->v_skip_threshold <= 1.f))
     return fail(TQ_EINVAL, "v_skip_threshold %g outside [0, 1]", (double)c->v_skip_threshold);
+  if (!(c->k_skip_threshold >= 0.f && c->k_skip_threshold <= 1.f))
+    return fail(TQ_EINVAL, "k_skip_threshold %g outside [0, 1]", (double)c->k_skip_threshold);
   const long long slots = (long long)c->batch * c->num_kv_heads * c->capacity;
   if (slots * 128 > (1LL << 46)) return fail(TQ_EINVAL, "cache too large");
   return TQ_OK;
@@ -250,6 +252,9 @@ tq_status decode_setup(const tq_cache* cache, const int32_t* seq_lens_host, int3
   a.col0 = 0;
   a.split_append = 0;
   a.v_skip_log2 = cache->v_skip_threshold > 0.f ? std::log2(cache->v_skip_threshold) : -INFINITY;
+  // the K-side bound needs the stored norms of a quantised K format
+  a.k_skip_log2 = cache->k_skip_threshold > 0.f && is_turbo(cache->k_format) ? std::log2(cache->k_skip_threshold)
+                                                                            : -INFINITY;
   a.q_len = 1;
   return TQ_OK;
 }

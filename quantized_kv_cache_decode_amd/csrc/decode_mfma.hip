@@ -383,8 +383,8 @@ __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[k
 template <int NS>
 constexpr int min_waves() { return TQ_MFMA_MIN_WAVES == 0 ? 1 : (NS == 4 ? TQ_MFMA_MIN_WAVES - 1 : TQ_MFMA_MIN_WAVES); }
 
-// SPARSE: the sparse-V skip is compiled in (its per-set branches cost the exact
-// route a few percent of scheduling freedom, so that route goes without them).
+// SPARSE: the sparse-V and sparse-K skips are compiled in (their branches cost the
+// exact route a few percent of scheduling freedom, so that route goes without them).
 template <int KFMT, int VFMT, int NS, bool SPARSE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(min_waves<NS>())))
 void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
@@ -510,6 +510,24 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   q_finish(a, qs, lane, qraw, a.q_rotate != 0);
   __syncthreads();
 
+  // Sparse K: kbound * n is an upper bound on this lane's column's score (log2
+  // units) against any token of stored K norm n, whatever its codes -- by
+  // Cauchy-Schwarz, |q| * n * sqrt(128) * max|c| (the rotation keeps |q|), widened by
+  // 2^-8 for the fp16 rounding of q and the fp32 sums of the score MFMAs.
+  float kbound = 0.f;
+  if constexpr (SPARSE && KFMT != kFmtF16) {
+    const float* qrow = &qs[min(hn, G - 1)][32 * g];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ss += qrow[i] * qrow[i];
+    ss = xsum4(ss);
+    const uint32_t kc[4] = {cbraw[0].x, cbraw[0].y, cbraw[0].z, cbraw[0].w};
+    float cmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cmax = fmaxf(cmax, fabsf(half_bits_to_float(uint16_t(kc[i >> 1] >> (16 * (i & 1))))));
+    kbound = a.scale * kLog2e * sqrtf(ss) * sqrtf(float(kDim)) * cmax * (1.f + 0x1p-8f);
+  }
+
   // q in this lane's score-MFMA B slots: q[hn][part*128/P + 8kk + t] * scale*log2(e),
   // zero unless the lane's k-slots belong to its column's set.
   // Kept in VGPRs: reading these operands from LDS inside the loop measured slower.
@@ -550,11 +568,10 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // One iteration over TOK tokens from `base`.  TAIL: the iteration reaches past
-  // t1 and the scores of slots >= t1 are masked (only the last one can).
-  auto step = [&](int base, auto tail_c) {
-    constexpr bool TAIL = decltype(tail_c)::value;
-    const int tn = ((base >> 5) + sn) << 5;      // first token of this lane's column tile
+  // Scores of the TOK tokens from `base` (log2 units, K norms applied, not yet
+  // masked) into S; the next iteration's K words and norms are requested as soon
+  // as this one's are turned into MFMA operands.
+  auto score_phase = [&](int base, floatx4 (&S)[2]) {
 #if TQ_MFMA_Q_LDS
     // an offset the compiler cannot see through keeps the q reads inside the loop
     int qoff = 0;
@@ -571,7 +588,6 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
         z[4 * rb + j] = KFMT != kFmtF16 ? half_bits_to_float(uint16_t(w >> (16 * (j & 1)))) : 1.f;
       }
     }
-    floatx4 S[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       S[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -601,13 +617,25 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
       }
     }
     load_k(base + TOK);     // next iteration's K words and K norms
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[rb][j] *= z[4 * rb + j];
+    }
+  };
 
-    // ---- online softmax (log2 domain) for the 8 tokens of this lane's column
+  // Softmax and values of the TOK tokens from `base` whose scores are in S.  TAIL:
+  // the iteration reaches past t1 and the scores of slots >= t1 are masked (only
+  // the last one can).
+  auto value_phase = [&](int base, const floatx4 (&S)[2], auto tail_c) {
+    constexpr bool TAIL = decltype(tail_c)::value;
+    const int tn = ((base >> 5) + sn) << 5;      // first token of this lane's column tile
+    float z[8];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float v = S[rb][j] * z[4 * rb + j];
+        float v = S[rb][j];
         if (TAIL && tn + 16 * rb + 4 * g + j >= t_col) v = -INFINITY;
         z[4 * rb + j] = v;
       }
@@ -683,9 +711,44 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
     load_v(base + TOK);     // next iteration's V words and V norms
   };
 
+  // Sparse K (compiled in with sparse V): an iteration is skipped whole -- no K
+  // dequant, no scores, no softmax update, no values -- when for every real column
+  // the norm-only upper bound of its tile's scores, kbound * (largest K norm of the
+  // tile), is below the column's running max + log2 tau_K, so every skipped token's
+  // weight is below tau_K relative to a maximum already seen.  The iteration's words
+  // were requested anyway; the next ones are requested as usual.
+  auto k_skip = [&]() -> bool {
+    if (!SPARSE || !(a.k_skip_log2 > -INFINITY)) return false;
+    // norms are non-negative fp16, which order like their bit patterns: the largest
+    // of the lane's 8 with packed 16-bit integer maxima, then of the column's 4 lanes
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    const u16x2 m2 = __builtin_elementwise_max(
+        __builtin_elementwise_max(__builtin_bit_cast(u16x2, nk[0].x), __builtin_bit_cast(u16x2, nk[0].y)),
+        __builtin_elementwise_max(__builtin_bit_cast(u16x2, nk[1].x), __builtin_bit_cast(u16x2, nk[1].y)));
+    const float nmax = xmax4(half_bits_to_float(m2.x > m2.y ? m2.x : m2.y));   // the column's 32-token tile
+    return !__any(hn < G && kbound * nmax >= m_run + a.k_skip_log2);
+  };
+
   int base = t0;
-  for (; base + TOK <= t_all; base += TOK) step(base, std::false_type{});
-  for (; base < t1; base += TOK) step(base, std::true_type{});  // at most two: t1 - t_all < 16 <= TOK
+  floatx4 S[2];
+  for (; base + TOK <= t_all; base += TOK) {
+    if (k_skip()) {
+      load_k(base + TOK);
+      load_v(base + TOK);
+      continue;
+    }
+    score_phase(base, S);
+    value_phase(base, S, std::false_type{});
+  }
+  for (; base < t1; base += TOK) {  // at most two: t1 - t_all < 16 <= TOK
+    if (k_skip()) {
+      load_k(base + TOK);
+      load_v(base + TOK);
+      continue;
+    }
+    score_phase(base, S);
+    value_phase(base, S, std::true_type{});
+  }
 
   // ---- finish: sum l over the column's 4 lanes, merge the NS sets of each head
   float l_tot = xsum4(l_run);
@@ -743,7 +806,7 @@ void launch_sets(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_
 
 template <int KF, int VF>
 hipError_t launch_fmt(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
-  if (a.v_skip_log2 > -INFINITY) launch_sets<KF, VF, true>(a, lens, batch, stream);
+  if (a.v_skip_log2 > -INFINITY || a.k_skip_log2 > -INFINITY) launch_sets<KF, VF, true>(a, lens, batch, stream);
   else launch_sets<KF, VF, false>(a, lens, batch, stream);
   return hipGetLastError();
 }

@@ -76,6 +76,7 @@ struct DecodeArgs {
   int q_fp32;               // q_in is fp32 (else fp16 bits)
   int q_rotate;             // q_in goes through H(s_K * q)/sqrt(128) in-kernel (else it is in K's basis)
   float v_skip_log2;        // sparse V: log2 of the weight threshold, -inf when off
+  float k_skip_log2;        // sparse K: log2 of the weight threshold, -inf when off (always off for F16 K)
   int v_rotated;            // V is stored in its rotated basis (the output is taken back); 0 for fp16 V
   int q_len;                // query positions per head (>= 1): a causal chunk of the last q_len tokens;
                             // `group` then counts (head, position) columns, head-major

@@ -416,6 +416,74 @@ def test_sparse_v_drops_only_droppable_tokens(tau, variant, codebooks):
         assert moved > 0.0
 
 
+# ----------------------------------------------------------------------------- sparse K
+
+@pytest.mark.parametrize("variant", [2, "fused"])
+def test_sparse_k_skips_nothing_on_gaussian_scores(variant, codebooks):
+    """At tau = 1e-6 the norm bound of Gaussian keys (about 24 above the scores' scale)
+    never falls below the running max + ln tau, so the output is bit-identical to exact
+    attention's."""
+    w, lens = _small_workloads()["c1"]
+    cache, _, _, _, q = S.prefill_and_step(w, lengths=lens)
+    exact = S.gpu_decode(cache, q, variant=variant)
+    cache.k_skip_threshold = 1e-6
+    np.testing.assert_array_equal(S.gpu_decode(cache, q, variant=variant), exact)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("variant", [2, "fused", "step"])
+def test_sparse_k_drops_only_droppable_tokens(variant, codebooks):
+    """Keys with small norms outside every 512-token block's first 128 tokens (K x 0.01,
+    their V x 1000 so that their weight shows), queries x 3, G = 4, a call of >= 4M
+    token-heads (splits of many 128-token iterations).  The iterations of small-norm keys
+    qualify at tau = 1e-2 once a split has seen a block start (the norm bound, about 0.7,
+    is below a running max of about 7.8 + ln 1e-2) and never at 1e-6.  With the skip the
+    output moves from the exact route's by at most the oracle's bound for dropping tokens
+    from the whole softmax (tau widened by 10% for the scores' fp16 rounding) -- and it
+    does move; at 1e-6 it is bit-identical."""
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    from oracle import attention as att
+    from synth import kv_slice
+    B, L = 64, 8200
+    w = S.scaled(get_workload(0), batch=B, num_q_heads=32, num_kv_heads=8)
+    pre = L - (1 if variant == "step" else 0)
+    assert pre * B * 8 >= 4 << 20
+    small = (np.arange(pre) % 512) >= 128
+    k0 = np.stack([kv_slice(w, 0, "k", 0, h, pre) for h in range(8)]).astype(np.float32)
+    v0 = np.stack([kv_slice(w, 0, "v", 0, h, pre) for h in range(8)]).astype(np.float32)
+    k0[:, small] *= 0.01
+    v0[:, small] *= 1000.0
+    k0, v0 = k0.astype(np.float16), v0.astype(np.float16)
+    cache = S.make_cache(w, 8224)
+    tq.tq_encode_append(cache, torch.from_numpy(k0).cuda()[None].expand(B, -1, -1, -1).contiguous(),
+                        torch.from_numpy(v0).cuda()[None].expand(B, -1, -1, -1).contiguous())
+    q = (queries(w, 0) * 3).astype(np.float32)
+    kn, vn = S.new_token_rows(w, 0)
+
+    def run(threshold):
+        cache.k_skip_threshold = threshold
+        if variant == "step":
+            cache.set_lengths(np.full(B, pre, dtype=np.int32))   # the step rewrites the same slot
+            return S.gpu_decode_step(cache, kn, vn, q).astype(np.float64)
+        return S.gpu_decode(cache, q, variant=variant).astype(np.float64)
+
+    exact = run(0.0)
+    np.testing.assert_array_equal(run(1e-6), exact)
+    got = run(1e-2)
+    moved = 0.0
+    for b in (0, B - 1):
+        k_hat, v_hat = S.oracle_dequant_bytes(cache, b, L, codebooks)
+        _, bound = att.sparse_k_bound(q[b], k_hat, v_hat, L, S.SCALE, 1.1e-2)
+        diff = np.abs(got[b] - exact[b])
+        slack = np.abs(exact[b]) * 2.0 ** -9 + 1e-5   # the two routes' fp16 output rounding
+        assert np.all(diff <= bound + slack), f"b={b}: {np.max(diff - bound - slack)}"
+        moved = max(moved, float(diff.max()))
+        _say(f"[sparse K {variant}] b={b} max move {diff.max():.2e}, max bound {bound.max():.2e}")
+    assert moved > 0.0
+
+
 # ----------------------------------------------------------------------------- chunk (Tq > 1)
 
 def _gpu_chunk(cache, q_np):

@@ -212,6 +212,17 @@ def test_sparse_v_threshold_range(lib):
         assert "v_skip_threshold" in _err(lib)
 
 
+def test_sparse_k_threshold_range(lib):
+    q = ctypes.c_void_p(0x20000)
+    for tau, status in ((-0.5, binding.TQ_EINVAL), (1.5, binding.TQ_EINVAL), (float("nan"), binding.TQ_EINVAL)):
+        d = _desc(k_skip_threshold=tau)
+        assert lib.tq_rotate_q(ctypes.byref(d), q, 0, 4, q, None) == status
+        assert "k_skip_threshold" in _err(lib)
+    d = _desc(k_skip_threshold=1e-6)   # valid: the heads check fails next
+    assert lib.tq_rotate_q(ctypes.byref(d), q, 0, 3, q, None) == binding.TQ_EINVAL
+    assert "num_q_heads" in _err(lib)
+
+
 def test_f16_v_only_with_f16_k(lib):
     q = ctypes.c_void_p(0x20000)
     ok = _desc(k_format=0, v_format=0, k_norms=0, k_signs=0, k_codebook=0, v_norms=0, v_signs=0, v_codebook=0)

@@ -23,10 +23,10 @@ overhead is not in the timed region.
 
 Prints ONE JSON line.  value = KV token-heads per second of whole steps
 (visible tokens x KV heads / step time).  roofline = the decode call
-(split-K kernel + LSE combine) timed by HIP events on its stream, eagerly
-enqueued behind a GPU sleep so the calls run back to back: algorithmic packed
-K+V bytes per call / average call duration (both kernels of the call), against
-8 TB/s.
+(split-K kernel + LSE combine) timed by HIP events on its stream around a run of
+calls enqueued eagerly behind a GPU sleep, so they run back to back: algorithmic
+packed K+V bytes per call / average call duration (both kernels of the call),
+against 8 TB/s.
 cpu_baseline = the float64 oracle (oracle/) doing the same step on a bounded
 sample, on the host cores.
 """
@@ -308,18 +308,17 @@ def main():
     # ---- decode-call duration by HIP events on the launch stream.  Events cannot be
     # recorded inside a captured graph here, so the calls are enqueued eagerly behind a
     # GPU sleep long enough for the host to queue them all: they then run back to back
-    # and each event pair brackets exactly one call (split-K kernel + LSE merge).
-    call_ms = []
+    # (split-K kernel + LSE merge each, a new cache copy each) and one event pair
+    # brackets the whole run, so no event sits between two calls' kernels.
     n_calls = min(per_graph, 512)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(int(5e7))
+    ev0.record()
     for i in range(n_calls):
-        c = caches[i % n_copies]
-        ev[i][0].record()
-        decode_call(c)
-        ev[i][1].record()
+        decode_call(caches[i % n_copies])
+    ev1.record()
     torch.cuda.synchronize()
-    call_ms = [a.elapsed_time(b) for a, b in ev]
+    call_ms = [ev0.elapsed_time(ev1) / n_calls]
     ms_per_step = (t1 - t0) * 1e3 / steps
     token_heads = int(L.sum()) * w.num_kv_heads
     value = token_heads / (ms_per_step * 1e-3)

@@ -276,6 +276,7 @@ tq_status launch_decode_and_merge(const tq_cache* cache, const int32_t* seq_lens
     // (grid columns 0 and 1), which run beside the splits; on bandwidth-bound calls
     // the splits fill the chip in one round and the row's first two splits append it.
     const bool step = a.app.k_new != nullptr;
+    a.step = step;
     a.col0 = step && !a.plan.bandwidth_bound ? 2 : 0;
     a.split_append = step && a.plan.bandwidth_bound;
     const hipError_t e = variant == 1 ? tq::launch_decode_reference(a, lens, nb, s)

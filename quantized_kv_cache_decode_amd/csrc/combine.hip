@@ -88,12 +88,27 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens)
   const int h = hq / G, g = hq % G;
   // Decode step: the splits cover the tokens before the append and the appended
   // token has its own slot.
-  const bool step = a.app.k_new != nullptr;
+  const bool step = a.step != 0;
   const int L = min(lens.len[blockIdx.y], a.cap);
   const int nsplit = min((L + a.plan.chunk - 1) / a.plan.chunk, a.plan.max_splits);
   const int nparts = nsplit + (step ? 1 : 0);  // partial v lives in slot v, the step's last in slot max_splits
   const size_t p0 = partial_index(a, size_t(b) * a.hkv + h, 0, g);  // slot s: p0 + s*G
   const int lane = threadIdx.x, j = lane & 15, sg = lane >> 4;
+
+  // The V sign flips of this lane's 8 dims are requested first: the inverse rotation
+  // at the end then waits for no memory round trip of its own.
+  // (Requested unconditionally, so no branch makes the compiler wait for them early;
+  // without a rotation they come from the workspace and are not used.)
+  float4 sgn0 = make_float4(1.f, 1.f, 1.f, 1.f), sgn1 = sgn0;
+  if constexpr (INVERSE) {
+    const float* sp = a.v_rotated ? a.v_signs : a.part_o;   // (>= 128 floats either way)
+    sgn0 = reinterpret_cast<const float4*>(sp + 8 * j)[0];
+    sgn1 = reinterpret_cast<const float4*>(sp + 8 * j)[1];
+  }
+  // Slot v of this (row, head): partials at o_row + v * G * 128 and ml_row + v * G * 2
+  // (the row's base is the same for every lane; the per-slot offsets fit in 32 bits).
+  const float* o_row = a.part_o + p0 * kDim + 8 * j;
+  const float* ml_row = a.part_ml + 2 * p0;
 
   Acc acc;
   acc.m = -INFINITY;
@@ -104,21 +119,21 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens)
     float ms[kBatch], ls[kBatch];
     float4 oa[kBatch], ob[kBatch];
     // Every load of the round is issued unconditionally (a partial past the end
-    // reads slot 0, always in bounds) and masked afterwards, so the round costs one
-    // memory round trip instead of one per partial.
+    // reads the step's slot, always in bounds) and masked afterwards, so the round
+    // costs one memory round trip instead of one per partial.
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int v = s0 + kGroups * k;
-      const size_t p = p0 + size_t(v < nsplit ? v : (v < nparts ? a.plan.max_splits : 0)) * G;
-      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * p);
-      const float4* src = reinterpret_cast<const float4*>(a.part_o + p * kDim + 8 * j);
+      const int slot = (v < nsplit ? v : a.plan.max_splits) * G;
+      const float2 ml = *reinterpret_cast<const float2*>(ml_row + 2 * slot);
+      const float4* src = reinterpret_cast<const float4*>(o_row + slot * kDim);
       ms[k] = ml.x;
       ls[k] = ml.y;
       oa[k] = src[0];
       ob[k] = src[1];
     }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < kBatch; ++k) {   // (branches the whole wave skips when every lane is in)
       if (s0 + kGroups * k >= nparts) {
         ms[k] = -INFINITY;
         ls[k] = 0.f;
@@ -154,8 +169,9 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens)
   const size_t row = size_t(b) * a.hkv * G + hq;
   if (INVERSE) {
     uint32_t w[4];
-    if (a.v_rotated) rotate_row_inverse_f16(v, a.v_signs, j, w);  // every row of 16 lanes, the same bits
-    else round_row_f16(v, w);                                      // fp16 V: already the original basis
+    const float s8[8] = {sgn0.x, sgn0.y, sgn0.z, sgn0.w, sgn1.x, sgn1.y, sgn1.z, sgn1.w};
+    if (a.v_rotated) rotate_row_inverse_f16_s8(v, s8, j, w);  // every row of 16 lanes, the same bits
+    else round_row_f16(v, w);                                         // fp16 V: already the original basis
     if (sg == 0) *reinterpret_cast<uint4*>(a.out + row * kDim + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
   } else if (sg == 0) {
     float4* dst = reinterpret_cast<float4*>(a.out_rot + row * kDim + 8 * j);

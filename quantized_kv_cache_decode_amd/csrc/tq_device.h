@@ -182,14 +182,22 @@ __device__ inline void round_row_f16(const float v[8], uint32_t w[4]) {
            (uint32_t(__half_as_ushort(__float2half_rn(v[2 * i + 1]))) << 16);
 }
 
-__device__ inline void rotate_row_inverse_f16(float v[8], const float* signs, int lane16, uint32_t w[4]) {
+// s8: the sign flips of this lane's elements 8*lane16 .. 8*lane16+7, already in registers
+__device__ inline void rotate_row_inverse_f16_s8(float v[8], const float (&s8)[8], int lane16, uint32_t w[4]) {
   fwht128_row(v, lane16);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float x0 = v[2 * i] * kInvSqrtD * signs[8 * lane16 + 2 * i];
-    const float x1 = v[2 * i + 1] * kInvSqrtD * signs[8 * lane16 + 2 * i + 1];
+    const float x0 = v[2 * i] * kInvSqrtD * s8[2 * i];
+    const float x1 = v[2 * i + 1] * kInvSqrtD * s8[2 * i + 1];
     w[i] = uint32_t(__half_as_ushort(__float2half_rn(x0))) | (uint32_t(__half_as_ushort(__float2half_rn(x1))) << 16);
   }
+}
+
+__device__ inline void rotate_row_inverse_f16(float v[8], const float* signs, int lane16, uint32_t w[4]) {
+  float s8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s8[i] = signs[8 * lane16 + i];
+  rotate_row_inverse_f16_s8(v, s8, lane16, w);
 }
 
 }  // namespace tq

@@ -86,6 +86,7 @@ struct DecodeArgs {
   float* part_ml;           // [B*Hkv*slots][group][2]     m (log2 units: z = scale*log2(e)*q.k), l
   float* out_rot;           // [B][Hq][128] fp32 in V's basis, or NULL when `out` is written
   uint16_t* out;            // [B][Hq][128] fp16 bits in the original basis, or NULL
+  int step;                 // decode step: the appended token has its own partial slot (app is set)
   EncodeArgs app;           // decode step: the one-token append (app.k_new == NULL otherwise)
 };
 

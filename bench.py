@@ -28,7 +28,9 @@ calls enqueued eagerly behind a GPU sleep, so they run back to back: algorithmic
 packed K+V bytes per call / average call duration (both kernels of the call),
 against 8 TB/s.
 cpu_baseline = the float64 oracle (oracle/) doing the same step on a bounded
-sample, on the host cores.
+sample, on the host cores; its output for sequence 0 also gates the run: the
+GPU's output of the timed step must sit within the tests' parity bars (rel-L2
+1e-3, max-abs 5e-3), reported as "parity", or bench.py exits non-zero.
 """
 import argparse
 import json
@@ -134,16 +136,20 @@ def cache_bytes(c):
 
 
 def cpu_baseline(w, seed, budget_s):
-    """The oracle doing the same step (append one token, full-dequant attention) on host cores."""
+    """The oracle doing the same step (append one token, full-dequant attention) on host cores.
+
+    Returns (record, o): the baseline record and the oracle's float64 output [Hq, 128] of
+    sequence 0, against which main() checks the GPU's output of the same step."""
     from threadpoolctl import threadpool_info
 
     from oracle import codec, reference
     from synth import kv_slice, new_token_kv, queries, sign_vector
+    from synth.gen import context_lengths
     from tests.conftest import load_codebook
     cbs = {"turbo3": load_codebook("turbo3"), "turbo4": load_codebook("turbo4")}
     sk, sv = sign_vector(seed, "k"), sign_vector(seed, "v")
     b = 0
-    L = int(w.context or 8192)
+    L = int(context_lengths(w, seed)[b])   # sequence 0's visible tokens after the step's append
     pre = L - 1
     k16 = np.stack([kv_slice(w, seed, "k", b, h, pre) for h in range(w.num_kv_heads)])
     v16 = np.stack([kv_slice(w, seed, "v", b, h, pre) for h in range(w.num_kv_heads)])
@@ -162,13 +168,13 @@ def cpu_baseline(w, seed, budget_s):
         c, n = codec.encode(vn, sv, cbs[w.v_format])
         enc["v_codes"][:, pre], enc["v_norms"][:, pre] = c[:, 0], n[:, 0]
         k_hat, v_hat = reference.dequant_sequence(enc, w.k_format, w.v_format, sk, sv, cbs, L)
-        reference.decode_sequence(q, k_hat, v_hat, L)
+        o = reference.decode_sequence(q, k_hat, v_hat, L)
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {
+    return o, {
         "value": steps * L * w.num_kv_heads / el,
         "unit": "KV token-heads/s",
         "cores": int(threads),
@@ -336,7 +342,17 @@ def main():
             + " + combine_kernel)",
             "call_us": dec_ms * 1e3,
             "algorithmic_bytes_per_call": alg}
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, seed, args.cpu_seconds)
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        o_ref, cpu = cpu_baseline(w, seed, args.cpu_seconds)
+        # Exactness gate: the timed calls' output for sequence 0 (every cache copy holds the
+        # same tokens, so the last call's output is the step's) against the oracle's output
+        # of the same step, at the parity bars of the tests.  Only where the step is the
+        # oracle's: exact attention, unscaled queries, one query position.
+        if args.path != "chunk" and args.q_scale == 1.0 and not args.v_skip_threshold and not args.k_skip_threshold:
+            rel, mx = S.errors(out[0].cpu().numpy(), o_ref)
+            parity = {"sequence": 0, "rel_l2": rel, "max_abs": mx, "rel_l2_bound": 1e-3, "max_abs_bound": 5e-3,
+                      "ok": bool(rel <= 1e-3 and mx <= 5e-3)}
     line = {
         "metric": METRIC, "value": value, "unit": "KV token-heads/s", "n_gpus": 1, "steps": steps,
         "warmup": warm_reps * per_graph if use_graph else args.warmup, "ms_per_step": ms_per_step,
@@ -352,8 +368,12 @@ def main():
                    "q_len": args.q_len if args.path == "chunk" else 1},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(line), flush=True)
+    if parity is not None and not parity["ok"]:
+        print(f"bench.py: the timed output of sequence 0 is outside the parity bars: {parity}", file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

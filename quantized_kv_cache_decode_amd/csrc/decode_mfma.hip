@@ -47,12 +47,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #ifndef TQ_MFMA_NS_SMALL_GROUP
 #define TQ_MFMA_NS_SMALL_GROUP 4   // token sets per MFMA for group sizes <= 4 (4 or 2)
 #endif
-#ifndef TQ_MFMA_Q_LDS
-#define TQ_MFMA_Q_LDS 0   // 1: score-MFMA q operands read from LDS in the loop (frees VGPRs)
-#endif
-#ifndef TQ_MFMA_V_FENCE
-#define TQ_MFMA_V_FENCE 0
-#endif
 #ifndef TQ_MFMA_LAZY_RESCALE
 #define TQ_MFMA_LAZY_RESCALE 1
 #endif
@@ -377,17 +371,11 @@ __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[k
   append_k_partial<KFMT, VFMT>(a, qs, row, L, lane, kin, kraw, s8);
 }
 
-#ifndef TQ_MFMA_MIN_WAVES
-#define TQ_MFMA_MIN_WAVES 0   // >0: ask the compiler for this many waves per SIMD (NS=4: minus 1)
-#endif
-template <int NS>
-constexpr int min_waves() { return TQ_MFMA_MIN_WAVES == 0 ? 1 : (NS == 4 ? TQ_MFMA_MIN_WAVES - 1 : TQ_MFMA_MIN_WAVES); }
 
 // SPARSE: the sparse-V and sparse-K skips are compiled in (their branches cost the
 // exact route a few percent of scheduling freedom, so that route goes without them).
 template <int KFMT, int VFMT, int NS, bool SPARSE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(min_waves<NS>())))
-void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   constexpr int P = 4 / NS;                  // lane groups per set in the score MFMA
   constexpr int Gp = 16 / NS;                // columns (padded heads) per set
   constexpr int TOK = 32 * NS;               // tokens per iteration
@@ -531,24 +519,6 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   // q in this lane's score-MFMA B slots: q[hn][part*128/P + 8kk + t] * scale*log2(e),
   // zero unless the lane's k-slots belong to its column's set.
   // Kept in VGPRs: reading these operands from LDS inside the loop measured slower.
-#if TQ_MFMA_Q_LDS
-  // fp16 operands in LDS: rows 0..G-1 = q * scale*log2(e), row kMaxGroup = zeros.
-  __shared__ half8 qh[kMaxGroup + 1][kDim / 8];
-  {
-    const float f = a.scale * kLog2e;
-    for (int i = lane; i < (G + 1) * (kDim / 8); i += 64) {
-      const int r = i / (kDim / 8), c = i % (kDim / 8);
-      const bool zero = r == G;
-      const float* src = &qs[zero ? 0 : r][8 * c];
-      const float ff = zero ? 0.f : f;
-      qh[zero ? kMaxGroup : r][c] = half8{_Float16(src[0] * ff), _Float16(src[1] * ff), _Float16(src[2] * ff),
-                                          _Float16(src[3] * ff), _Float16(src[4] * ff), _Float16(src[5] * ff),
-                                          _Float16(src[6] * ff), _Float16(src[7] * ff)};
-    }
-  }
-  __syncthreads();
-  const half8* qbase = (hn < G && sig == sn) ? &qh[hn][part * (NKK)] : &qh[kMaxGroup][0];
-#else
   half8 qb[NKK];
   {
     const bool use = hn < G && sig == sn;
@@ -562,7 +532,6 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
                      _Float16(x1.x * f), _Float16(x1.y * f), _Float16(x1.z * f), _Float16(x1.w * f)};
     }
   }
-#endif
   floatx4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -572,12 +541,6 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   // masked) into S; the next iteration's K words and norms are requested as soon
   // as this one's are turned into MFMA operands.
   auto score_phase = [&](int base, floatx4 (&S)[2]) {
-#if TQ_MFMA_Q_LDS
-    // an offset the compiler cannot see through keeps the q reads inside the loop
-    int qoff = 0;
-    asm volatile("" : "+v"(qoff));
-    const half8* qi = qbase + qoff;
-#endif
     // ---- scores (dequant of each operand right before its MFMA)
     float z[8];
 #pragma unroll
@@ -608,11 +571,7 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
             default: A = dq_turbo3<3>(wa, wb, wc, ktab); break;
           }
         }
-#if TQ_MFMA_Q_LDS
-        const half8 qk = qi[kk];
-#else
         const half8 qk = qb[kk];
-#endif
         S[rb] = mfma(A, qk, S[rb]);
       }
     }
@@ -705,9 +664,6 @@ void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
         acc[nb] = mfma(A, bsg, acc[nb]);
       }
     }
-#if TQ_MFMA_V_FENCE
-    __builtin_amdgcn_sched_barrier(0);  // keep the V requests after this iteration's PV
-#endif
     load_v(base + TOK);     // next iteration's V words and V norms
   };
 

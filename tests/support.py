@@ -1,11 +1,13 @@
 """Helpers shared by the GPU parity tests: seeded inputs, GPU encode/decode through
-the C ABI, download of the library's bytes, and the oracle on the same inputs."""
+the C ABI, download of the library's bytes, and the oracle on the same inputs.
+
+The oracle is imported only inside the helpers that run it (oracle_*, compare_codes),
+so importing this module -- as bench.py does for its GPU set-up -- loads no oracle code."""
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import replace
 
 import numpy as np
 
-from oracle import codec, reference
 from synth import context_lengths, kv_slice, new_token_kv, queries, sign_vector
 
 SCALE = 1.0 / np.sqrt(128.0)
@@ -69,12 +71,14 @@ def download_sequence(cache, b):
 
 def oracle_on_bytes(cache, b, L, q_b, codebooks, seed=0):
     """Oracle attention [Hq, 128] over the GPU-written bytes of sequence b (unpacked by the oracle)."""
+    from oracle import reference
     k_hat, v_hat = oracle_dequant_bytes(cache, b, L, codebooks, seed)
     return reference.decode_sequence(q_b, k_hat, v_hat, L)
 
 
 def oracle_dequant_bytes(cache, b, L, codebooks, seed=0):
     """K and V [Hkv, L, 128] (float64, original basis) of sequence b from the GPU-written bytes."""
+    from oracle import reference
     d = download_sequence(cache, b)
     kc, vc = reference.codes_from_library_layout(d.get("k_rec"), d["v_tiles"], cache.k_format, cache.v_format)
     enc = {"v_f16": vc} if cache.v_format == "f16" else {"v_codes": vc, "v_norms": d["v_norms"]}
@@ -88,6 +92,7 @@ def oracle_dequant_bytes(cache, b, L, codebooks, seed=0):
 
 def oracle_end_to_end(w, k16, v16, L, q_b, codebooks, seed=0):
     """Oracle encode + full-dequant attention [Hq, 128] of one sequence from its fp16 inputs."""
+    from oracle import reference
     sk, sv = sign_vector(seed, "k"), sign_vector(seed, "v")
     enc = reference.encode_sequence(k16[:, :L], v16[:, :L], w.k_format, w.v_format, sk, sv, codebooks)
     k_hat, v_hat = reference.dequant_sequence(enc, w.k_format, w.v_format, sk, sv, codebooks, L)
@@ -136,6 +141,7 @@ def compare_codes(cache, b, k16, v16, L, w, codebooks, seed=0):
 
     Returns (mismatching codes, codes within 1e-5 of a decision threshold, total codes);
     asserts norms bit-exact and every mismatch inside the boundary margin."""
+    from oracle import codec, reference
     sk, sv = sign_vector(seed, "k"), sign_vector(seed, "v")
     d = download_sequence(cache, b)
     kc, vc = reference.codes_from_library_layout(d.get("k_rec"), d["v_tiles"], w.k_format, w.v_format)

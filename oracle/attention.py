@@ -200,9 +200,9 @@ def score_upper_bound(q_row, k_norm, codebook, scale: float) -> float:
 def attention_chunk(q, k_hat, v_hat, lengths, scale: float) -> np.ndarray:
     """Decode attention of a chunk of Tq query positions per sequence (float64).
 
-    SURVEY's next step "Tq > 1 decode attention" (the pages' decode output is
-    [B, Hq, Tq, D], mlxcel PR #369 "Change"; the chunk's own tokens are the last Tq
-    of the cache and are causal among themselves): query position tau of sequence b
+    Decode with Tq > 1 query positions (speculative verification, chunked decode;
+    mlxcel PR #369 "Change" shapes the decode output [B, Hq, Tq, D]; the chunk's own
+    tokens are the last Tq of the cache and are causal among themselves): query position tau of sequence b
     (0 <= tau < Tq) sits at absolute position L_b - Tq + tau and attends to tokens
     t <= L_b - Tq + tau, i.e. to the first L_b - Tq + 1 + tau tokens.
 

@@ -149,12 +149,102 @@ def test_reconstruction_error_matches_lloyd_max_mse(fmt, bits, codebooks):
     assert abs(rel.mean() / want - 1) < 0.03
 
 
-@pytest.mark.parametrize("fmt,bound", [("turbo3", 1e-4), ("turbo4", 1e-4)])
-def test_boundary_margin_fraction(fmt, bound, codebooks):
+# Hand-placed coordinates.  A group with x_0 = a and x_1 = c (all else 0) has rotated
+# coordinates y_i = (s_0 a + (-1)^i s_1 c) / sqrt(128) (row i of the Sylvester matrix has
+# entries +1 and (-1)^i in columns 0 and 1), and the norm RNE_fp16(sqrt(a^2 + c^2)).  The
+# pairs below were found by a search over fp16 values; "delta" is where y_0 sits relative
+# to n16 * beta_j, checked below with 60-digit arithmetic.  The "+-2e-5" groups lie within
+# 1e-5 of the threshold in normalised units (2e-5 / n16 < 1e-5) and the "beta" groups within
+# 1e-5 of the unscaled midpoint beta_j itself, so a margin measured in normalised units, or
+# against beta_j without the norm, flags them.
+_MARGIN_GROUPS = {
+    "turbo3": [  # (x_0, x_1, threshold j, where y_0 sits)
+        (5.85546875, -0.30078125, 5, "+0.5e-5"),
+        (7.73046875, -0.3984375, 5, "-0.5e-5"),
+        (5.265625, -0.271484375, 5, "+2e-5"),
+        (3.83984375, -0.19775390625, 5, "-2e-5"),
+        (0.1256103515625, -0.375, 4, "beta"),
+    ],
+    "turbo4": [
+        (4.2421875, 1.828125, 9, "+0.5e-5"),
+        (4.1015625, 0.765625, 10, "-0.5e-5"),
+        (4.4765625, 1.9296875, 9, "+2e-5"),
+        (7.19921875, -0.7578125, 11, "-2e-5"),
+        (0.1251220703125, -0.133056640625, 8, "beta"),
+    ],
+}
+
+
+def _exact_coordinates(x16, signs):
+    """y = H (s * x) / sqrt(128) per coordinate, as 60-digit decimals (from the matrix
+    definition, not the oracle's transform)."""
+    H = sylvester()
+    sx = [Fraction(float(s)) * Fraction(float(v)) for s, v in zip(signs, x16)]
+    root = Decimal(128).sqrt()
+    out = []
+    for i in range(128):
+        acc = sum((sx[j] if H[i, j] > 0 else -sx[j]) for j in range(128) if sx[j] != 0)
+        acc = Fraction(acc)
+        out.append(Decimal(acc.numerator) / Decimal(acc.denominator) / root)
+    return out
+
+
+def _midpoints(codebook16):
+    c = [Fraction(float(v)) for v in codebook16]
+    return [(c[j] + c[j + 1]) / 2 for j in range(len(c) - 1)]
+
+
+@pytest.mark.parametrize("fmt", ["turbo3", "turbo4"])
+def test_boundary_margin_hand_placed(fmt, codebooks):
+    """Which coordinates lie within 1e-5 (input units) of n16 * beta_j, decided in 60-digit
+    arithmetic from the definition, for groups placed just inside and just outside the margin
+    of a threshold scaled by a non-unit norm."""
+    s = sign_vector(0, "k")
+    cb = codebooks[fmt]
+    mids = _midpoints(cb)
+    eps = Decimal("1e-5")
+    rows = []
+    for x0, x1, j, where in _MARGIN_GROUPS[fmt]:
+        x = _group([x0, x1])
+        n16 = _brute_norm(x)
+        y = _exact_coordinates(x, s)
+        thr = [Decimal(float(n16)) * Decimal(m.numerator) / Decimal(m.denominator) for m in mids]
+        beta_j = Decimal(mids[j].numerator) / Decimal(mids[j].denominator)
+        d0 = y[0] - thr[j]
+        if where == "beta":
+            assert abs(y[0] - beta_j) < Decimal("0.5e-5") and abs(float(n16) - 1) > 0.2
+            assert min(abs(y[0] - t) for t in thr) > eps
+        else:
+            target = Decimal(where.replace("e-5", "")) * eps
+            assert abs(d0 - target) < Decimal("0.06e-5"), (where, d0)
+            if where.endswith("2e-5"):
+                assert abs(d0) / Decimal(float(n16)) < eps      # inside a normalised-units margin
+        want = np.array([min(abs(yi - t) for t in thr) < eps for yi in y])
+        rows.append((x, want, where))
+    got = codec.boundary_margin(np.stack([r[0] for r in rows]), s, cb)
+    for (x, want, where), g in zip(rows, got):
+        np.testing.assert_array_equal(g, want, err_msg=where)
+        assert g[0] == (where in ("+0.5e-5", "-0.5e-5")), where
+
+
+@pytest.mark.parametrize("fmt", ["turbo3", "turbo4"])
+def test_boundary_margin_fraction(fmt, codebooks):
+    """On N(0,1) rows a rotated coordinate given the norm n is about n times a N(0, 1/128)
+    variable, so the fraction within eps of the thresholds n * beta_j is about
+    2 eps sum_j phi(sqrt(128) beta_j) E[sqrt(128) / n]; 15.4M coordinates (~500 to ~1000
+    events) must land within 20% of it, and under the 1e-4 the parity bars allow."""
+    from scipy.stats import norm
+    from oracle.lloyd_max import decision_boundaries
     rng = np.random.default_rng(9)
-    x = rng.standard_normal((20000, 128)).astype(np.float16)
-    frac = codec.boundary_margin(x, sign_vector(0, "k"), codebooks[fmt]).mean()
-    assert 0 < frac < bound
+    x = rng.standard_normal((120000, 128)).astype(np.float16)
+    s = sign_vector(0, "k")
+    frac = np.mean([codec.boundary_margin(x[i:i + 20000], s, codebooks[fmt]).mean()
+                    for i in range(0, len(x), 20000)])
+    n = codec.group_norm_fp16(x).astype(np.float64)
+    b = decision_boundaries(codebooks[fmt]).astype(np.float64) * np.sqrt(128.0)
+    predicted = 2e-5 * norm.pdf(b).sum() * np.mean(np.sqrt(128.0) / n)
+    assert abs(frac / predicted - 1) < 0.2, (frac, predicted)
+    assert frac < 1e-4
 
 
 # ----------------------------------------------------------------------------- layouts

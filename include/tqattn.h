@@ -205,8 +205,9 @@ tq_status tq_decode_attention(const tq_cache* cache, const int32_t* seq_lens_hos
                               void* stream);
 
 /* Same as tq_decode_attention with an explicit kernel variant, for A/B
- * comparison of kernel designs: 0 = default (the MFMA kernel), 1 = plain VALU
- * reference kernel, 2 = MFMA kernel.  Unknown variants give TQ_EINVAL. */
+ * comparison of kernel designs: 0 = the MFMA kernel (what every other decode
+ * call runs), 1 = the plain VALU reference kernel (quantised V formats only,
+ * else TQ_EUNSUPPORTED).  Other values give TQ_EINVAL. */
 tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_lens_host,
                                       const float* q_rot, int32_t num_q_heads, float scale,
                                       float* out_rot, void* workspace, size_t workspace_bytes,

@@ -100,9 +100,52 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _host_i32(lengths):
+def _host_i32(lengths, n=None, what="seq_lens_host"):
     arr = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    if n is not None and arr.shape != (n,):
+        raise ValueError(f"{what} has shape {arr.shape}; one entry per sequence ({n}) is needed")
     return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+# Argument checks, all made before the library is called: the C ABI takes bare device
+# pointers, so a tensor of the wrong shape, dtype, layout or device would otherwise become
+# an out-of-bounds device access instead of a Python error.
+def _tensor(t, name, shape, dtypes):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected {' or '.join(str(d) for d in dtypes)}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _on_gpu(cache, *named):
+    """Every tensor (and the cache's own buffers) on the cache's GPU."""
+    dev = cache.k_data.device
+    if dev.type != "cuda":
+        raise ValueError("the cache's buffers are not on a GPU")
+    for name, t in named:
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the cache on {dev}")
+
+
+def _workspace(workspace):
+    import torch
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous torch tensor")
+    return workspace
+
+
+def _q_shape(cache, q, name="q"):
+    """[B, Hq, 128] (or [B, Hq, Tq, 128] for a chunk) with Hq a multiple of Hkv."""
+    if q.dim() < 3 or q.shape[0] != cache.batch or q.shape[-1] != 128 or q.shape[1] % cache.num_kv_heads:
+        raise ValueError(f"{name} has shape {tuple(q.shape)}; expected [{cache.batch}, Hq, ..., 128] with Hq a "
+                         f"multiple of {cache.num_kv_heads}")
+    return tuple(q.shape)
 
 
 class Cache:
@@ -178,12 +221,19 @@ def tq_encode_append(cache: Cache, k_new, v_new, seq_lens_host=None, counts=None
     """Append fp16 rows k_new, v_new [B, Hkv, t_new, 128] at each sequence's current length.
 
     counts: optional per-sequence number of rows to take (ragged prefill)."""
+    import torch
+    if getattr(k_new, "dim", lambda: 0)() != 4:
+        raise ValueError("k_new must be [B, Hkv, t_new, 128]")
     t_new = int(k_new.shape[2])
-    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
+    shape = (cache.batch, cache.num_kv_heads, t_new, 128)
+    _tensor(k_new, "k_new", shape, (torch.float16,))
+    _tensor(v_new, "v_new", shape, (torch.float16,))
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host, cache.batch)
     if counts is None:
         cnt, pc = np.full(cache.batch, t_new, dtype=np.int32), ctypes.c_void_p(0)
     else:
-        cnt, pc = _host_i32(counts)
+        cnt, pc = _host_i32(counts, cache.batch, "counts")
+    _on_gpu(cache, ("k_new", k_new), ("v_new", v_new))
     _check(load_library().tq_encode_append(cache.desc, p, _ptr(k_new), _ptr(v_new), t_new, pc, _stream(stream)))
     cache.lengths = arr + cnt
 
@@ -191,12 +241,18 @@ def tq_encode_append(cache: Cache, k_new, v_new, seq_lens_host=None, counts=None
 def tq_rotate_q(cache: Cache, q, q_rot, stream=None):
     """q [B, Hq, 128] (fp16 or fp32) -> q_rot fp32 in K's codec basis."""
     import torch
+    shape = _q_shape(cache, q)
+    if len(shape) != 3:
+        raise ValueError("q must be [B, Hq, 128]")
+    _tensor(q, "q", shape, (torch.float16, torch.float32))
+    _tensor(q_rot, "q_rot", shape, (torch.float32,))
+    _on_gpu(cache, ("q", q), ("q_rot", q_rot))
     _check(load_library().tq_rotate_q(cache.desc, _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]),
                                       _ptr(q_rot), _stream(stream)))
 
 
 def tq_decode_workspace_size(cache: Cache, num_q_heads: int, seq_lens_host=None) -> int:
-    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host, cache.batch)
     n = load_library().tq_decode_workspace_size(cache.desc, num_q_heads, p)
     if n == 0:
         raise TqError(TQ_EINVAL, load_library().tq_last_error().decode())
@@ -205,8 +261,18 @@ def tq_decode_workspace_size(cache: Cache, num_q_heads: int, seq_lens_host=None)
 
 def tq_decode_attention(cache: Cache, q_rot, scale, out_rot, workspace, seq_lens_host=None, variant=0,
                         stream=None):
-    """out_rot [B, Hq, 128] fp32 = decode attention in V's rotated basis (workspace: device uint8)."""
-    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
+    """out_rot [B, Hq, 128] fp32 = decode attention in V's rotated basis (workspace: device memory).
+
+    variant 0 (default): the MFMA kernel; 1: the plain VALU reference kernel."""
+    import torch
+    shape = _q_shape(cache, q_rot, "q_rot")
+    if len(shape) != 3:
+        raise ValueError("q_rot must be [B, Hq, 128]")
+    _tensor(q_rot, "q_rot", shape, (torch.float32,))
+    _tensor(out_rot, "out_rot", shape, (torch.float32,))
+    _workspace(workspace)
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host, cache.batch)
+    _on_gpu(cache, ("q_rot", q_rot), ("out_rot", out_rot), ("workspace", workspace))
     _check(load_library().tq_decode_attention_variant(
         cache.desc, p, _ptr(q_rot), int(q_rot.shape[1]), float(scale), _ptr(out_rot), _ptr(workspace),
         int(workspace.numel() * workspace.element_size()), int(variant), _stream(stream)))
@@ -216,7 +282,14 @@ def tq_decode_attention_fused(cache: Cache, q, scale, out, workspace, seq_lens_h
     """out fp16 [B, Hq, 128] = decode attention of q [B, Hq, 128] (fp16 or fp32, unrotated), with the
     q rotation and the output's inverse rotation done inside the decode and merge kernels."""
     import torch
-    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
+    shape = _q_shape(cache, q)
+    if len(shape) != 3:
+        raise ValueError("q must be [B, Hq, 128]")
+    _tensor(q, "q", shape, (torch.float16, torch.float32))
+    _tensor(out, "out", shape, (torch.float16,))
+    _workspace(workspace)
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host, cache.batch)
+    _on_gpu(cache, ("q", q), ("out", out), ("workspace", workspace))
     _check(load_library().tq_decode_attention_fused(
         cache.desc, p, _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]), float(scale), _ptr(out),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream)))
@@ -227,7 +300,14 @@ def tq_decode_chunk_fused(cache: Cache, q, scale, out, workspace, seq_lens_host=
     q [B, Hq, Tq, 128] (fp16 or fp32, unrotated) over each sequence's visible tokens, the
     chunk's own Tq tokens last.  Workspace: tq_decode_workspace_size(cache, Hq * Tq)."""
     import torch
-    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
+    shape = _q_shape(cache, q)
+    if len(shape) != 4:
+        raise ValueError("q must be [B, Hq, Tq, 128]")
+    _tensor(q, "q", shape, (torch.float16, torch.float32))
+    _tensor(out, "out", shape, (torch.float16,))
+    _workspace(workspace)
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host, cache.batch)
+    _on_gpu(cache, ("q", q), ("out", out), ("workspace", workspace))
     _check(load_library().tq_decode_chunk_fused(
         cache.desc, p, _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]), int(q.shape[2]), float(scale),
         _ptr(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream)))
@@ -238,9 +318,17 @@ def tq_decode_step(cache: Cache, k_new, v_new, q, scale, out, workspace, seq_len
     [B, Hq, 128] over all visible tokens including it; out fp16 [B, Hq, 128].  The workspace is
     sized with the lengths before the append."""
     import torch
-    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host)
-    if int(k_new.shape[2]) != 1 or int(v_new.shape[2]) != 1:
-        raise ValueError("tq_decode_step appends exactly one token per sequence")
+    kv_shape = (cache.batch, cache.num_kv_heads, 1, 128)
+    _tensor(k_new, "k_new", kv_shape, (torch.float16,))
+    _tensor(v_new, "v_new", kv_shape, (torch.float16,))
+    shape = _q_shape(cache, q)
+    if len(shape) != 3:
+        raise ValueError("q must be [B, Hq, 128]")
+    _tensor(q, "q", shape, (torch.float16, torch.float32))
+    _tensor(out, "out", shape, (torch.float16,))
+    _workspace(workspace)
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host, cache.batch)
+    _on_gpu(cache, ("k_new", k_new), ("v_new", v_new), ("q", q), ("out", out), ("workspace", workspace))
     _check(load_library().tq_decode_step(
         cache.desc, p, _ptr(k_new), _ptr(v_new), _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]),
         float(scale), _ptr(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
@@ -250,5 +338,12 @@ def tq_decode_step(cache: Cache, k_new, v_new, q, scale, out, workspace, seq_len
 
 def tq_inverse_rotate_out(cache: Cache, out_rot, out, stream=None):
     """out_rot fp32 [B, Hq, 128] -> out fp16 [B, Hq, 128] in the original basis."""
+    import torch
+    shape = _q_shape(cache, out_rot, "out_rot")
+    if len(shape) != 3:
+        raise ValueError("out_rot must be [B, Hq, 128]")
+    _tensor(out_rot, "out_rot", shape, (torch.float32,))
+    _tensor(out, "out", shape, (torch.float16,))
+    _on_gpu(cache, ("out_rot", out_rot), ("out", out))
     _check(load_library().tq_inverse_rotate_out(cache.desc, _ptr(out_rot), int(out_rot.shape[1]), _ptr(out),
                                                 _stream(stream)))

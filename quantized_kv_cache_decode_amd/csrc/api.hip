@@ -296,7 +296,7 @@ tq_status tq_decode_attention_variant(const tq_cache* cache, const int32_t* seq_
   tq_status st = decode_setup(cache, seq_lens_host, num_q_heads, scale, workspace, ws_bytes, a);
   if (st != TQ_OK) return st;
   if (!q_rot || !out_rot) return fail(TQ_EINVAL, "q_rot / out_rot is NULL");
-  if (variant < 0 || variant > 2) return fail(TQ_EINVAL, "unknown decode variant %d", variant);
+  if (variant < 0 || variant > 1) return fail(TQ_EINVAL, "unknown decode variant %d", variant);
   if (variant == 1 && cache->v_format == TQ_FMT_F16)
     return fail(TQ_EUNSUPPORTED, "the VALU reference variant reads quantised V only");
   a.q_rot = q_rot;  // (the reference kernel reads it; the MFMA kernel stages it as fp32 q, unrotated)

@@ -1,4 +1,4 @@
-// MFMA split-K decode attention for gfx950 (variant 2).
+// MFMA split-K decode attention for gfx950 (the default decode kernel, variant 0).
 //
 // One wave per work item (split s of KV head h of sequence b).  Both
 // contractions run on v_mfma_f32_16x16x32_f16 with fp32 accumulation; the VALU

@@ -102,7 +102,8 @@ def oracle_end_to_end(w, k16, v16, L, q_b, codebooks, seed=0):
 def gpu_decode(cache, q_np, variant=0):
     """Decode of q [B, Hq, 128] through the C ABI; returns fp16 [B, Hq, 128] as numpy.
 
-    variant 0/1/2: tq_rotate_q -> tq_decode_attention(variant) -> tq_inverse_rotate_out;
+    variant 0 (MFMA) / 1 (VALU reference): tq_rotate_q -> tq_decode_attention(variant) ->
+    tq_inverse_rotate_out;
     "fused": tq_decode_attention_fused (rotations inside the decode and merge kernels)."""
     import torch
 

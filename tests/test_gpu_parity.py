@@ -19,7 +19,7 @@ from tests import support as S
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [1, 2, "fused"]
+VARIANTS = [0, 1, "fused"]
 
 
 def _say(*a):
@@ -184,7 +184,7 @@ def test_fused_call_matches_separate_calls_bitwise(name):
     the workloads cover fp32 q (c0) and fp16 q, and the unrotated fp16-K mode (c2)."""
     w, lens = _small_workloads()[name]
     cache, _, _, _, q = S.prefill_and_step(w, lengths=lens)
-    sep = S.gpu_decode(cache, q, variant=2)
+    sep = S.gpu_decode(cache, q, variant=0)
     fused = S.gpu_decode(cache, q, variant="fused")
     np.testing.assert_array_equal(fused.view(np.uint16), sep.view(np.uint16))
 
@@ -355,7 +355,7 @@ def test_bandwidth_bound_step_edge_rows(codebooks):
 
 # ----------------------------------------------------------------------------- sparse V
 
-@pytest.mark.parametrize("variant", [2, "fused"])
+@pytest.mark.parametrize("variant", [0, "fused"])
 def test_sparse_v_skips_nothing_on_gaussian_scores(variant, codebooks):
     """At tau = 1e-6 the benchmark-like inputs (Gaussian keys and queries) leave no V tile
     below the threshold, so the output is bit-identical to exact attention's."""
@@ -368,7 +368,7 @@ def test_sparse_v_skips_nothing_on_gaussian_scores(variant, codebooks):
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("tau", [1e-6, 1e-2])
-@pytest.mark.parametrize("variant", [2, "fused", "step"])
+@pytest.mark.parametrize("variant", [0, "fused", "step"])
 def test_sparse_v_drops_only_droppable_tokens(tau, variant, codebooks):
     """Peaked scores (queries x16, G = 4) on a call large enough (>= 4M token-heads) that the
     splits run 16 iterations: the output with sparse V moves from the exact route's by at
@@ -418,7 +418,7 @@ def test_sparse_v_drops_only_droppable_tokens(tau, variant, codebooks):
 
 # ----------------------------------------------------------------------------- sparse K
 
-@pytest.mark.parametrize("variant", [2, "fused"])
+@pytest.mark.parametrize("variant", [0, "fused"])
 def test_sparse_k_skips_nothing_on_gaussian_scores(variant, codebooks):
     """At tau = 1e-6 the norm bound of Gaussian keys (about 24 above the scores' scale)
     never falls below the running max + ln tau, so the output is bit-identical to exact
@@ -431,7 +431,7 @@ def test_sparse_k_skips_nothing_on_gaussian_scores(variant, codebooks):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("variant", [2, "fused", "step"])
+@pytest.mark.parametrize("variant", [0, "fused", "step"])
 def test_sparse_k_drops_only_droppable_tokens(variant, codebooks):
     """Keys with small norms outside every 512-token block's first 128 tokens (K x 0.01,
     their V x 1000 so that their weight shows), queries x 3, G = 4, a call of >= 4M
@@ -528,7 +528,7 @@ def test_chunk_of_one_is_the_fused_decode():
 # ----------------------------------------------------------------------------- fp16 comparison cache
 
 @pytest.mark.parametrize("group", [1, 7, 16])
-@pytest.mark.parametrize("variant", [2, "fused", "step", "chunk"])
+@pytest.mark.parametrize("variant", [0, "fused", "step", "chunk"])
 def test_f16_cache_parity(group, variant, codebooks):
     """The uncompressed fp16 K and V cache (the pages' '× fp16' comparison point) through the
     same MFMA decode: rows stored bit for bit, outputs against the oracle's plain attention on

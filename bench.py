@@ -18,19 +18,25 @@ Hkv=4, head dim 128, 8192 visible tokens, turbo3 K and V) unless --workload says
 otherwise.  The cache is replicated into distinct HBM copies (>= 1 GiB in all)
 and the steps rotate through them, so every step streams its cache from HBM
 rather than from the 256 MB Infinity Cache (each copy stands for another layer
-of the model).  Steps are captured in a HIP graph and replayed, so host launch
-overhead is not in the timed region.
+of the model); the timed steps use copies the warm-up did not touch, after a
+512 MiB copy has flushed the Infinity Cache.  Steps are captured in HIP graphs
+(uploaded before the warm-up) and replayed, so host launch overhead is not in
+the timed region: exactly --warmup untimed steps, then exactly --steps timed ones.
 
 Prints ONE JSON line.  value = KV token-heads per second of whole steps
 (visible tokens x KV heads / step time).  roofline = the decode call
 (split-K kernel + LSE combine) timed by HIP events on its stream around a run of
 calls enqueued eagerly behind a GPU sleep, so they run back to back: algorithmic
 packed K+V bytes per call / average call duration (both kernels of the call),
-against 8 TB/s.
-cpu_baseline = the float64 oracle (oracle/) doing the same step on a bounded
-sample, on the host cores; its output for sequence 0 also gates the run: the
-GPU's output of the timed step must sit within the tests' parity bars (rel-L2
-1e-3, max-abs 5e-3), reported as "parity", or bench.py exits non-zero.
+against 8 TB/s.  With the defaults the line also carries "per_workload": the
+same call timing and parity for the 16K fp16-K + turbo4-V layer, the batched
+turbo4 workload and the ragged turbo3 workload (measured after the timed steps).
+cpu_baseline = the float64 oracle (oracle/) doing the same step over a process
+pool on the host cores (one worker per (sequence, KV head, token block) unit,
+one BLAS thread each); its output for sequence 0 also gates the run: the GPU's
+output of the timed step must sit within the tests' parity bars (rel-L2 1e-3,
+max-abs 5e-3) and its codes must equal the oracle's outside the 1e-5 boundary
+margin, reported as "parity", or bench.py exits non-zero.
 """
 import argparse
 import json
@@ -47,9 +53,11 @@ sys.path.insert(0, ROOT)
 METRIC = "quantized-KV decode attention: KV tokens/s/head + % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 BYTES_PER_TOKEN_HEAD = {"turbo3": 50, "turbo4": 66, "f16": 256}
+EXTRA_WORKLOADS = (2, 3, 4)     # carried in the default line besides the headline workload
+CODE_SLICE_TOKENS = 4096         # tokens of sequence 0 whose codes the parity record compares
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=3200)
@@ -63,6 +71,7 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the per-workload records of the other workloads")
     p.add_argument("--v-skip-threshold", type=float, default=0.0,
                    help="sparse-V weight threshold of the decode calls (0 = exact attention)")
     p.add_argument("--k-skip-threshold", type=float, default=0.0,
@@ -73,17 +82,18 @@ def parse():
                    help="query positions per sequence of --path chunk (a causal chunk of the last tokens)")
     p.add_argument("--q-scale", type=float, default=1.0,
                    help="multiply the synthetic queries (e.g. 16 for peaked attention weights)")
-    return p.parse_args()
+    return p.parse_args(argv)
 
 
 KERNEL_SOURCES = tuple("quantized_kv_cache_decode_amd/csrc/" + f
-                       for f in ("decode_mfma.hip", "decode_ref.hip", "combine.hip", "tq_device.h", "tq_encode.h",
-                                 "tq_launch.h"))
+                       for f in ("api.hip", "decode_mfma.hip", "decode_ref.hip", "combine.hip", "tq_device.h",
+                                 "tq_encode.h", "tq_launch.h"))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash():
-    """sha256 of the decode and merge kernel sources (ties recorded counters to the code)."""
+    """sha256 of the decode and merge kernel sources and of the split planner (ties recorded
+    counters to the code)."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -95,7 +105,6 @@ def kernel_source_hash():
 def recorded_traffic(workload_name):
     """HBM bytes per decode call from the committed FETCH_SIZE/WRITE_SIZE profile, or None
     when there is none for this workload or the kernels changed since it was taken."""
-    import json
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -135,58 +144,246 @@ def cache_bytes(c):
     return sum(t.numel() * t.element_size() for t in (c.k_data, c.k_norms, c.v_data, c.v_norms) if t is not None)
 
 
-def cpu_baseline(w, seed, budget_s):
-    """The oracle doing the same step (append one token, full-dequant attention) on host cores.
+# ============================================================================ oracle leg
+# Everything below that imports oracle/ is the CPU baseline and the parity gate; the GPU
+# path above and in main() never calls it.
 
-    Returns (record, o): the baseline record and the oracle's float64 output [Hq, 128] of
-    sequence 0, against which main() checks the GPU's output of the same step."""
-    from threadpoolctl import threadpool_info
+def _oracle_unit(task, barrier, results):
+    """One worker of the CPU baseline: the oracle's share of a decode step for one
+    (sequence b, KV head h, token block [t0, t1)) unit, repeated until the budget is spent.
 
+    Per repetition: encode the appended token when the block holds slot L-1, dequantise the
+    block's K and V rows (float64, original basis) and form the unnormalised partial (m, l, o)
+    of the G query heads of h over them.  BLAS runs single-threaded in every worker."""
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    from dataclasses import replace
+
+    from oracle import attention as att
     from oracle import codec, reference
-    from synth import kv_slice, new_token_kv, queries, sign_vector
-    from synth.gen import context_lengths
+    from synth import get_workload, kv_slice, new_token_kv, queries, sign_vector
     from tests.conftest import load_codebook
+    uid, widx, formats, seed, b, h, t0, t1, L, budget = task
+    w = get_workload(widx)
+    if formats:
+        w = replace(w, k_format=formats[0], v_format=formats[1])
     cbs = {"turbo3": load_codebook("turbo3"), "turbo4": load_codebook("turbo4")}
     sk, sv = sign_vector(seed, "k"), sign_vector(seed, "v")
-    b = 0
-    L = int(context_lengths(w, seed)[b])   # sequence 0's visible tokens after the step's append
-    pre = L - 1
-    k16 = np.stack([kv_slice(w, seed, "k", b, h, pre) for h in range(w.num_kv_heads)])
-    v16 = np.stack([kv_slice(w, seed, "v", b, h, pre) for h in range(w.num_kv_heads)])
-    enc = reference.encode_sequence(k16, v16, w.k_format, w.v_format, sk, sv, cbs, capacity=((L + 31) // 32) * 32)
-    kn = np.stack([new_token_kv(w, seed, "k", b, h, 0) for h in range(w.num_kv_heads)])
-    vn = np.stack([new_token_kv(w, seed, "v", b, h, 0) for h in range(w.num_kv_heads)])
-    q = queries(w, seed)[b]
-    steps, t0 = 0, time.perf_counter()
+    pre = L - 1                       # the step appends token L-1
+    k16 = kv_slice(w, seed, "k", b, h, pre)[None, t0:min(t1, pre)]
+    v16 = kv_slice(w, seed, "v", b, h, pre)[None, t0:min(t1, pre)]
+    holds_new = t1 == L
+    if holds_new:                     # the appended row's slot, filled by the timed loop
+        k16 = np.concatenate([k16, np.zeros((1, 1, 128), np.float16)], axis=1)
+        v16 = np.concatenate([v16, np.zeros((1, 1, 128), np.float16)], axis=1)
+    enc = reference.encode_sequence(k16, v16, w.k_format, w.v_format, sk, sv, cbs)
+    kn = new_token_kv(w, seed, "k", b, h, 0)[None]
+    vn = new_token_kv(w, seed, "v", b, h, 0)[None]
+    G = w.group
+    q_rows = np.asarray(queries(w, seed)[b][h * G:(h + 1) * G], dtype=np.float64)
+    n_tok = t1 - t0
+    barrier.wait()
+    start = time.perf_counter()
+    reps = 0
     while True:
-        # append: encode the new token into slot L-1
-        if w.k_format == "f16":
-            enc["k_f16"][:, pre] = kn[:, 0]
-        else:
-            c, n = codec.encode(kn, sk, cbs[w.k_format])
-            enc["k_codes"][:, pre], enc["k_norms"][:, pre] = c[:, 0], n[:, 0]
-        c, n = codec.encode(vn, sv, cbs[w.v_format])
-        enc["v_codes"][:, pre], enc["v_norms"][:, pre] = c[:, 0], n[:, 0]
-        k_hat, v_hat = reference.dequant_sequence(enc, w.k_format, w.v_format, sk, sv, cbs, L)
-        o = reference.decode_sequence(q, k_hat, v_hat, L)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+        if holds_new:
+            s = n_tok - 1
+            if w.k_format == "f16":
+                enc["k_f16"][:, s] = kn[:, 0]
+            else:
+                c, n = codec.encode(kn, sk, cbs[w.k_format])
+                enc["k_codes"][:, s], enc["k_norms"][:, s] = c[:, 0], n[:, 0]
+            if w.v_format == "f16":
+                enc["v_f16"][:, s] = vn[:, 0]
+            else:
+                c, n = codec.encode(vn, sv, cbs[w.v_format])
+                enc["v_codes"][:, s], enc["v_norms"][:, s] = c[:, 0], n[:, 0]
+        k_hat, v_hat = reference.dequant_sequence(enc, w.k_format, w.v_format, sk, sv, cbs, n_tok)
+        part = att.partial(q_rows, k_hat[0], v_hat[0], reference.SCALE)
+        reps += 1
+        el = time.perf_counter() - start
+        if el >= budget:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return o, {
-        "value": steps * L * w.num_kv_heads / el,
+    results.put((uid, reps, el, n_tok, part))
+
+
+def cpu_baseline(w, widx, formats, seed, budget_s):
+    """The float64 oracle doing the step for sequence 0 (append one token + full-dequant
+    attention over all its visible tokens) over a process pool on the host cores.
+
+    Units are (sequence 0, KV head, token block): the KV heads, each cut into enough token
+    blocks that there is one unit per available core.  Every worker sets up its unit (not
+    timed), waits at a barrier, then repeats its unit for the budget; the rate is the sum of
+    the workers' rates.  Returns (record, o): o is the oracle's float64 output [Hq, 128] of
+    sequence 0 for the step, the LSE merge of the units' last partials."""
+    import multiprocessing as mp
+    import queue
+
+    from oracle import attention as att
+    from synth.gen import context_lengths
+    host_cores = len(os.sched_getaffinity(0))
+    b = 0
+    L = int(context_lengths(w, seed)[b])
+    H = w.num_kv_heads
+    blocks = max(1, min(host_cores // H, L // 64))
+    bounds = [(L * i) // blocks for i in range(blocks + 1)]
+    tasks = [(h * blocks + i, widx, formats, seed, b, h, bounds[i], bounds[i + 1], L, budget_s)
+             for h in range(H) for i in range(blocks)]
+    ctx = mp.get_context("spawn")     # fresh interpreters: the parent holds a GPU context
+    barrier, results = ctx.Barrier(len(tasks)), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_unit, args=(t, barrier, results), daemon=True) for t in tasks]
+    for p in procs:
+        p.start()
+    got, deadline = [], time.time() + 600 + 4 * budget_s
+    while len(got) < len(procs):
+        try:
+            got.append(results.get(timeout=1.0))
+        except queue.Empty:
+            dead = [p.exitcode for p in procs if p.exitcode not in (None, 0)]
+            if dead or time.time() > deadline:
+                for p in procs:
+                    p.terminate()
+                raise RuntimeError(f"CPU baseline workers failed (exit codes {dead}) or timed out")
+    for p in procs:
+        p.join(timeout=60)
+    got.sort(key=lambda r: r[0])
+    rate = sum(r[1] * r[3] / r[2] for r in got)        # token-heads per second (one KV head per unit)
+    o = np.concatenate([att.combine([got[h * blocks + i][4] for i in range(blocks)]) for h in range(H)])
+    reps = [r[1] for r in got]
+    rec = {
+        "value": rate,
         "unit": "KV token-heads/s",
-        "cores": int(threads),
+        "cores": len(procs),
+        "host_cores": host_cores,
         "kind": "oracle",
-        "sample": f"{steps} steps of sequence 0 of {w.name} (append 1 token + float64 full-dequant "
-                  f"attention over {L} tokens x {w.num_kv_heads} KV heads x {w.group} query heads each) "
-                  f"in {el:.1f} s",
+        "sample": f"sequence 0 of {w.name}: append 1 token + float64 full-dequant attention over {L} tokens x "
+                  f"{H} KV heads x {w.group} query heads each, as {len(procs)} single-threaded worker processes "
+                  f"(one per (KV head, token block) unit, {blocks} blocks per head), {budget_s:.0f} s each, "
+                  f"{min(reps)}-{max(reps)} repetitions per unit",
     }
+    return rec, o
 
 
-def main():
-    args = parse()
+def oracle_parity(cache, w, b, L_b, k16, v16, q_b, got_b, o_ref=None, codebooks=None):
+    """Parity of one sequence of the timed step's output: against o_ref (the oracle's end-to-end
+    output, when given) or the oracle on the GPU-written bytes; codes and norms of the first
+    CODE_SLICE_TOKENS tokens against the oracle's encode of the same rows."""
+    from tests import support as S
+    from tests.conftest import load_codebook
+    codebooks = codebooks or {"turbo3": load_codebook("turbo3"), "turbo4": load_codebook("turbo4")}
+    if o_ref is None:
+        o_ref = S.oracle_on_bytes(cache, b, L_b, q_b, codebooks)
+        against = "oracle on the GPU-written bytes"
+    else:
+        against = "oracle end to end (its own encode)"
+    rel, mx = S.errors(got_b, o_ref)
+    n = L_b if w.v_format == "f16" else min(L_b, CODE_SLICE_TOKENS)   # (fp16 rows: no encode, all of them)
+    codes = {"tokens": n}
+    try:
+        m, g, t = S.compare_codes(cache, b, k16[:, :n], v16[:, :n], n, w, codebooks)
+        codes.update(mismatches=m, within_margin=g, total=t, ok=bool(m <= g <= 1e-4 * max(t, 1)))
+    except AssertionError as e:       # norms differ, or codes differ outside the margin
+        codes.update(ok=False, error=str(e).splitlines()[0][:200])
+    return {"sequence": b, "against": against, "rel_l2": rel, "max_abs": mx, "rel_l2_bound": 1e-3,
+            "max_abs_bound": 5e-3, "codes": codes,
+            "ok": bool(rel <= 1e-3 and mx <= 5e-3 and codes["ok"])}
+
+
+# ============================================================================ GPU timing
+
+def hip_graph_upload(graph):
+    """Upload an instantiated graph to the device (hipGraphUpload) so that its first replay
+    does not carry the upload; best effort (a no-op where the handle is not exposed)."""
+    import ctypes
+
+    import torch
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")      # the runtime torch already loaded
+        hip.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        ex = graph.raw_cuda_graph_exec()
+        return hip.hipGraphUpload(ctypes.c_void_p(int(ex)), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+    except Exception:  # pragma: no cover
+        return False
+
+
+def time_calls(call, caches, n_calls):
+    """Average duration (ms) of n_calls back-to-back calls, one HIP event pair on the launch
+    stream around them all.  Events cannot be recorded inside a captured graph here, so the
+    calls are enqueued eagerly behind a GPU sleep long enough for the host to queue them."""
+    import torch
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(5e7))
+    ev0.record()
+    for i in range(n_calls):
+        call(caches[i % len(caches)])
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / n_calls
+
+
+def flush_infinity_cache():
+    """Write and read 512 MiB of other memory, so cache copies touched before are out of the
+    256 MB Infinity Cache."""
+    import torch
+    a = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
+    a.fill_(1.0)
+    b = a.clone()
+    del a, b
+
+
+def setup_copies(w, seed, copies_gib, min_copies=1):
+    """Prefill L-1 tokens of every sequence (setup) and replicate the cache into distinct HBM
+    copies of >= copies_gib in all."""
+    from tests import support as S
+    master, k_list, v_list, L, q_np = S.prefill_and_step(w, seed)
+    per_copy = cache_bytes(master)
+    n_copies = max(min_copies, int(math.ceil(copies_gib * (1 << 30) / per_copy)))
+    caches = [master] + [clone_cache(master) for _ in range(n_copies - 1)]
+    return caches, k_list, v_list, L, q_np
+
+
+def extra_workload(widx, seed, with_oracle, codebooks):
+    """Call timing and parity of tq_decode_step on another workload (not the timed steps)."""
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    from synth import get_workload
+    from tests import support as S
+    w = get_workload(widx)
+    caches, k_list, v_list, L, q_np = setup_copies(w, seed, 1.0, min_copies=2)
+    pre = (L - 1).astype(np.int32)
+    kn, vn = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in S.new_token_rows(w, seed))
+    q = torch.from_numpy(np.ascontiguousarray(q_np)).cuda()
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float16, device="cuda")
+    ws = torch.zeros(tq.tq_decode_workspace_size(caches[0], w.num_q_heads, pre), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(128.0)
+
+    def call(c):
+        tq.tq_decode_step(c, kn, vn, q, scale, out, ws, seq_lens_host=pre)
+
+    call(caches[0])
+    torch.cuda.synchronize()
+    n_calls = max(8, min(256, 64 * len(caches)))
+    flush_infinity_cache()
+    call_ms = time_calls(call, caches, n_calls)
+    alg = algorithmic_bytes(w, L)
+    achieved = alg / (call_ms * 1e-3) / 1e9
+    rec = {"call_us": call_ms * 1e3, "calls_timed": n_calls, "cache_copies": len(caches),
+           "algorithmic_bytes_per_call": alg, "achieved_GBs": achieved, "frac": achieved / HBM_PEAK_GBS,
+           "kv_token_heads_per_s": int(L.sum()) * w.num_kv_heads / (call_ms * 1e-3),
+           "traffic": recorded_traffic(w.name), "parity": None}
+    if with_oracle:
+        got = out.cpu().numpy()
+        rec["parity"] = oracle_parity(caches[0], w, 0, int(L[0]), k_list[0], v_list[0], q_np[0], got[0],
+                                      codebooks=codebooks)
+    del caches, k_list, v_list, kn, vn, q, out, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return w.name, rec
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode path is built and measured "
               "on a single MI355X; sharding is described, not built.", file=sys.stderr)
@@ -194,29 +391,30 @@ def main():
     import torch
 
     import quantized_kv_cache_decode_amd as tq
-    from synth import get_workload, new_token_kv, queries
+    from synth import get_workload, queries
     from tests import support as S
     tq.load_library()
     torch.cuda.set_device(0)
     w = get_workload(args.workload)
+    formats = None
     if args.formats:
         from dataclasses import replace
-        kf, vf = args.formats.split("/")
-        w = replace(w, k_format=kf, v_format=vf)
+        formats = tuple(args.formats.split("/"))
+        w = replace(w, k_format=formats[0], v_format=formats[1])
     seed = 0
+    K, W = int(args.steps), int(args.warmup)
+    if K < 1 or W < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
 
-    # ---- setup (not timed): prefill L-1 tokens, append the step's token once
-    master, k_list, v_list, L, q_np = S.prefill_and_step(w, seed)
-    master.v_skip_threshold = args.v_skip_threshold   # (the copies below inherit them)
-    master.k_skip_threshold = args.k_skip_threshold
+    # ---- setup (not timed): prefill L-1 tokens, replicate the cache into distinct copies
+    caches, k_list, v_list, L, q_np = setup_copies(w, seed, args.copies_gib)
+    for c in caches:
+        c.v_skip_threshold = args.v_skip_threshold
+        c.k_skip_threshold = args.k_skip_threshold
+    n_copies = len(caches)
+    master = caches[0]
     pre = (L - 1).astype(np.int32)
-    per_copy = cache_bytes(master)
-    n_copies = max(1, int(math.ceil(args.copies_gib * (1 << 30) / per_copy)))
-    caches = [master] + [clone_cache(master) for _ in range(n_copies - 1)]
-    kn = S.padded_tensor([np.stack([new_token_kv(w, seed, "k", b, h, 0) for h in range(w.num_kv_heads)])
-                          for b in range(w.batch)], 1)
-    vn = S.padded_tensor([np.stack([new_token_kv(w, seed, "v", b, h, 0) for h in range(w.num_kv_heads)])
-                          for b in range(w.batch)], 1)
+    kn, vn = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in S.new_token_rows(w, seed))
     q_np = (q_np.astype(np.float32) * args.q_scale).astype(q_np.dtype)
     q = torch.from_numpy(np.ascontiguousarray(q_np)).cuda()
     B, Hq = w.batch, w.num_q_heads
@@ -237,8 +435,6 @@ def main():
         qc = torch.from_numpy(np.ascontiguousarray((qc_np.astype(np.float32) * args.q_scale).astype(qc_np.dtype))).cuda()
         out_c = torch.empty((B, Hq, Tq, 128), dtype=torch.float16, device="cuda")
         ws = torch.zeros(tq.tq_decode_workspace_size(master, Hq * Tq, L), dtype=torch.uint8, device="cuda")
-    del k_list, v_list
-    per_graph = n_copies
     # a plain 512 MiB device copy (setup, untimed): its FETCH_SIZE / WRITE_SIZE counters
     # calibrate the HBM traffic figures read for the decode kernel in the same profile
     calib = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
@@ -274,66 +470,76 @@ def main():
         if sep:
             tq.tq_inverse_rotate_out(c, out_rot, out)
 
+    # Warm-up steps use copies 0, 1, ...; the timed steps continue the rotation from copy W,
+    # so with --steps + --warmup <= the number of copies no timed step finds its copy in a cache.
+    warm_idx = [i % n_copies for i in range(W)]
+    timed_idx = [(W + i) % n_copies for i in range(K)]
+    step(0)                           # load the kernels' code objects before any capture (setup)
+    torch.cuda.synchronize()
+
+    def plan(idx):
+        """Graphs for a list of step indices: (graph over the first min(len, n_copies) steps,
+        replays) + (graph over the remainder, 1); the rotation is periodic in n_copies."""
+        n = len(idx)
+        if n == 0:
+            return []
+        full = min(n, n_copies)
+        parts = [(idx[:full], n // full)]
+        if n % full:
+            parts.append((idx[:n % full], 1))
+        return parts
+
     use_graph = not args.no_graph
-    graph = None
+    graphs = {}
     if use_graph:
         try:
-            for i in range(per_graph):       # warm the launch path outside capture
-                step(i)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for i in range(per_graph):
-                    step(i)
+            for name, idx in (("warm", warm_idx), ("timed", timed_idx)):
+                graphs[name] = []
+                for sub, reps in plan(idx):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        for i in sub:
+                            step(i)
+                    hip_graph_upload(g)
+                    graphs[name].append((g, reps))
         except Exception as e:  # pragma: no cover - reported, then eager timing
             print(f"graph capture unavailable ({e!r}); timing eager launches", file=sys.stderr)
-            graph, use_graph = None, False
+            graphs, use_graph = {}, False
 
-    reps = max(1, args.steps // per_graph) if use_graph else 0
-    steps = reps * per_graph if use_graph else args.steps
-    warm_reps = max(1, args.warmup // per_graph) if use_graph else 0
-    if use_graph:
-        for _ in range(warm_reps):
-            graph.replay()
-    else:
-        for i in range(args.warmup):
-            step(i)
+    def run(name, idx):
+        if use_graph:
+            for g, reps in graphs[name]:
+                for _ in range(reps):
+                    g.replay()
+        else:
+            for i in idx:
+                step(i)
+
+    run("warm", warm_idx)
+    torch.cuda.synchronize()
+    flush_infinity_cache()
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole steps, synchronised on both sides
+    # ---- timed region: exactly K whole steps, synchronised on both sides
     t0 = time.perf_counter()
-    if use_graph:
-        for _ in range(reps):
-            graph.replay()
-    else:
-        for i in range(steps):
-            step(i)
+    run("timed", timed_idx)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    got_out = (out_c if args.path == "chunk" else out).cpu().numpy()
 
-    # ---- decode-call duration by HIP events on the launch stream.  Events cannot be
-    # recorded inside a captured graph here, so the calls are enqueued eagerly behind a
-    # GPU sleep long enough for the host to queue them all: they then run back to back
-    # (split-K kernel + LSE merge each, a new cache copy each) and one event pair
-    # brackets the whole run, so no event sits between two calls' kernels.
-    n_calls = min(per_graph, 512)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(5e7))
-    ev0.record()
-    for i in range(n_calls):
-        decode_call(caches[i % n_copies])
-    ev1.record()
-    torch.cuda.synchronize()
-    call_ms = [ev0.elapsed_time(ev1) / n_calls]
-    ms_per_step = (t1 - t0) * 1e3 / steps
+    # ---- decode-call duration by HIP events (split-K kernel + LSE merge each, a new cache
+    # copy each, back to back)
+    flush_infinity_cache()
+    n_calls = min(n_copies, 512)
+    dec_ms = time_calls(decode_call, caches, n_calls)
+    ms_per_step = (t1 - t0) * 1e3 / K
     token_heads = int(L.sum()) * w.num_kv_heads
     value = token_heads / (ms_per_step * 1e-3)
 
     alg = algorithmic_bytes(w, L)
-    dec_ms = float(np.mean(call_ms)) if call_ms else float("nan")
-    achieved = alg / (dec_ms * 1e-3) / 1e9 if call_ms else None
+    achieved = alg / (dec_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+            "frac": achieved / HBM_PEAK_GBS,
             # counters are recorded for the default route (tq_decode_step, MFMA kernel) only
             "traffic": recorded_traffic(w.name) if args.path == "step" and not args.formats else None,
             "kernel": {"step": "tq_decode_step", "fused": "tq_decode_attention_fused",
@@ -341,21 +547,39 @@ def main():
             + (" (decode_ref_kernel" if args.variant == 1 else " (decode_mfma_kernel")
             + " + combine_kernel)",
             "call_us": dec_ms * 1e3,
+            "calls_timed": n_calls,
             "algorithmic_bytes_per_call": alg}
+    exact = args.path != "chunk" and args.q_scale == 1.0 and not args.v_skip_threshold \
+        and not args.k_skip_threshold
     cpu, parity = None, None
+    codebooks = None
     if not args.no_cpu_baseline:
-        o_ref, cpu = cpu_baseline(w, seed, args.cpu_seconds)
-        # Exactness gate: the timed calls' output for sequence 0 (every cache copy holds the
-        # same tokens, so the last call's output is the step's) against the oracle's output
-        # of the same step, at the parity bars of the tests.  Only where the step is the
-        # oracle's: exact attention, unscaled queries, one query position.
-        if args.path != "chunk" and args.q_scale == 1.0 and not args.v_skip_threshold and not args.k_skip_threshold:
-            rel, mx = S.errors(out[0].cpu().numpy(), o_ref)
-            parity = {"sequence": 0, "rel_l2": rel, "max_abs": mx, "rel_l2_bound": 1e-3, "max_abs_bound": 5e-3,
-                      "ok": bool(rel <= 1e-3 and mx <= 5e-3)}
+        from tests.conftest import load_codebook
+        codebooks = {"turbo3": load_codebook("turbo3"), "turbo4": load_codebook("turbo4")}
+        cpu, o_ref = cpu_baseline(w, args.workload, formats, seed, args.cpu_seconds)
+        # Exactness gate: the timed steps' output for sequence 0 (every cache copy holds the
+        # same tokens, so the last step's output is the step's) against the oracle's output of
+        # the same step, at the parity bars of the tests.  Only where the step is the oracle's:
+        # exact attention, unscaled queries, one query position.
+        if exact:
+            parity = oracle_parity(master, w, 0, int(L[0]), k_list[0], v_list[0], q_np[0], got_out[0], o_ref=o_ref,
+                                   codebooks=codebooks)
+    per_workload = None
+    if not args.no_extra and args.workload == 1 and args.path == "step" and exact and not args.formats:
+        del caches, k_list, v_list
+        torch.cuda.empty_cache()
+        per_workload = {w.name: {"call_us": dec_ms * 1e3, "algorithmic_bytes_per_call": alg,
+                                 "achieved_GBs": achieved, "frac": achieved / HBM_PEAK_GBS,
+                                 "kv_token_heads_per_s": token_heads / (dec_ms * 1e-3),
+                                 "traffic": roof["traffic"], "parity": parity}}
+        for widx in EXTRA_WORKLOADS:
+            name, rec = extra_workload(widx, seed, not args.no_cpu_baseline, codebooks)
+            per_workload[name] = rec
+            print(f"bench.py: {name} {rec['call_us']:.1f} us per call, {rec['frac']:.3f} of 8 TB/s",
+                  file=sys.stderr, flush=True)
     line = {
-        "metric": METRIC, "value": value, "unit": "KV token-heads/s", "n_gpus": 1, "steps": steps,
-        "warmup": warm_reps * per_graph if use_graph else args.warmup, "ms_per_step": ms_per_step,
+        "metric": METRIC, "value": value, "unit": "KV token-heads/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u8 codes, f32 valu" if args.variant == 1 else "u8 codes, f16 mfma, f32 accumulate",
         "data": "synthetic (seeded; no model weights)",
@@ -369,10 +593,12 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": parity,
+        "per_workload": per_workload,
     }
     print(json.dumps(line), flush=True)
-    if parity is not None and not parity["ok"]:
-        print(f"bench.py: the timed output of sequence 0 is outside the parity bars: {parity}", file=sys.stderr)
+    bad = [p for p in [parity] + [r["parity"] for r in (per_workload or {}).values()] if p is not None and not p["ok"]]
+    if bad:
+        print(f"bench.py: outside the parity bars: {bad}", file=sys.stderr)
         sys.exit(1)
 
 

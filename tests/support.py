@@ -78,16 +78,38 @@ def oracle_on_bytes(cache, b, L, q_b, codebooks, seed=0):
 
 def oracle_dequant_bytes(cache, b, L, codebooks, seed=0):
     """K and V [Hkv, L, 128] (float64, original basis) of sequence b from the GPU-written bytes."""
+    return oracle_dequant_download(download_sequence(cache, b), cache.k_format, cache.v_format, L, codebooks, seed)
+
+
+def oracle_dequant_download(d, k_format, v_format, L, codebooks, seed=0):
+    """K and V [Hkv, L, 128] (float64, original basis) from bytes already downloaded by
+    download_sequence (no GPU access: safe to run in worker threads)."""
     from oracle import reference
-    d = download_sequence(cache, b)
-    kc, vc = reference.codes_from_library_layout(d.get("k_rec"), d["v_tiles"], cache.k_format, cache.v_format)
-    enc = {"v_f16": vc} if cache.v_format == "f16" else {"v_codes": vc, "v_norms": d["v_norms"]}
-    if cache.k_format == "f16":
+    kc, vc = reference.codes_from_library_layout(d.get("k_rec"), d["v_tiles"], k_format, v_format)
+    enc = {"v_f16": vc} if v_format == "f16" else {"v_codes": vc, "v_norms": d["v_norms"]}
+    if k_format == "f16":
         enc["k_f16"] = d["k_f16"]
     else:
         enc["k_codes"], enc["k_norms"] = kc, d["k_norms"]
-    return reference.dequant_sequence(enc, cache.k_format, cache.v_format, sign_vector(seed, "k"),
+    return reference.dequant_sequence(enc, k_format, v_format, sign_vector(seed, "k"),
                                       sign_vector(seed, "v"), codebooks, L)
+
+
+def oracle_errors_all_sequences(cache, L, q, got, codebooks, seed=0, workers=8):
+    """(rel-L2, max-abs) of every sequence's GPU output against the oracle on the GPU-written
+    bytes; the bytes are downloaded first, the oracle runs in worker threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import reference
+    downloads = [download_sequence(cache, b) for b in range(cache.batch)]
+
+    def one(b):
+        k_hat, v_hat = oracle_dequant_download(downloads[b], cache.k_format, cache.v_format, int(L[b]), codebooks,
+                                               seed)
+        return errors(got[b], reference.decode_sequence(q[b], k_hat, v_hat, int(L[b])))
+
+    with ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(one, range(cache.batch)))
 
 
 def oracle_end_to_end(w, k16, v16, L, q_b, codebooks, seed=0):

@@ -27,16 +27,36 @@ def test_algorithmic_bytes_follow_the_formats():
 
 
 def test_recorded_traffic_is_keyed_to_the_kernel_sources(tmp_path, monkeypatch):
-    """The committed counters are reported only while the decode/merge sources hash as recorded."""
+    """Recorded counters are reported only while the decode/merge sources and the split planner
+    hash as they did when the counters were taken."""
     sys.path.insert(0, ROOT)
     import bench
-    with open(bench.TRAFFIC_FILE) as f:
-        rec = json.load(f)
-    name = next(iter(rec["workloads"]))
-    assert rec["kernel_source_sha256"] == bench.kernel_source_hash()
-    assert bench.recorded_traffic(name) == rec["workloads"][name]["bytes_per_call"]
-    stale = dict(rec, kernel_source_sha256="0" * 64)
+    assert "quantized_kv_cache_decode_amd/csrc/api.hip" in bench.KERNEL_SOURCES      # the split plan
+    rec = {"kernel_source_sha256": bench.kernel_source_hash(),
+           "workloads": {"w": {"bytes_per_call": 12345}}}
     p = tmp_path / "traffic.json"
-    p.write_text(json.dumps(stale))
+    p.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
-    assert bench.recorded_traffic(name) is None
+    assert bench.recorded_traffic("w") == 12345
+    assert bench.recorded_traffic("other") is None
+    p.write_text(json.dumps(dict(rec, kernel_source_sha256="0" * 64)))
+    assert bench.recorded_traffic("w") is None
+
+
+def test_committed_traffic_record_names_its_sources():
+    """The committed record carries the source hash it was taken under (reported only while
+    that hash is current)."""
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        rec = json.load(f)
+    assert len(rec["kernel_source_sha256"]) == 64
+    for name, r in rec["workloads"].items():
+        assert r["bytes_per_call"] >= r["algorithmic_bytes"] * 0.9, name
+
+
+def test_bench_arguments_default_to_one_gpu_and_whole_counts():
+    sys.path.insert(0, ROOT)
+    import bench
+    a = bench.parse([])
+    assert a.gpus == 1 and a.workload == 1 and a.path == "step" and a.steps >= 1 and a.warmup >= 0
+    a = bench.parse(["--steps", "20", "--warmup", "5"])
+    assert (a.steps, a.warmup) == (20, 5)

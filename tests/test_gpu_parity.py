@@ -79,13 +79,15 @@ def _small_workloads():
         "c0": (get_workload(0), None),
         "c1": (get_workload(1), None),
         "c2": (get_workload(2), None),
+        # fp16 K + turbo3 V (turbo3-asym, the low-memory mix of mlxcel commit #376)
+        "c2t3": (S.scaled(get_workload(2), v_format="turbo3"), None),
         "c3s": (S.scaled(get_workload(3), batch=3, context=2048), None),
         "c4s": (S.scaled(get_workload(4), batch=6, context=None, ragged_range=(1, 3000)),
                 np.array([1, 31, 33, 2049, 700, 2999])),
     }
 
 
-@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3s", "c4s"])
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c2t3", "c3s", "c4s"])
 def test_encode_bit_exact(name, codebooks):
     w, lens = _small_workloads()[name]
     cache, k_list, v_list, L, _ = S.prefill_and_step(w, lengths=lens)
@@ -100,7 +102,7 @@ def test_encode_bit_exact(name, codebooks):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3s", "c4s"])
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c2t3", "c3s", "c4s"])
 def test_decode_parity(name, variant, codebooks):
     w, lens = _small_workloads()[name]
     cache, k_list, v_list, L, q = S.prefill_and_step(w, lengths=lens)
@@ -177,7 +179,7 @@ def test_workspace_reused_across_calls(variant, codebooks):
                        f"step {step} L={L}")
 
 
-@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3s", "c4s"])
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c2t3", "c3s", "c4s"])
 def test_fused_call_matches_separate_calls_bitwise(name):
     """tq_decode_attention_fused == tq_rotate_q + tq_decode_attention + tq_inverse_rotate_out,
     bit for bit (the same rotation routine and merge arithmetic run inside the fused kernels);
@@ -189,7 +191,7 @@ def test_fused_call_matches_separate_calls_bitwise(name):
     np.testing.assert_array_equal(fused.view(np.uint16), sep.view(np.uint16))
 
 
-@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3s", "c4s"])
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c2t3", "c3s", "c4s"])
 def test_decode_step_parity(name, codebooks):
     """tq_decode_step (append + attend in one call): the appended token's codes and norms are
     bit-exact, the lengths advance by one, and the output matches the oracle end to end and
@@ -235,7 +237,9 @@ def test_decode_step_sixteen_steps_gqa_4_over_2(codebooks):
 
 
 @pytest.mark.parametrize("group,k_format,v_format", [(1, "turbo4", "turbo3"), (16, "turbo3", "turbo4"),
-                                                     (7, "f16", "turbo4")])
+                                                     (7, "f16", "turbo4"), (1, "f16", "turbo3"),
+                                                     (4, "f16", "turbo3"), (7, "f16", "turbo3"),
+                                                     (16, "f16", "turbo3")])
 def test_decode_step_groups_formats_and_empty(group, k_format, v_format, codebooks):
     """The step at group sizes 1, 7 and 16, mixed formats and fp16 K, with a sequence whose
     first token the step appends (length 0 before it) and one ending on a tile boundary."""
@@ -280,10 +284,11 @@ def test_empty_and_single_token_sequences(variant, codebooks):
     np.testing.assert_allclose(got[0].astype(np.float64), np.repeat(v0, 2, axis=0), atol=2e-3, rtol=0)
 
 
-@pytest.mark.parametrize("group", [1, 16])
+@pytest.mark.parametrize("k_format", ["turbo4", "f16"])
+@pytest.mark.parametrize("group", [1, 4, 16])
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_group_size_extremes(group, variant, codebooks):
-    w = S.scaled(get_workload(0), num_q_heads=2 * group, num_kv_heads=2, k_format="turbo4", v_format="turbo3")
+def test_group_size_extremes(group, variant, k_format, codebooks):
+    w = S.scaled(get_workload(0), num_q_heads=2 * group, num_kv_heads=2, k_format=k_format, v_format="turbo3")
     cache, k_list, v_list, L, q = S.prefill_and_step(w, lengths=np.array([300]))
     got = S.gpu_decode(cache, q, variant=variant)
     S.assert_close(got[0], S.oracle_end_to_end(w, k_list[0], v_list[0], 300, q[0], codebooks), f"G={group}")
@@ -312,13 +317,14 @@ def test_appends_merge_into_partial_tiles(codebooks):
 
 # ----------------------------------------------------------------------------- full size
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("index", [1, 2, 3, 4])
 def test_full_size_sampled(index, codebooks):
     """Full-size workloads in the launch configuration the benchmark times (prefill, then one
-    tq_decode_step); codes of the sampled sequences are checked in full, outputs of the sampled
-    sequences against the oracle on the GPU bytes (codes equal the oracle's, so this is also
-    end to end)."""
+    tq_decode_step): the outputs of every sequence against the oracle on the GPU-written bytes;
+    codes and norms of the sampled sequences (the shortest and longest, or the first and last)
+    in full against the oracle's encode of the same rows, which makes the sampled outputs end
+    to end as well."""
     w = get_workload(index)
     _say(f"[full {w.name}] generating + encoding")
     cache, k_list, v_list, L, q, got = S.prefill_then_decode_step(w)
@@ -327,9 +333,11 @@ def test_full_size_sampled(index, codebooks):
         m, g, t = S.compare_codes(cache, b, k_list[b], v_list[b], int(L[b]), w, codebooks)
         _say(f"[full {w.name}] b={b} L={int(L[b])} code mismatches {m}/{t}, margin {g}")
         assert m <= g <= 1e-4 * t
-        rel, mx = S.assert_close(got[b], S.oracle_on_bytes(cache, b, int(L[b]), q[b], codebooks), f"b={b}")
-        _say(f"[full {w.name}] b={b} rel-L2 {rel:.2e} max-abs {mx:.2e}")
-    assert np.all(np.isfinite(got.astype(np.float32)))
+    errs = S.oracle_errors_all_sequences(cache, L, q, got, codebooks)
+    worst_rel, worst_abs = max(e[0] for e in errs), max(e[1] for e in errs)
+    _say(f"[full {w.name}] all {w.batch} sequences: worst rel-L2 {worst_rel:.2e} max-abs {worst_abs:.2e}")
+    for b, (rel, mx) in enumerate(errs):
+        assert rel <= S.REL_L2_TOL and mx <= S.MAX_ABS_TOL, f"b={b}: rel-L2 {rel:.3e} max-abs {mx:.3e}"
 
 
 @pytest.mark.timeout(600)
@@ -501,7 +509,8 @@ def _gpu_chunk(cache, q_np):
 
 @pytest.mark.parametrize("group,q_len,k_format,v_format", [
     (2, 3, "turbo3", "turbo3"), (4, 4, "turbo4", "turbo4"), (7, 2, "f16", "turbo4"), (1, 16, "turbo3", "turbo4"),
-    (8, 2, "turbo3", "turbo3")])
+    (8, 2, "turbo3", "turbo3"), (1, 5, "f16", "turbo3"), (4, 3, "f16", "turbo3"), (7, 2, "f16", "turbo3"),
+    (16, 1, "f16", "turbo3")])
 def test_chunk_decode_parity(group, q_len, k_format, v_format, codebooks):
     """Causal decode of a chunk of q_len positions per sequence against the oracle, with a
     sequence exactly q_len long, one whose chunk straddles a split boundary (129 tokens,

@@ -285,6 +285,15 @@ tq_status tq_inverse_rotate_out(const tq_cache* cache, const float* out_rot,
                                 int32_t num_q_heads, uint16_t* out, void* stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
+/* Measurement aid, not a step of the method: a plain streaming read of `bytes`
+ * bytes of device memory at `src` (16-byte aligned; bytes a positive multiple
+ * of 16), the practical HBM read ceiling that the decode kernel's achieved
+ * bandwidth is compared with.  `blocks` work groups of 256 lanes (1..2^20) read
+ * 16-byte words in a grid-stride loop; work group i writes the XOR of the words
+ * it read to sums[i] (device uint32 [blocks]), so the XOR of all of sums is the
+ * XOR of the buffer's 32-bit words.  Invalid arguments give TQ_EINVAL. */
+tq_status tq_stream_read(const void* src, size_t bytes, uint32_t* sums, int32_t blocks, void* stream);
+
 const char* tq_last_error(void);
 
 /* Library version string. */

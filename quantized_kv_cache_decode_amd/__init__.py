@@ -16,4 +16,5 @@ from .binding import (  # noqa: F401
     tq_encode_append,
     tq_inverse_rotate_out,
     tq_rotate_q,
+    tq_stream_read,
 )

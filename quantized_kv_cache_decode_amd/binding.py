@@ -23,7 +23,7 @@ V_TILE_BYTES = {"turbo3": 1536, "turbo4": 2048, "f16": 8192}
 EXPORTED = (
     "tq_encode_append", "tq_rotate_q", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_decode_attention_variant", "tq_decode_attention_fused", "tq_decode_chunk_fused", "tq_decode_step",
-    "tq_inverse_rotate_out",
+    "tq_inverse_rotate_out", "tq_stream_read",
     "tq_last_error", "tq_version",
 )
 
@@ -68,11 +68,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tq_decode_step.argtypes = [cp, P, P, P, P, I32, I32, F32, P, P, SZ, P]
     lib.tq_decode_chunk_fused.argtypes = [cp, P, P, I32, I32, I32, F32, P, P, SZ, P]
     lib.tq_inverse_rotate_out.argtypes = [cp, P, I32, P, P]
+    lib.tq_stream_read.argtypes = [P, SZ, P, I32, P]
     lib.tq_last_error.restype = ctypes.c_char_p
     lib.tq_version.restype = ctypes.c_char_p
     for name in ("tq_encode_append", "tq_rotate_q", "tq_decode_attention", "tq_decode_attention_variant",
                  "tq_decode_attention_fused", "tq_decode_chunk_fused", "tq_decode_step",
-                 "tq_inverse_rotate_out"):
+                 "tq_inverse_rotate_out", "tq_stream_read"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -347,3 +348,17 @@ def tq_inverse_rotate_out(cache: Cache, out_rot, out, stream=None):
     _on_gpu(cache, ("out_rot", out_rot), ("out", out))
     _check(load_library().tq_inverse_rotate_out(cache.desc, _ptr(out_rot), int(out_rot.shape[1]), _ptr(out),
                                                 _stream(stream)))
+
+
+def tq_stream_read(src, sums, stream=None):
+    """Measurement aid: stream-read every byte of the contiguous device tensor `src`; work
+    group i writes the XOR of the 32-bit words it read to sums[i] (device uint32/int32 tensor,
+    one entry per work group)."""
+    import torch
+    if not isinstance(src, torch.Tensor) or not src.is_contiguous() or not src.is_cuda:
+        raise ValueError("src must be a contiguous device tensor")
+    if not isinstance(sums, torch.Tensor) or sums.dtype not in (torch.int32, torch.uint32) or sums.dim() != 1 \
+            or not sums.is_contiguous() or sums.device != src.device:
+        raise ValueError("sums must be a contiguous 1-D int32 tensor on src's device")
+    _check(load_library().tq_stream_read(_ptr(src), int(src.numel() * src.element_size()), _ptr(sums),
+                                         int(sums.numel()), _stream(stream)))

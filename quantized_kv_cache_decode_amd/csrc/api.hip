@@ -391,6 +391,14 @@ tq_status tq_decode_attention(const tq_cache* cache, const int32_t* seq_lens_hos
                                      0, stream);
 }
 
+tq_status tq_stream_read(const void* src, size_t bytes, uint32_t* sums, int32_t blocks, void* stream) {
+  if (!src || !sums) return fail(TQ_EINVAL, "src / sums is NULL");
+  if (bytes == 0 || bytes % 16) return fail(TQ_EINVAL, "bytes %zu must be a positive multiple of 16", bytes);
+  if (blocks < 1 || blocks > (1 << 20)) return fail(TQ_EINVAL, "blocks %d outside [1, 2^20]", blocks);
+  return hip_status(tq::launch_stream_read(src, bytes, sums, blocks, static_cast<hipStream_t>(stream)),
+                    "stream_read launch");
+}
+
 tq_status tq_inverse_rotate_out(const tq_cache* cache, const float* out_rot, int32_t num_q_heads, uint16_t* out,
                                 void* stream) {
   tq_status st = check_cache(cache);

@@ -100,4 +100,7 @@ hipError_t launch_decode_reference(const DecodeArgs& a, const SeqLens& lens, int
 hipError_t launch_decode_mfma(const DecodeArgs& a, const SeqLens& lens, int nb, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, const SeqLens& lens, int nb, hipStream_t stream);
 
+// ---- measurement aid: plain streaming read (one XOR checksum word per work group)
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sums, int blocks, hipStream_t stream);
+
 }  // namespace tq

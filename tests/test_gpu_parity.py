@@ -586,3 +586,21 @@ def test_more_sequences_than_one_launch(variant, codebooks):
         assert m == 0
         S.assert_close(got[b], S.oracle_end_to_end(w, k_list[b], v_list[b], int(L[b]), q[b], codebooks),
                        f"{variant} b={b} L={int(L[b])}")
+
+
+# ----------------------------------------------------------------------------- measurement aid
+
+@pytest.mark.parametrize("n_bytes,blocks", [(16, 1), (4096, 3), ((1 << 24) + 48, 1024)])
+def test_stream_read_reads_every_word(n_bytes, blocks):
+    """The streaming-read kernel behind the HBM read ceiling reads every 16-byte word once:
+    the XOR of its per-work-group checksums equals the XOR of the buffer's 32-bit words."""
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    words = np.random.default_rng(3).integers(0, 2 ** 32, n_bytes // 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    sums = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    tq.tq_stream_read(src, sums)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sums.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)

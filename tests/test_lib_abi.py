@@ -234,3 +234,14 @@ def test_f16_v_only_with_f16_k(lib):
     a, p = _lens(10, 10)
     st = lib.tq_decode_attention_variant(ctypes.byref(ok), p, q, 4, ctypes.c_float(0.1), q, q, 10 ** 9, 1, None)
     assert st == binding.TQ_EUNSUPPORTED and "reference" in _err(lib)
+
+
+def test_stream_read_checks(lib):
+    """The streaming-read measurement aid validates before launching (no GPU needed)."""
+    p = ctypes.c_void_p(0x10000)
+    assert lib.tq_stream_read(None, 1024, p, 4, None) == binding.TQ_EINVAL
+    assert lib.tq_stream_read(p, 1024, None, 4, None) == binding.TQ_EINVAL
+    assert lib.tq_stream_read(p, 0, p, 4, None) == binding.TQ_EINVAL
+    assert lib.tq_stream_read(p, 1000, p, 4, None) == binding.TQ_EINVAL
+    assert lib.tq_stream_read(p, 1024, p, 0, None) == binding.TQ_EINVAL
+    assert lib.tq_stream_read(p, 1024, p, (1 << 20) + 1, None) == binding.TQ_EINVAL

@@ -277,6 +277,28 @@ tq_status tq_decode_step(const tq_cache* cache, const int32_t* seq_lens_host,
                          uint16_t* out, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc -- and so
+ * cannot hand in a workspace: tq_decode_step with the split partials kept in
+ * a device array of the library's own, TQ_NOALLOC_SCRATCH_BYTES (64 MiB) per
+ * GPU, held from the first call on that GPU until the process ends.  Same
+ * kernels, same plan, same output and cache contents as tq_decode_step.
+ *   Arguments as for tq_decode_step, without the workspace.  `stream` must
+ *   belong to the calling thread's current device.
+ *   Calls whose partials need more than TQ_NOALLOC_SCRATCH_BYTES (what
+ *   tq_decode_workspace_size returns) give TQ_EWORKSPACE before anything is
+ *   enqueued.  No hipMalloc or hipFree is made; the first call on a device
+ *   resolves the array's device address once (hipGetSymbolAddress), and a
+ *   failure there gives TQ_EHIP.
+ *   Every call on one GPU shares that GPU's array and leaves its partials
+ *   there; nothing in it needs initial contents.  Calls that overlap on one
+ *   GPU (several streams or threads at once) race on it: serialise them. */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+tq_status tq_decode_step_noalloc(const tq_cache* cache, const int32_t* seq_lens_host,
+                                 const void* k_new, const void* v_new, const void* q,
+                                 int32_t q_is_fp32, int32_t num_q_heads, float scale,
+                                 uint16_t* out, void* stream);
+
 /* Back to the original basis: out = s_V * H (out_rot) / sqrt(128), rounded to
  * nearest-even fp16 (mlxcel PR #369, "Change": only the small [B, Hq, D]
  * output is inverse-rotated).
@@ -284,7 +306,6 @@ tq_status tq_decode_step(const tq_cache* cache, const int32_t* seq_lens_host,
 tq_status tq_inverse_rotate_out(const tq_cache* cache, const float* out_rot,
                                 int32_t num_q_heads, uint16_t* out, void* stream);
 
-/* Message for the calling thread's last non-OK status ("" if none). */
 /* Measurement aid, not a step of the method: a plain streaming read of `bytes`
  * bytes of device memory at `src` (16-byte aligned; bytes a positive multiple
  * of 16), the practical HBM read ceiling that the decode kernel's achieved
@@ -294,6 +315,7 @@ tq_status tq_inverse_rotate_out(const tq_cache* cache, const float* out_rot,
  * XOR of the buffer's 32-bit words.  Invalid arguments give TQ_EINVAL. */
 tq_status tq_stream_read(const void* src, size_t bytes, uint32_t* sums, int32_t blocks, void* stream);
 
+/* Message for the calling thread's last non-OK status ("" if none). */
 const char* tq_last_error(void);
 
 /* Library version string. */

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     tq_decode_attention_fused,
     tq_decode_chunk_fused,
     tq_decode_step,
+    tq_decode_step_noalloc,
     tq_decode_workspace_size,
     tq_encode_append,
     tq_inverse_rotate_out,

@@ -20,9 +20,11 @@ TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_ECAPACITY, TQ_EWORKSPACE, TQ_EHIP = range(
 TQ_FMT = {"f16": 0, "turbo3": 3, "turbo4": 4}
 K_RECORD_BYTES = {"turbo3": 48, "turbo4": 64}
 V_TILE_BYTES = {"turbo3": 1536, "turbo4": 2048, "f16": 8192}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # TQ_NOALLOC_SCRATCH_BYTES: the no-allocation step's partials, per GPU
 EXPORTED = (
     "tq_encode_append", "tq_rotate_q", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_decode_attention_variant", "tq_decode_attention_fused", "tq_decode_chunk_fused", "tq_decode_step",
+    "tq_decode_step_noalloc",
     "tq_inverse_rotate_out", "tq_stream_read",
     "tq_last_error", "tq_version",
 )
@@ -66,13 +68,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tq_decode_attention_variant.argtypes = [cp, P, P, I32, F32, P, P, SZ, I32, P]
     lib.tq_decode_attention_fused.argtypes = [cp, P, P, I32, I32, F32, P, P, SZ, P]
     lib.tq_decode_step.argtypes = [cp, P, P, P, P, I32, I32, F32, P, P, SZ, P]
+    lib.tq_decode_step_noalloc.argtypes = [cp, P, P, P, P, I32, I32, F32, P, P]
     lib.tq_decode_chunk_fused.argtypes = [cp, P, P, I32, I32, I32, F32, P, P, SZ, P]
     lib.tq_inverse_rotate_out.argtypes = [cp, P, I32, P, P]
     lib.tq_stream_read.argtypes = [P, SZ, P, I32, P]
     lib.tq_last_error.restype = ctypes.c_char_p
     lib.tq_version.restype = ctypes.c_char_p
     for name in ("tq_encode_append", "tq_rotate_q", "tq_decode_attention", "tq_decode_attention_variant",
-                 "tq_decode_attention_fused", "tq_decode_chunk_fused", "tq_decode_step",
+                 "tq_decode_attention_fused", "tq_decode_chunk_fused", "tq_decode_step", "tq_decode_step_noalloc",
                  "tq_inverse_rotate_out", "tq_stream_read"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
@@ -334,6 +337,27 @@ def tq_decode_step(cache: Cache, k_new, v_new, q, scale, out, workspace, seq_len
         cache.desc, p, _ptr(k_new), _ptr(v_new), _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]),
         float(scale), _ptr(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
         _stream(stream)))
+    cache.lengths = arr + 1
+
+
+def tq_decode_step_noalloc(cache: Cache, k_new, v_new, q, scale, out, seq_lens_host=None, stream=None):
+    """tq_decode_step without a workspace, for callers that cannot allocate: the split partials
+    live in the library's own per-GPU array (NOALLOC_SCRATCH_BYTES); calls that overlap on one
+    GPU race on it."""
+    import torch
+    kv_shape = (cache.batch, cache.num_kv_heads, 1, 128)
+    _tensor(k_new, "k_new", kv_shape, (torch.float16,))
+    _tensor(v_new, "v_new", kv_shape, (torch.float16,))
+    shape = _q_shape(cache, q)
+    if len(shape) != 3:
+        raise ValueError("q must be [B, Hq, 128]")
+    _tensor(q, "q", shape, (torch.float16, torch.float32))
+    _tensor(out, "out", shape, (torch.float16,))
+    arr, p = _host_i32(cache.lengths if seq_lens_host is None else seq_lens_host, cache.batch)
+    _on_gpu(cache, ("k_new", k_new), ("v_new", v_new), ("q", q), ("out", out))
+    _check(load_library().tq_decode_step_noalloc(
+        cache.desc, p, _ptr(k_new), _ptr(v_new), _ptr(q), int(q.dtype == torch.float32), int(q.shape[1]),
+        float(scale), _ptr(out), _stream(stream)))
     cache.lengths = arr + 1
 
 

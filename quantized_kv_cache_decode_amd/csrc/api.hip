@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/tqattn.h"
 #include "tq_device.h"
@@ -351,6 +352,69 @@ tq_status tq_decode_chunk_fused(const tq_cache* cache, const int32_t* seq_lens_h
   return launch_decode_and_merge(cache, seq_lens_host, a, 0, static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
+// Split partials of tq_decode_step_noalloc: one copy per GPU (each device that loads
+// this code object holds its own), resolved to a device address once per device.
+static __device__ __align__(256) unsigned char scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`.  Host code uses only this address: the
+// array's name is a host-side stand-in, not a device address.
+tq_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TQ_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(TQ_EHIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TQ_OK;
+}
+
+// tq_decode_step's body after the workspace is known (validated by decode_setup).
+tq_status decode_step_launch(const tq_cache* cache, const int32_t* seq_lens_host, const void* k_new,
+                             const void* v_new, const void* q, int32_t q_is_fp32, tq::DecodeArgs& a, uint16_t* out,
+                             void* stream);
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_decode_step_noalloc(const tq_cache* cache, const int32_t* seq_lens_host, const void* k_new,
+                                 const void* v_new, const void* q, int32_t q_is_fp32, int32_t num_q_heads,
+                                 float scale, uint16_t* out, void* stream) {
+  // Everything is checked on the host before the device is touched, the size against the
+  // array included (a non-NULL stand-in passes decode_setup's workspace check).
+  tq_status st = check_cache(cache);
+  if (st != TQ_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != TQ_OK) return st;
+  if ((st = check_lengths(cache, seq_lens_host, 1)) != TQ_OK) return st;
+  const size_t need = workspace_bytes(cache, num_q_heads,
+                                      make_plan(cache, seq_lens_host, num_q_heads / cache->num_kv_heads));
+  if (need > TQ_NOALLOC_SCRATCH_BYTES)
+    return fail(TQ_EWORKSPACE, "the call's partials need %zu bytes, more than the %zu bytes of the no-allocation "
+                "scratch array", need, (size_t)TQ_NOALLOC_SCRATCH_BYTES);
+  if (!k_new || !v_new || !q || !out) return fail(TQ_EINVAL, "k_new / v_new / q / out is NULL");
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws)) != TQ_OK) return st;
+  tq::DecodeArgs a;
+  if ((st = decode_setup(cache, seq_lens_host, num_q_heads, scale, ws, TQ_NOALLOC_SCRATCH_BYTES, a)) != TQ_OK)
+    return st;
+  return decode_step_launch(cache, seq_lens_host, k_new, v_new, q, q_is_fp32, a, out, stream);
+}
+
 tq_status tq_decode_step(const tq_cache* cache, const int32_t* seq_lens_host, const void* k_new, const void* v_new,
                          const void* q, int32_t q_is_fp32, int32_t num_q_heads, float scale, uint16_t* out,
                          void* workspace, size_t ws_bytes, void* stream) {
@@ -359,6 +423,16 @@ tq_status tq_decode_step(const tq_cache* cache, const int32_t* seq_lens_host, co
   if (st != TQ_OK) return st;
   if ((st = check_lengths(cache, seq_lens_host, 1)) != TQ_OK) return st;  // room for the new token
   if (!k_new || !v_new || !q || !out) return fail(TQ_EINVAL, "k_new / v_new / q / out is NULL");
+  return decode_step_launch(cache, seq_lens_host, k_new, v_new, q, q_is_fp32, a, out, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+tq_status decode_step_launch(const tq_cache* cache, const int32_t* seq_lens_host, const void* k_new,
+                             const void* v_new, const void* q, int32_t q_is_fp32, tq::DecodeArgs& a, uint16_t* out,
+                             void* stream) {
   a.q_in = q;
   a.q_fp32 = q_is_fp32 != 0;
   a.q_rotate = cache->k_format != TQ_FMT_F16;
@@ -383,6 +457,10 @@ tq_status tq_decode_step(const tq_cache* cache, const int32_t* seq_lens_host, co
   e.v_cb = cache->v_codebook;
   return launch_decode_and_merge(cache, seq_lens_host, a, 0, static_cast<hipStream_t>(stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 tq_status tq_decode_attention(const tq_cache* cache, const int32_t* seq_lens_host, const float* q_rot,
                               int32_t num_q_heads, float scale, float* out_rot, void* workspace, size_t ws_bytes,

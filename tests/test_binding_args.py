@@ -126,3 +126,12 @@ def test_decode_step_rejects(cache, k_new, q, out, match):
 def test_inverse_rotate_rejects(cache, out_rot, out, match):
     with pytest.raises(ValueError, match=match):
         tq.tq_inverse_rotate_out(cache, out_rot, out)
+
+
+def test_decode_step_noalloc_rejects(cache):
+    with pytest.raises(ValueError, match="v_new has shape"):
+        tq.tq_decode_step_noalloc(cache, f16(B, HKV, 1, 128), f16(B, HKV, 2, 128), f16(B, HQ, 128), 0.1,
+                                  f16(B, HQ, 128))
+    with pytest.raises(ValueError, match="not on a GPU"):
+        tq.tq_decode_step_noalloc(cache, f16(B, HKV, 1, 128), f16(B, HKV, 1, 128), f16(B, HQ, 128), 0.1,
+                                  f16(B, HQ, 128))

@@ -245,3 +245,25 @@ def test_stream_read_checks(lib):
     assert lib.tq_stream_read(p, 1000, p, 4, None) == binding.TQ_EINVAL
     assert lib.tq_stream_read(p, 1024, p, 0, None) == binding.TQ_EINVAL
     assert lib.tq_stream_read(p, 1024, p, (1 << 20) + 1, None) == binding.TQ_EINVAL
+
+
+def test_noalloc_step_checks_before_touching_the_device(lib):
+    """The no-allocation step rejects, on the host, calls whose partials exceed its per-GPU
+    array (1024 x 8 rows of 2 slots x 16 heads x 520 bytes = 136 MB > 64 MiB), full caches
+    and NULL pointers -- no device call is made on these paths."""
+    q = ctypes.c_void_p(0x20000)
+    d = _desc(batch=1024, num_kv_heads=8, capacity=32)
+    a, p = _lens(*([10] * 1024))
+    n = lib.tq_decode_workspace_size(ctypes.byref(d), 128, p)
+    assert n > binding.NOALLOC_SCRATCH_BYTES
+    st = lib.tq_decode_step_noalloc(ctypes.byref(d), p, q, q, q, 0, 128, ctypes.c_float(0.1), q, None)
+    assert st == binding.TQ_EWORKSPACE and "scratch" in _err(lib)
+    d = _desc()
+    a, p = _lens(64, 3)
+    assert lib.tq_decode_step_noalloc(ctypes.byref(d), p, q, q, q, 0, 4, ctypes.c_float(0.1), q, None) == \
+        binding.TQ_ECAPACITY
+    a, p = _lens(5, 3)
+    assert lib.tq_decode_step_noalloc(ctypes.byref(d), p, q, ctypes.c_void_p(0), q, 0, 4, ctypes.c_float(0.1), q,
+                                      None) == binding.TQ_EINVAL
+    assert lib.tq_decode_step_noalloc(ctypes.byref(d), p, q, q, q, 0, 3, ctypes.c_float(0.1), q, None) == \
+        binding.TQ_EINVAL

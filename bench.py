@@ -309,16 +309,33 @@ def hip_graph_upload(graph):
 def time_calls(call, caches, n_calls):
     """Average duration (ms) of n_calls back-to-back calls, one HIP event pair on the launch
     stream around them all.  Events cannot be recorded inside a captured graph here, so the
-    calls are enqueued eagerly behind a GPU sleep long enough for the host to queue them."""
+    calls are enqueued eagerly behind a GPU sleep; the sleep is checked to outlast the host's
+    enqueueing (else the GPU would wait for the host between calls and the figure would be the
+    host's), and lengthened until it does."""
     import torch
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(5e7))
-    ev0.record()
-    for i in range(n_calls):
-        call(caches[i % len(caches)])
-    ev1.record()
-    torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / n_calls
+    cycles = int(1e8)
+    for _ in range(4):
+        es, e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        es.record()
+        torch.cuda._sleep(cycles)
+        e0.record()
+        h0 = time.perf_counter()
+        for i in range(n_calls):
+            call(caches[i % len(caches)])
+        host_ms = (time.perf_counter() - h0) * 1e3
+        e1.record()
+        torch.cuda.synchronize()
+        if es.elapsed_time(e0) > 1.2 * host_ms:
+            return e0.elapsed_time(e1) / n_calls
+        cycles *= 4
+    raise RuntimeError(f"the GPU sleep never outlasted the host's enqueueing of {n_calls} calls ({host_ms:.1f} ms)")
+
+
+def calls_to_time(n_copies):
+    """Back-to-back calls in one event-timed run: at least 8, at most 192 (more would fill the
+    launch queue while the GPU sleeps, and the host would wait for the GPU), and no more than
+    the copies where there are enough (a copy comes back only after >= 1 GiB of other copies)."""
+    return max(8, min(192, 64 * n_copies))
 
 
 def flush_infinity_cache():
@@ -329,6 +346,34 @@ def flush_infinity_cache():
     a.fill_(1.0)
     b = a.clone()
     del a, b
+
+
+def stream_read_ceiling(gib=1.0):
+    """The practical HBM read ceiling on this GPU: the library's plain streaming-read kernel
+    (tq_stream_read) over a 1 GiB buffer at several grid sizes, 10 timed passes each; the
+    best rate in GB/s."""
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    n = int(gib * (1 << 30)) // 16 * 16
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    best = (0.0, 0)
+    for blocks in (8192, 32768, 131072):
+        sums = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+        for _ in range(2):
+            tq.tq_stream_read(src, sums)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            tq.tq_stream_read(src, sums)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = n / (e0.elapsed_time(e1) / 10) / 1e6
+        best = max(best, (gbs, blocks))
+    del src
+    torch.cuda.empty_cache()
+    return {"kernel": "stream_read_kernel (tq_stream_read)", "bytes": n, "best_blocks": best[1],
+            "achieved": best[0], "unit": "GB/s", "frac_of_peak": best[0] / HBM_PEAK_GBS}
 
 
 def setup_copies(w, seed, copies_gib, min_copies=1):
@@ -342,7 +387,7 @@ def setup_copies(w, seed, copies_gib, min_copies=1):
     return caches, k_list, v_list, L, q_np
 
 
-def extra_workload(widx, seed, with_oracle, codebooks):
+def extra_workload(widx, seed, with_oracle, codebooks, ceiling_gbs):
     """Call timing and parity of tq_decode_step on another workload (not the timed steps)."""
     import torch
 
@@ -363,13 +408,14 @@ def extra_workload(widx, seed, with_oracle, codebooks):
 
     call(caches[0])
     torch.cuda.synchronize()
-    n_calls = max(8, min(256, 64 * len(caches)))
+    n_calls = calls_to_time(len(caches))
     flush_infinity_cache()
     call_ms = time_calls(call, caches, n_calls)
     alg = algorithmic_bytes(w, L)
     achieved = alg / (call_ms * 1e-3) / 1e9
     rec = {"call_us": call_ms * 1e3, "calls_timed": n_calls, "cache_copies": len(caches),
            "algorithmic_bytes_per_call": alg, "achieved_GBs": achieved, "frac": achieved / HBM_PEAK_GBS,
+           "frac_of_read_ceiling": achieved / ceiling_gbs,
            "kv_token_heads_per_s": int(L.sum()) * w.num_kv_heads / (call_ms * 1e-3),
            "traffic": recorded_traffic(w.name), "parity": None}
     if with_oracle:
@@ -530,7 +576,7 @@ def main(argv=None):
     # ---- decode-call duration by HIP events (split-K kernel + LSE merge each, a new cache
     # copy each, back to back)
     flush_infinity_cache()
-    n_calls = min(n_copies, 512)
+    n_calls = calls_to_time(n_copies)
     dec_ms = time_calls(decode_call, caches, n_calls)
     ms_per_step = (t1 - t0) * 1e3 / K
     token_heads = int(L.sum()) * w.num_kv_heads
@@ -538,8 +584,10 @@ def main(argv=None):
 
     alg = algorithmic_bytes(w, L)
     achieved = alg / (dec_ms * 1e-3) / 1e9
+    ceiling = stream_read_ceiling()
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
+            "read_ceiling": ceiling, "frac_of_read_ceiling": achieved / ceiling["achieved"],
             # counters are recorded for the default route (tq_decode_step, MFMA kernel) only
             "traffic": recorded_traffic(w.name) if args.path == "step" and not args.formats else None,
             "kernel": {"step": "tq_decode_step", "fused": "tq_decode_attention_fused",
@@ -570,10 +618,11 @@ def main(argv=None):
         torch.cuda.empty_cache()
         per_workload = {w.name: {"call_us": dec_ms * 1e3, "algorithmic_bytes_per_call": alg,
                                  "achieved_GBs": achieved, "frac": achieved / HBM_PEAK_GBS,
+                                 "frac_of_read_ceiling": achieved / ceiling["achieved"],
                                  "kv_token_heads_per_s": token_heads / (dec_ms * 1e-3),
                                  "traffic": roof["traffic"], "parity": parity}}
         for widx in EXTRA_WORKLOADS:
-            name, rec = extra_workload(widx, seed, not args.no_cpu_baseline, codebooks)
+            name, rec = extra_workload(widx, seed, not args.no_cpu_baseline, codebooks, ceiling["achieved"])
             per_workload[name] = rec
             print(f"bench.py: {name} {rec['call_us']:.1f} us per call, {rec['frac']:.3f} of 8 TB/s",
                   file=sys.stderr, flush=True)

@@ -1,9 +1,11 @@
 // Measurement aid, not a step of the decode path: a plain streaming read of a
 // device buffer, the practical HBM read ceiling the decode kernel's achieved
 // bandwidth is set against.  Every lane reads 16-byte words in a grid-stride
-// loop (four independent loads in flight per lane per round) and folds them
-// into an XOR checksum; each work group writes one checksum word, so the
-// loads cannot be dropped and the writes are negligible.
+// loop (four independent non-temporal loads in flight per lane per round: each
+// byte is read once, and on this chip that reads faster than cached loads at
+// the same occupancy) and folds them into an XOR checksum; each work group
+// writes one checksum word, so the loads cannot be dropped and the writes are
+// negligible.
 #include "tq_device.h"
 #include "tq_launch.h"
 
@@ -16,9 +18,12 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4
                                                                      uint32_t* __restrict__ sums) {
   const size_t stride = size_t(gridDim.x) * kStreamThreads;
   size_t i = size_t(blockIdx.x) * kStreamThreads + threadIdx.x;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
   uint32_t acc = 0;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    const u32x4 a = __builtin_nontemporal_load(s4 + i), b = __builtin_nontemporal_load(s4 + i + stride),
+                c = __builtin_nontemporal_load(s4 + i + 2 * stride), d = __builtin_nontemporal_load(s4 + i + 3 * stride);
     acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
   }
   for (; i < n16; i += stride) {

@@ -5,14 +5,23 @@
 // the group norm).
 //
 // Per 128-element row x (fp16), held by a 16-lane group (lane j: elements 8j..8j+7):
-//   norm  n = RNE_fp16(sqrt(sum x_i^2)) computed exactly: each |x_i| * 2^24 is
-//         an integer below 2^40; its square is split in 20-bit halves whose sums
-//         fit in u64, recombined in a u128, and the fp16 rounding decision is an
-//         integer comparison (4 S vs q^2 (2k+1)^2).
-//   y     = H (s * x) / sqrt(128): butterflies in binary64 (exact: fp16 terms
-//         are multiples of 2^-24 below 2^16), then one IEEE division.
-//   idx_i = #{j : y_i > n * beta_j}, beta_j = midpoints of adjacent fp16 codebook
-//         entries (n * beta_j is exact in binary64).
+//   norm  n = RNE_fp16(sqrt(sum x_i^2)), bit-exact: the sum of squares is taken in
+//         binary64 (every square is exact; 11 roundings at most along any path of
+//         the 16-lane sum), so sqrt is known to a relative 2^-49; the fp16 rounding
+//         is decided from it unless it lies within 2^-45 of a rounding midpoint, in
+//         which case (ties included) the exact integer method decides: each
+//         |x_i| * 2^24 is an integer below 2^40, its square split in 20-bit halves
+//         whose sums fit in u64, recombined in a u128, and the rounding decision is
+//         an integer comparison (4 S vs q^2 (2k+1)^2).
+//   yhat  = H (s * x): butterflies in binary64, exact (fp16 terms are multiples of
+//         2^-24 below 2^16).
+//   idx_i = #{j : y_i > n * beta_j} with y_i = yhat_i / sqrt(128) and beta_j the
+//         midpoints of adjacent fp16 codebook entries, decided as yhat_i against
+//         the thresholds n * beta_j * sqrt(128) in binary64, and, since the codebook
+//         is symmetric (c[K-1-i] = -c[i], so beta is too, with 0 in the middle), as
+//         |yhat_i| against the positive half of them.  This differs from dividing
+//         first only where y_i is within a few ulps of a threshold -- inside the
+//         1e-5 boundary margin the parity checks excuse.
 #pragma once
 
 #include "tq_device.h"
@@ -58,13 +67,26 @@ __device__ __forceinline__ void load_thresholds(const uint16_t* cb, double (&bet
   for (int i = 0; i < K - 1; ++i) beta[i] = 0.5 * (double(c[i]) + double(c[i + 1]));
 }
 
-// Encode one 128-element row held by a 16-lane group (lane j: elements 8j..8j+7,
-// fp16 bits in w4, sign flips in sg).  Returns the fp16 norm bits (the same in all
-// 16 lanes) and this lane's 8 codes.  All 16 lanes of the group execute it together.
-template <int FMT>
-__device__ __forceinline__ uint16_t encode_row(const uint32_t (&w4)[4], const float (&sg)[8],
-                                      const double (&beta)[levels(FMT) - 1], int j, uint8_t (&code)[8]) {
-  double x[8];
+// fp16 bits of RNE(sqrt(ss)), ss a binary64 sum of squares whose square root is
+// within a relative 2^-49 of the exact norm; 0xffff when that cannot decide the
+// rounding (within 2^-45 of a rounding midpoint, ties included).  Saturates at 65504.
+__device__ __forceinline__ uint32_t fast_norm_fp16(double ss) {
+  if (ss == 0.0) return 0;
+  const double r = sqrt(ss);
+  if (r >= 65504.0) return 0x7bff;                // everything from 65504 up gives 65504
+  const int e = ilogb(r);
+  const int qe = (e < -14 ? -14 : e) - 10;        // fp16 spacing 2^qe at r (2^-24 below 2^-14)
+  const double k = ldexp(r, -qe);                 // r in units of the spacing (exact)
+  const double fk = floor(k);
+  const double frac = k - fk;                     // exact
+  if (fabs(frac - 0.5) <= k * 0x1p-45) return 0xffff;
+  const double kr = frac > 0.5 ? fk + 1.0 : fk;
+  return __half_as_ushort(__float2half_rn(float(ldexp(kr, qe))));  // an fp16 value: exact
+}
+
+// The exact norm (integer method) of a row held by a 16-lane group; every lane of
+// the group must execute it.
+__device__ __noinline__ uint16_t exact_row_norm_fp16(const uint32_t (&w4)[4]) {
   uint64_t sA = 0, sB = 0, sC = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -74,13 +96,37 @@ __device__ __forceinline__ uint16_t encode_row(const uint32_t (&w4)[4], const fl
     sA += mh * mh;
     sB += mh * ml;
     sC += ml * ml;
-    x[e] = xv * double(sg[e]);
   }
   auto sum_stage = [&](auto m_c) {
     constexpr int M = decltype(m_c)::value;
     sA += xor_lane16<M>(sA);
     sB += xor_lane16<M>(sB);
     sC += xor_lane16<M>(sC);
+  };
+  sum_stage(std::integral_constant<int, 1>{});
+  sum_stage(std::integral_constant<int, 2>{});
+  sum_stage(std::integral_constant<int, 4>{});
+  sum_stage(std::integral_constant<int, 8>{});
+  return exact_norm_fp16(sA, sB, sC);
+}
+
+// Encode one 128-element row held by a 16-lane group (lane j: elements 8j..8j+7,
+// fp16 bits in w4, sign flips in sg).  Returns the fp16 norm bits (the same in all
+// 16 lanes) and this lane's 8 codes.  All 16 lanes of the group execute it together.
+template <int FMT>
+__device__ __forceinline__ uint16_t encode_row(const uint32_t (&w4)[4], const float (&sg)[8],
+                                      const double (&beta)[levels(FMT) - 1], int j, uint8_t (&code)[8]) {
+  double x[8];
+  double ss = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double xv = double(half_bits_to_float(uint16_t(w4[e >> 1] >> (16 * (e & 1)))));
+    ss = fma(xv, xv, ss);  // the square is exact: one rounding per term
+    x[e] = xv * double(sg[e]);
+  }
+  auto sum_stage = [&](auto m_c) {
+    constexpr int M = decltype(m_c)::value;
+    ss += xor_lane16<M>(ss);   // both lanes of a pair add the same two values: identical sums
   };
   sum_stage(std::integral_constant<int, 1>{});
   sum_stage(std::integral_constant<int, 2>{});
@@ -100,29 +146,36 @@ __device__ __forceinline__ uint16_t encode_row(const uint32_t (&w4)[4], const fl
   }
   auto fwht_stage = [&](auto m_c) {
     constexpr int M = decltype(m_c)::value;
+    const double sgn = (j & M) ? -1.0 : 1.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const double o = xor_lane16<M>(x[e]);
-      x[e] = (j & M) ? (o - x[e]) : (x[e] + o);
+      x[e] = fma(x[e], sgn, o);  // o - x or x + o, exactly
     }
   };
   fwht_stage(std::integral_constant<int, 1>{});
   fwht_stage(std::integral_constant<int, 2>{});
   fwht_stage(std::integral_constant<int, 4>{});
   fwht_stage(std::integral_constant<int, 8>{});
-  const uint16_t nbits = exact_norm_fp16(sA, sB, sC);
+  uint32_t nb = fast_norm_fp16(ss);
+  if (nb == 0xffffu) nb = exact_row_norm_fp16(w4);  // the same for all 16 lanes of the row
+  const uint16_t nbits = uint16_t(nb);
   const double nd = double(half_bits_to_float(nbits));
-  constexpr int K = levels(FMT);
-  double T[K - 1];
+  constexpr int K = levels(FMT), Hf = K / 2;
+  double U[Hf - 1];  // the positive thresholds, scaled by sqrt(128): n * beta_(Hf-1+k) * sqrt(128)
 #pragma unroll
-  for (int i = 0; i < K - 1; ++i) T[i] = nd * beta[i];  // exact in binary64
+  for (int k = 1; k < Hf; ++k) U[k - 1] = (nd * beta[Hf - 1 + k]) * kSqrtD;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const double y = x[e] / kSqrtD;
-    int c = 0;  // the number of thresholds below y
+    const double a = fabs(x[e]);
+    int cnt = 0;  // positive thresholds below |yhat|
 #pragma unroll
-    for (int i = 0; i < K - 1; ++i) c += y > T[i] ? 1 : 0;
-    code[e] = uint8_t(c);
+    for (int k = 0; k < Hf - 1; ++k) cnt += a > U[k] ? 1 : 0;
+    // y > 0: the Hf thresholds <= 0 and cnt positive ones lie below it; y <= 0: of the
+    // Hf - 1 negative thresholds -U, those above -|y| (|y| < U) lie below it.  An all-zero
+    // row (n = 0) encodes to index 0 everywhere.
+    const int c = x[e] > 0.0 ? Hf + cnt : Hf - 1 - cnt;
+    code[e] = uint8_t(nd == 0.0 ? 0 : c);
   }
   return nbits;
 }

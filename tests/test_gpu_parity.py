@@ -604,3 +604,55 @@ def test_stream_read_reads_every_word(n_bytes, blocks):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sums.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(words)
+
+
+# ----------------------------------------------------------------------------- encoder edge rows
+
+def _adversarial_rows():
+    """fp16 rows whose norms sit on or next to fp16 rounding midpoints (exact ties both
+    ways, a hair above a tie), in the subnormal range, at saturation, and all-zero or
+    single-element rows, plus Gaussian rows scaled across the fp16 range."""
+    rows = []
+    def row(vals):
+        x = np.zeros(128, dtype=np.float16)
+        x[:len(vals)] = np.array(vals, dtype=np.float64).astype(np.float16)
+        return x
+    rows += [row([2048, 64, 1]),                       # sqrt = 2049: tie, even wins (2048)
+             row([2048, 110, 14, 1]),                  # sqrt = 2051: tie, even wins (2052)
+             row([2048, 64, 1, 2.0 ** -24]),           # a hair above the tie: 2050
+             row([3 * 2.0 ** -24, 4 * 2.0 ** -24]),    # subnormal, exact
+             row([-7.5]), row([0.0]), row([65504.0]), row([65504.0, 65504.0]),
+             row([60000.0, 20000.0]), row([2.0 ** -14, -2.0 ** -14, 2.0 ** -24]),
+             row([1.0] * 128), row([-1.0] * 64 + [1.0] * 64), row([0.5] * 4)]
+    rng = np.random.default_rng(11)
+    for scale in (2.0 ** -20, 2.0 ** -12, 1.0, 64.0, 2048.0):
+        g = rng.standard_normal((24, 128)) * scale
+        rows += list(np.clip(g, -65504, 65504).astype(np.float16))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("fmt", ["turbo3", "turbo4"])
+def test_encode_adversarial_norms_and_codes(fmt, codebooks):
+    """Rows whose norm rounding is decided by the encoder's exact fallback (ties and near-ties),
+    subnormal and saturating norms, zero rows: norms bit for bit and codes equal to the oracle's
+    outside the 1e-5 boundary margin, through the bulk append and through the decode step."""
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    x = _adversarial_rows()
+    n = len(x)
+    w = S.scaled(get_workload(0), batch=1, num_q_heads=2, num_kv_heads=1, k_format=fmt, v_format=fmt)
+    cap = ((n + 31) // 32) * 32
+    cache = S.make_cache(w, cap)
+    kx = torch.from_numpy(x[None, None]).cuda()
+    tq.tq_encode_append(cache, kx, kx.clone())
+    m, g, t = S.compare_codes(cache, 0, x[None], x[None], n, w, codebooks)
+    assert m <= g
+    _say(f"[adversarial {fmt}] {n} rows: codes {m} mismatches / {t}, {g} within the margin")
+    # the decode step's in-kernel append: each row in turn as the step's new token
+    cache2 = S.make_cache(w, cap)
+    q = np.zeros((1, 2, 128), dtype=np.float16)
+    for i in range(n):
+        S.gpu_decode_step(cache2, x[None, None, i:i + 1], x[None, None, i:i + 1], q)
+    m2, g2, t2 = S.compare_codes(cache2, 0, x[None], x[None], n, w, codebooks)
+    assert m2 <= g2

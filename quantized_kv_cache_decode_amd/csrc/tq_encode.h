@@ -86,7 +86,7 @@ __device__ __forceinline__ uint32_t fast_norm_fp16(double ss) {
 
 // The exact norm (integer method) of a row held by a 16-lane group; every lane of
 // the group must execute it.
-__device__ __noinline__ uint16_t exact_row_norm_fp16(const uint32_t (&w4)[4]) {
+__device__ __forceinline__ uint16_t exact_row_norm_fp16(const uint32_t (&w4)[4]) {
   uint64_t sA = 0, sB = 0, sC = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {

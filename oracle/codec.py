@@ -28,15 +28,19 @@ Byte layouts (the pages print none; these are this library's):
         B[8j..8j+2] = c[8+j],  B[8j+3..8j+5] = c[12+j], B[8j+6..8j+7] = c[28+j] & 3
         C[8j..8j+2] = c[16+j], C[8j+3..8j+5] = c[20+j], C[8j+6] = c[24+j] >> 2,
         C[8j+7] = c[28+j] >> 2
-  * K record (token-major, one per token and KV head): turbo3 48 bytes = 4
-    sub-blocks for dims 32q..32q+31; turbo4 64 bytes = 16 octet words for dims
-    8w..8w+7.
+  * K record (one per token and KV head): turbo3 48 bytes = 4 sub-blocks for
+    dims 32q..32q+31; turbo4 64 bytes = 16 octet words for dims 8w..8w+7.  In
+    memory turbo3 records follow each other token by token; turbo4 records are
+    kept in blocks of 16 tokens, 16-byte piece p (words 4p..4p+3) of the block's
+    token i at byte 256 p + 16 i of the block's 1024 bytes.
   * V tile (32 tokens of one KV head, token-tiled): 64 chunks, chunk 16g + n
     holds the 8 tokens of slot group g and the 8 dims 8n..8n+7; element
     e = 8*nb + i of a chunk is dim 8n + nb of the token in tile slot
     r = 16*(i // 4) + 4*g + (i % 4).  turbo3 chunk = 2 sub-blocks (24 bytes,
-    elements 0..31 then 32..63); turbo4 chunk = 8 octet words (32 bytes), word
-    nb holding elements 8nb..8nb+7.  Tile = 1536 (turbo3) or 2048 (turbo4) bytes.
+    elements 0..31 then 32..63), chunk c at tile byte 24 c; turbo4 chunk = 8 octet
+    words (32 bytes), word nb holding elements 8nb..8nb+7, stored as two 16-byte
+    pieces: piece p (words 4p..4p+3) of chunk c at tile byte 1024 p + 16 c.  Tile =
+    1536 (turbo3) or 2048 (turbo4) bytes.
 """
 import math
 
@@ -232,6 +236,32 @@ def unpack_k_record(rec, fmt: str) -> np.ndarray:
     raise ValueError(fmt)
 
 
+K_BLOCK_TOKENS = 16   # turbo4 K records are interleaved in 16-byte pieces over blocks of this many tokens
+
+
+def k_records_to_memory(records, fmt: str) -> np.ndarray:
+    """Records [..., T, bytes] (T a multiple of 16) -> the bytes in memory order, same shape:
+    turbo3 unchanged; turbo4 piece p of token 16 b + i at byte 1024 b + 256 p + 16 i."""
+    r = np.asarray(records, dtype=np.uint8)
+    if fmt != "turbo4":
+        return r.copy()
+    T = r.shape[-2]
+    if T % K_BLOCK_TOKENS:
+        raise ValueError("token count must be a multiple of 16")
+    blk = r.reshape(r.shape[:-2] + (T // K_BLOCK_TOKENS, K_BLOCK_TOKENS, 4, 16))   # [.., blocks, i, p, 16]
+    return np.ascontiguousarray(np.swapaxes(blk, -3, -2)).reshape(r.shape)        # [.., blocks, p, i, 16]
+
+
+def k_memory_to_records(mem, fmt: str) -> np.ndarray:
+    """Inverse of k_records_to_memory."""
+    m = np.asarray(mem, dtype=np.uint8)
+    if fmt != "turbo4":
+        return m.copy()
+    T = m.shape[-2]
+    blk = m.reshape(m.shape[:-2] + (T // K_BLOCK_TOKENS, 4, K_BLOCK_TOKENS, 16))    # [.., blocks, p, i, 16]
+    return np.ascontiguousarray(np.swapaxes(blk, -3, -2)).reshape(m.shape)
+
+
 def v_tile_slot(g: int, i: int) -> int:
     """Tile slot (0..31) of element-token i (0..7) in slot group g (0..3)."""
     return 16 * (i // 4) + 4 * g + (i % 4)
@@ -274,6 +304,9 @@ def pack_v_tiles(codes, fmt: str) -> np.ndarray:
         chunk = np.concatenate([pack_sub3(el[..., :32]), pack_sub3(el[..., 32:])], axis=-1)
     elif fmt == "turbo4":
         chunk = np.concatenate([pack_oct4(el[..., 8 * nb:8 * nb + 8]) for nb in range(8)], axis=-1)
+        # two 16-byte pieces per chunk: piece p of chunk c at tile byte 1024 p + 16 c
+        pieces = np.swapaxes(chunk.reshape(chunk.shape[:-1] + (2, 16)), -3, -2)  # [.., nt, p, c, 16]
+        return np.ascontiguousarray(pieces).reshape(chunk.shape[:-2] + (-1,))
     elif fmt == "f16":
         chunk = np.ascontiguousarray(el).view(np.uint8)                # 64 little-endian fp16 values
     else:
@@ -285,7 +318,10 @@ def unpack_v_tiles(tiles, fmt: str) -> np.ndarray:
     """Inverse of pack_v_tiles: bytes [nt, tile bytes] -> codes [nt*32, 128]."""
     t = np.asarray(tiles, dtype=np.uint8)
     cb = V_CHUNK_BYTES[fmt]
-    ch = t.reshape(t.shape[:-1] + (64, cb))
+    if fmt == "turbo4":   # pieces back into chunks
+        ch = np.swapaxes(t.reshape(t.shape[:-1] + (2, 64, 16)), -3, -2).reshape(t.shape[:-1] + (64, cb))
+    else:
+        ch = t.reshape(t.shape[:-1] + (64, cb))
     if fmt == "turbo3":
         el = np.concatenate([unpack_sub3(ch[..., :12]), unpack_sub3(ch[..., 12:])], axis=-1)
     elif fmt == "f16":

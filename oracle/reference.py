@@ -34,7 +34,7 @@ def encode_sequence(k16, v16, k_format, v_format, k_signs, v_signs, codebooks, c
         norms = np.zeros((hkv, cap), dtype=np.float16)
         norms[:, :L] = kn
         out["k_codes"], out["k_norms"] = codes, norms
-        out["k_rec"] = codec.pack_k_record(codes, k_format)
+        out["k_rec"] = codec.k_records_to_memory(codec.pack_k_record(codes, k_format), k_format)
     if v_format == "f16":   # the uncompressed comparison cache: values stored as they come
         vf = np.zeros((hkv, cap, 128), dtype=np.float16)
         vf[:, :L] = v16
@@ -71,6 +71,6 @@ def decode_sequence(q, k_hat, v_hat, length, scale=SCALE):
 def codes_from_library_layout(k_rec, v_tiles, k_format, v_format):
     """Unpack the library's byte layout back to codes [Hkv, cap, 128] (K may be None for f16;
     for f16 V the values come back, fp16)."""
-    kc = None if k_rec is None else codec.unpack_k_record(k_rec, k_format)
+    kc = None if k_rec is None else codec.unpack_k_record(codec.k_memory_to_records(k_rec, k_format), k_format)
     vc = codec.unpack_v_tiles(v_tiles, v_format)
     return kc, vc

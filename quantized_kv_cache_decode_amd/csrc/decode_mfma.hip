@@ -166,6 +166,23 @@ __device__ inline void load_words(uint32_t (&w)[N], const uint8_t* p) {
   }
 }
 
+// NP 16-byte pieces at p, p + stride, ... (turbo4 K records and V chunks): every
+// piece load of the wave reads whole contiguous cache lines, and each byte once, so
+// the loads are non-temporal.
+template <int NP, int N>
+__device__ inline void load_pieces(uint32_t (&w)[N], const uint8_t* p, size_t stride) {
+  static_assert(N == 4 * NP, "four words per piece");
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * stride));
+    w[4 * i] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
+}
+
 template <int N>
 __device__ inline void zero_words(uint32_t (&w)[N]) {
 #pragma unroll
@@ -407,8 +424,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
   // every column sees the tokens before t_all.
   const int t_all = min(t1, L - (a.q_len - 1));
   const int t_col = min(t1, L - (a.q_len - 1 - hn % a.q_len));
-  const uint8_t* kbase = a.k_data + row * size_t(a.cap) * REC + part * (REC / P);
-  const uint8_t* vbase = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT) + lane * (VW * 4);
+  // turbo4 K: this lane's pieces part*(4/P) .. of token n of each 16-token block; turbo4
+  // V: pieces 0 and 1 of chunk `lane` of each tile; otherwise its contiguous share
+  const uint8_t* kbase = KFMT == kFmtTurbo4
+                             ? a.k_data + row * size_t(a.cap) * REC + n * 16 + part * (4 / P) * 256
+                             : a.k_data + row * size_t(a.cap) * REC + part * (REC / P);
+  const uint8_t* vbase = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT) +
+                         (VFMT == kFmtTurbo4 ? lane * 16 : lane * (VW * 4));
   const uint16_t* knorm = KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap);
   const uint16_t* vnorm = VFMT == kFmtF16 ? nullptr : a.v_norms + row * size_t(a.cap);
   __shared__ float qs[kMaxGroup][kDim];
@@ -445,7 +467,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
   auto load_k = [&](int base) {
     const int tk = min((base >> 5) + sig, last_tile) << 5;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) load_words(kw[rb], kbase + size_t(tk + 16 * rb + n) * REC);
+    for (int rb = 0; rb < 2; ++rb) {
+      if constexpr (KFMT == kFmtTurbo4) load_pieces<KW / 4>(kw[rb], kbase + size_t((tk >> 4) + rb) * 1024, 256);
+      else load_words(kw[rb], kbase + size_t(tk + 16 * rb + n) * REC);
+    }
     if (KFMT != kFmtF16) {
       const int tn = min((base >> 5) + sn, last_tile) << 5;
 #pragma unroll
@@ -454,8 +479,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
   };
   auto load_v = [&](int base) {
 #pragma unroll
-    for (int sg = 0; sg < NS; ++sg)
-      load_words(vw[sg], vbase + size_t(min((base >> 5) + sg, last_tile)) * v_tile_bytes(VFMT));
+    for (int sg = 0; sg < NS; ++sg) {
+      const uint8_t* tile = vbase + size_t(min((base >> 5) + sg, last_tile)) * v_tile_bytes(VFMT);
+      if constexpr (VFMT == kFmtTurbo4) load_pieces<2>(vw[sg], tile, 1024);
+      else load_words(vw[sg], tile);
+    }
     const int tn = min((base >> 5) + sn, last_tile) << 5;
     if (VFMT != kFmtF16) {
 #pragma unroll

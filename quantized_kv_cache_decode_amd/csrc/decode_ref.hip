@@ -33,15 +33,18 @@ __device__ inline void v_code_pair(const uint8_t* v_row, int t, int d, uint32_t&
   const int tile = t >> 5, r = t & 31;
   const int g = slot_group(r), i = slot_elem(r);
   const int n = d >> 3, nb = d & 7;
-  const uint8_t* chunk = v_row + size_t(tile) * v_tile_bytes(FMT) + (16 * g + n) * v_chunk_bytes(FMT);
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(chunk);
+  const uint8_t* vt = v_row + size_t(tile) * v_tile_bytes(FMT);
+  const int c = 16 * g + n;
   if (FMT == kFmtTurbo3) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(vt + v_chunk_byte_offset(FMT, c, 0));
     const int e0 = 8 * nb + i, e1 = e0 + 8;
     c0 = sub3_get(w + 3 * (e0 >> 5), e0 & 31);
     c1 = sub3_get(w + 3 * (e1 >> 5), e1 & 31);
   } else {
-    c0 = t4_index_of_nibble(oct4_get_nibble(w[nb], i));
-    c1 = t4_index_of_nibble(oct4_get_nibble(w[nb + 1], i));
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(vt + v_chunk_byte_offset(FMT, c, 4 * nb));
+    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(vt + v_chunk_byte_offset(FMT, c, 4 * nb + 4));
+    c0 = t4_index_of_nibble(oct4_get_nibble(w0, i));
+    c1 = t4_index_of_nibble(oct4_get_nibble(w1, i));
   }
 }
 
@@ -116,9 +119,9 @@ __global__ __launch_bounds__(256) void decode_ref_kernel(DecodeArgs a, SeqLens l
       } else {
         constexpr int kWords = k_record_bytes(KFMT) / 4;
         uint32_t rec[kWords];
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.k_data + (row * a.cap + t) * k_record_bytes(KFMT));
+        const uint8_t* row_k = a.k_data + row * a.cap * k_record_bytes(KFMT);
 #pragma unroll
-        for (int i = 0; i < kWords; ++i) rec[i] = src[i];
+        for (int i = 0; i < kWords; ++i) rec[i] = *reinterpret_cast<const uint32_t*>(row_k + k_byte_offset(KFMT, t, 4 * i));
 #pragma unroll
         for (int d = 0; d < kDim; ++d) {
           const float kv = kcb[k_code<KFMT>(rec, d)];

@@ -36,14 +36,15 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
   // Threads 0..63 own V-tile chunk tid.  When the tile already holds other tokens,
   // its old words are requested now so the read overlaps the encode below.
   const bool whole = lo == tile * kTileTokens && hi == tile * kTileTokens + kTileTokens;
-  uint8_t* chunk = a.v_data + (row * (a.cap / kTileTokens) + tile) * v_tile_bytes(VFMT) + (tid & 63) * v_chunk_bytes(VFMT);
+  uint8_t* vtile = a.v_data + (row * (a.cap / kTileTokens) + tile) * v_tile_bytes(VFMT);
   constexpr int kChunkWords = VFMT == kFmtF16 ? 1 : v_chunk_bytes(VFMT) / 4;  // (F16 V: rows stored directly)
   uint32_t old[kChunkWords];
 #pragma unroll
   for (int i = 0; i < kChunkWords; ++i) old[i] = 0;
   if (VFMT != kFmtF16 && tid < 64 && !whole) {
 #pragma unroll
-    for (int i = 0; i < kChunkWords; ++i) old[i] = reinterpret_cast<const uint32_t*>(chunk)[i];
+    for (int i = 0; i < kChunkWords; ++i)
+      old[i] = *reinterpret_cast<const uint32_t*>(vtile + v_chunk_byte_offset(VFMT, tid & 63, 4 * i));
   }
 
   // Active rows: n_tok new tokens of this tile, each with a K row and a V row.
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
       load_thresholds<KQ>(a.k_cb, beta);
       const uint16_t nbits = encode_row<KQ>(w4, sg, beta, j, code);
       if (j == 0) a.k_norms[slot] = nbits;
-      store_k_record<KQ>(a.k_data + slot * k_record_bytes(KQ), code, j);
+      store_k_record<KQ>(a.k_data + row * a.cap * k_record_bytes(KQ), t, code, j);
     }
   }
   __syncthreads();
@@ -111,25 +112,25 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
     for (int i = 0; i < 8; ++i) {
       const int rr = slot_of(g, i);
       const int tt = tile * kTileTokens + rr;
-      const bool fresh = tt >= lo && tt < hi;
+      if (tt >= lo && tt < hi) {  // a new token: its 8 codes of dims 8n..8n+7 in one LDS read
+        const uint2 c8 = *reinterpret_cast<const uint2*>(&vcodes[rr][8 * n]);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-        if (fresh) el[8 * nb + i] = vcodes[rr][8 * n + nb];
+        for (int nb = 0; nb < 8; ++nb) el[8 * nb + i] = uint8_t((nb < 4 ? c8.x : c8.y) >> (8 * (nb & 3)));
+      }
     }
     if constexpr (VFMT == kFmtTurbo3) {
       uint32_t w[6];
       sub3_pack(el, w);
       sub3_pack(el + 32, w + 3);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(chunk);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(vtile + v_chunk_byte_offset(VFMT, tid, 0));
 #pragma unroll
       for (int i = 0; i < 6; ++i) dst[i] = w[i];
     } else {
       uint32_t w[8];
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) w[nb] = oct4_pack(el + 8 * nb);
-      uint4* dst = reinterpret_cast<uint4*>(chunk);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      *reinterpret_cast<uint4*>(vtile + v_chunk_byte_offset(VFMT, tid, 0)) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(vtile + v_chunk_byte_offset(VFMT, tid, 16)) = make_uint4(w[4], w[5], w[6], w[7]);
     }
   }
   if (blockIdx.x == 0 && h == 0 && tid == 0) a.seq_lens[b] = end;

@@ -22,6 +22,22 @@ __host__ __device__ constexpr int v_chunk_bytes(int fmt) { return fmt == kFmtTur
 __host__ __device__ constexpr int v_tile_bytes(int fmt) { return 64 * v_chunk_bytes(fmt); }
 __host__ __device__ constexpr int levels(int fmt) { return fmt == kFmtTurbo3 ? 8 : 16; }
 
+// Byte order in memory.  turbo3 K records follow each other token by token (record
+// of token t at byte 48 t of its row) and turbo3 / fp16 V chunks chunk by chunk.
+// turbo4 bytes are stored in 16-byte pieces so that the 16 or 64 lanes reading the
+// same piece of neighbouring records / chunks read whole contiguous cache lines:
+// K records in blocks of 16 tokens, piece p (record bytes 16p..16p+15) of token
+// 16b + i at byte 1024 b + 256 p + 16 i; V chunk c's piece p (chunk bytes
+// 16p..16p+15) at tile byte 1024 p + 16 c.
+__host__ __device__ inline size_t k_byte_offset(int fmt, size_t t, int byte) {
+  if (fmt == kFmtTurbo4) return (t >> 4) * 1024 + size_t(byte >> 4) * 256 + (t & 15) * 16 + (byte & 15);
+  return t * size_t(fmt == kFmtTurbo3 ? 48 : 256) + byte;
+}
+__host__ __device__ inline int v_chunk_byte_offset(int fmt, int chunk, int byte) {
+  if (fmt == kFmtTurbo4) return (byte >> 4) * 1024 + chunk * 16 + (byte & 15);
+  return chunk * v_chunk_bytes(fmt) + byte;
+}
+
 // V tile: token slot r (0..31) <-> (slot group g = 0..3, element-token i = 0..7),
 // r = 16*(i/4) + 4*g + (i%4).
 __host__ __device__ inline int slot_group(int r) { return (r & 15) >> 2; }

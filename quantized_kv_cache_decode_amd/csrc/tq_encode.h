@@ -194,12 +194,14 @@ __device__ __forceinline__ void load_row_and_signs(const uint16_t* src, const fl
   sg[4] = s1.x; sg[5] = s1.y; sg[6] = s1.z; sg[7] = s1.w;
 }
 
-// Write the K record of one token from a 16-lane group's codes (lane j: dims 8j..8j+7).
+// Write the K record of token t of a row (row_k: the row's K bytes) from a 16-lane
+// group's codes (lane j: dims 8j..8j+7).
 template <int KFMT>
-__device__ __forceinline__ void store_k_record(uint8_t* rec, const uint8_t (&code)[8], int j) {
+__device__ __forceinline__ void store_k_record(uint8_t* row_k, int t, const uint8_t (&code)[8], int j) {
   if (KFMT == kFmtTurbo4) {
-    *reinterpret_cast<uint32_t*>(rec + 4 * j) = oct4_pack(code);
+    *reinterpret_cast<uint32_t*>(row_k + k_byte_offset(kFmtTurbo4, t, 4 * j)) = oct4_pack(code);
   } else {
+    uint8_t* rec = row_k + size_t(t) * k_record_bytes(KFMT);
     // Lanes 4q..4q+3 hold elements 8c..8c+7 (c = j % 4) of sub-block q.  Lanes with
     // c < 3 own word c outright (element 8c+i: byte i%4, bits 3*(i/4)); lane c = 3
     // holds elements 24..31, whose low two bits go to bits 6-7 of words A (24..27)
@@ -322,7 +324,8 @@ template <int VFMT>
 struct VRowInputs {
   RowInputs<VFMT> row;
   uint32_t cw[v_chunk_bytes(VFMT) / 4];  // the chunk words the token's fields go into
-  uint8_t* chunk;
+  uint8_t* tile;
+  int chunk;                             // chunk 16 g + j of the tile
   int ei;                                // chunk element of the token's slot
 };
 
@@ -331,12 +334,13 @@ __device__ __forceinline__ void load_v_inputs(const EncodeArgs& a, size_t row, i
                                      VRowInputs<VFMT>& in) {
   const int r = t % kTileTokens, g = slot_group(r);
   in.ei = slot_elem(r);
-  in.chunk = a.v_data + (row * (a.cap / kTileTokens) + t / kTileTokens) * v_tile_bytes(VFMT) +
-             (16 * g + j) * v_chunk_bytes(VFMT);
+  in.tile = a.v_data + (row * (a.cap / kTileTokens) + t / kTileTokens) * v_tile_bytes(VFMT);
+  in.chunk = 16 * g + j;
   // a token in slot 0 starts the tile: the other slots hold nothing visible yet
 #pragma unroll
   for (int k = 0; k < v_chunk_bytes(VFMT) / 4; ++k)
-    in.cw[k] = r == 0 ? 0u : reinterpret_cast<const uint32_t*>(in.chunk)[k];
+    in.cw[k] = r == 0 ? 0u
+                      : *reinterpret_cast<const uint32_t*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 4 * k));
   load_row_inputs<VFMT>(src, a.v_signs, a.v_cb, j, in.row);
 }
 
@@ -356,12 +360,11 @@ __device__ __forceinline__ uint16_t append_v_row(const EncodeArgs& a, size_t row
       sub3_set(cw[3 * sb], cw[3 * sb + 1], cw[3 * sb + 2], 8 * (n8 & 3) + in.ei, code[n8]);
     }
   }
-  if (VFMT == kFmtTurbo4) {
-    uint4* dst = reinterpret_cast<uint4*>(in.chunk);
-    dst[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-    dst[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+  if (VFMT == kFmtTurbo4) {  // two 16-byte pieces
+    *reinterpret_cast<uint4*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 0)) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    *reinterpret_cast<uint4*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 16)) = make_uint4(cw[4], cw[5], cw[6], cw[7]);
   } else {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(in.chunk);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 0));
 #pragma unroll
     for (int k = 0; k < v_chunk_bytes(VFMT) / 4; ++k) dst[k] = cw[k];
   }
@@ -376,7 +379,7 @@ __device__ __forceinline__ uint16_t append_k_row(const EncodeArgs& a, size_t row
   const uint16_t nbits = encode_row<KFMT>(in.w4, in.sg, in.beta, j, code);
   const size_t slot = row * a.cap + t;
   if (j == 0) a.k_norms[slot] = nbits;
-  store_k_record<KFMT>(a.k_data + slot * k_record_bytes(KFMT), code, j);
+  store_k_record<KFMT>(a.k_data + row * a.cap * k_record_bytes(KFMT), t, code, j);
   return nbits;
 }
 

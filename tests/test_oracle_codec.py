@@ -287,13 +287,21 @@ def test_turbo4_nibble_semantics(codebooks):
 
 
 def test_v_tile_hand_worked_bytes():
-    # turbo4: token slot 21 = (g=1, i=5), dim 42 = (n=5, nb=2) -> chunk 21, word 2, high nibble of byte 1
-    # -> byte 21*32 + 8 + 1 = 681 holds nibble(10) = 2 << 4; all other codes 8 (nibble 0)
+    # turbo4: token slot 21 = (g=1, i=5), dim 42 = (n=5, nb=2) -> chunk 21, word 2, high nibble of
+    # byte 1 -> chunk byte 9, in piece 0 -> tile byte 1024*0 + 16*21 + 9 = 345 holds nibble(10) = 2 << 4;
+    # all other codes 8 (nibble 0).  Dim 110 = (n=13, nb=6) of slot 30 = (g=3, i=6) -> chunk 61,
+    # word 6 = chunk bytes 24..27 (piece 1, bytes 8..11); element 6 is the high nibble of the word's
+    # byte 2 -> tile byte 1024 + 16*61 + 10 = 2010 holds nibble(9) = 1 << 4
     c = np.full((32, 128), 8)
     c[21, 42] = 10
     t = codec.pack_v_tiles(c, "turbo4")[0]
     nz = np.nonzero(t)[0]
-    assert list(nz) == [681] and t[681] == 0x20
+    assert list(nz) == [345] and t[345] == 0x20
+    c = np.full((32, 128), 8)
+    c[30, 110] = 9
+    t = codec.pack_v_tiles(c, "turbo4")[0]
+    nz = np.nonzero(t)[0]
+    assert list(nz) == [2010] and t[2010] == 0x10
     # turbo3: slot 2 = (g=0, i=2), dim 127 = (n=15, nb=7) -> chunk 15, element 58 = sub-block 1 element 26
     # -> C word of that sub-block, bit 22 -> byte 15*24 + 12 + 8 + 2 = 382 = 0x40
     c = np.zeros((32, 128), dtype=int)
@@ -319,6 +327,25 @@ def test_k_record_byte_positions():
         c4[d] = 0
         nz = np.nonzero(codec.pack_k_record(c4, "turbo4"))[0]
         assert list(nz) == [4 * (d // 8) + (d % 8) % 4]
+
+
+def test_k_memory_order_hand_worked():
+    # turbo4: token 37 = block 2, i = 5; dim 100 = word 12, element 4 -> high nibble of record byte 48,
+    # piece 3, byte 0 -> memory byte 1024*2 + 256*3 + 16*5 + 0 = 2896 (of the 64 * 64 bytes of 64 tokens)
+    c = np.full((64, 128), 8)
+    c[37, 100] = 10
+    mem = codec.k_records_to_memory(codec.pack_k_record(c, "turbo4"), "turbo4").reshape(-1)
+    nz = np.nonzero(mem)[0]
+    assert list(nz) == [2896] and mem[2896] == 0x20
+    # turbo3 records stay token by token: token 37's record starts at byte 37 * 48
+    c3 = np.zeros((64, 128), dtype=int)
+    c3[37, 0] = 5
+    mem3 = codec.k_records_to_memory(codec.pack_k_record(c3, "turbo3"), "turbo3").reshape(-1)
+    assert list(np.nonzero(mem3)[0]) == [37 * 48] and mem3[37 * 48] == 5
+    # round trip
+    rng = np.random.default_rng(2)
+    r = rng.integers(0, 256, (3, 48, 64), dtype=np.uint8)
+    np.testing.assert_array_equal(codec.k_memory_to_records(codec.k_records_to_memory(r, "turbo4"), "turbo4"), r)
 
 
 @pytest.mark.parametrize("fmt,k", [("turbo3", 8), ("turbo4", 16)])

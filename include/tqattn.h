@@ -44,16 +44,19 @@
  *       B[8j..8j+2]=c[8+j]  B[8j+3..8j+5]=c[12+j] B[8j+6..8j+7]=c[28+j]&3
  *       C[8j..8j+2]=c[16+j] C[8j+3..8j+5]=c[20+j] C[8j+6]=c[24+j]>>2
  *       C[8j+7]=c[28+j]>>2
- *   K record: turbo3 48 bytes = 4 sub-blocks (dims 32q..32q+31), stored token
- *     by token (token t's record at byte 48 t of its row); turbo4 64 bytes = 16
- *     octet words (dims 8w..8w+7), stored in blocks of 16 tokens as 16-byte
- *     pieces: piece p (words 4p..4p+3) of token 16b + i at byte
- *     1024 b + 256 p + 16 i of its row, so that the 16 lanes reading piece p of
- *     a block's tokens read 256 contiguous bytes.
+ *   K record: turbo3 48 bytes = 4 sub-blocks (dims 32q..32q+31); turbo4 64
+ *     bytes = 16 octet words (dims 8w..8w+7).  Both are stored in blocks of 16
+ *     tokens, as pieces, so that the lanes reading the same piece of a block's
+ *     tokens read contiguous bytes: turbo4 piece p (words 4p..4p+3) of token
+ *     16b + i at byte 1024 b + 256 p + 16 i of its row; turbo3 piece q (sub-block
+ *     q, 12 bytes) of token 16b + i at byte 768 b + 384 (q % 2) + 192 (q / 2) +
+ *     12 i (pieces 0 and 2 of the block's 16 tokens fill bytes 0..383 of the
+ *     block, pieces 1 and 3 bytes 384..767).
  *   V tile (32 tokens, token-tiled): 64 chunks; chunk 16g+n holds dims
  *     8n..8n+7 of the 8 tokens in tile slots r = 16(i/4) + 4g + (i%4),
  *     i = 0..7; chunk element 8*nb + i is dim 8n+nb of token slot r(g, i).
- *     turbo3 chunk = 2 sub-blocks (24 bytes) at tile byte 24 c; turbo4 chunk =
+ *     turbo3 chunk = 2 sub-blocks (24 bytes), sub-block p of chunk c at tile
+ *     byte 768 p + 12 c; turbo4 chunk =
  *     8 octet words, word nb = elements 8nb..8nb+7 (32 bytes), as two 16-byte
  *     pieces: piece p (words 4p..4p+3) of chunk c at tile byte 1024 p + 16 c;
  *     F16 chunk = the 64 elements as fp16 values (128 bytes) at tile byte

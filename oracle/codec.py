@@ -236,30 +236,43 @@ def unpack_k_record(rec, fmt: str) -> np.ndarray:
     raise ValueError(fmt)
 
 
-K_BLOCK_TOKENS = 16   # turbo4 K records are interleaved in 16-byte pieces over blocks of this many tokens
+K_BLOCK_TOKENS = 16   # quantised K records are interleaved in pieces over blocks of this many tokens
 
 
 def k_records_to_memory(records, fmt: str) -> np.ndarray:
-    """Records [..., T, bytes] (T a multiple of 16) -> the bytes in memory order, same shape:
-    turbo3 unchanged; turbo4 piece p of token 16 b + i at byte 1024 b + 256 p + 16 i."""
+    """Records [..., T, bytes] (T a multiple of 16) -> the bytes in memory order, same shape.
+
+    turbo4: piece p (record bytes 16p..16p+15) of token 16 b + i at byte 1024 b + 256 p + 16 i.
+    turbo3: piece q (sub-block q, record bytes 12q..12q+11) of token 16 b + i at byte
+    768 b + 384 (q % 2) + 192 (q // 2) + 12 i."""
     r = np.asarray(records, dtype=np.uint8)
-    if fmt != "turbo4":
+    if fmt not in ("turbo3", "turbo4"):
         return r.copy()
     T = r.shape[-2]
     if T % K_BLOCK_TOKENS:
         raise ValueError("token count must be a multiple of 16")
-    blk = r.reshape(r.shape[:-2] + (T // K_BLOCK_TOKENS, K_BLOCK_TOKENS, 4, 16))   # [.., blocks, i, p, 16]
-    return np.ascontiguousarray(np.swapaxes(blk, -3, -2)).reshape(r.shape)        # [.., blocks, p, i, 16]
+    nb = T // K_BLOCK_TOKENS
+    if fmt == "turbo4":
+        blk = r.reshape(r.shape[:-2] + (nb, K_BLOCK_TOKENS, 4, 16))               # [.., blocks, i, p, 16]
+        return np.ascontiguousarray(np.swapaxes(blk, -3, -2)).reshape(r.shape)    # [.., blocks, p, i, 16]
+    blk = r.reshape(r.shape[:-2] + (nb, K_BLOCK_TOKENS, 2, 2, 12))                # [.., blocks, i, q//2, q%2, 12]
+    mem = np.moveaxis(blk, (-4, -3, -2), (-2, -3, -4))                            # [.., blocks, q%2, q//2, i, 12]
+    return np.ascontiguousarray(mem).reshape(r.shape)
 
 
 def k_memory_to_records(mem, fmt: str) -> np.ndarray:
     """Inverse of k_records_to_memory."""
     m = np.asarray(mem, dtype=np.uint8)
-    if fmt != "turbo4":
+    if fmt not in ("turbo3", "turbo4"):
         return m.copy()
     T = m.shape[-2]
-    blk = m.reshape(m.shape[:-2] + (T // K_BLOCK_TOKENS, 4, K_BLOCK_TOKENS, 16))    # [.., blocks, p, i, 16]
-    return np.ascontiguousarray(np.swapaxes(blk, -3, -2)).reshape(m.shape)
+    nb = T // K_BLOCK_TOKENS
+    if fmt == "turbo4":
+        blk = m.reshape(m.shape[:-2] + (nb, 4, K_BLOCK_TOKENS, 16))               # [.., blocks, p, i, 16]
+        return np.ascontiguousarray(np.swapaxes(blk, -3, -2)).reshape(m.shape)
+    blk = m.reshape(m.shape[:-2] + (nb, 2, 2, K_BLOCK_TOKENS, 12))                # [.., blocks, q%2, q//2, i, 12]
+    rec = np.moveaxis(blk, (-4, -3, -2), (-2, -3, -4))                            # [.., blocks, i, q//2, q%2, 12]
+    return np.ascontiguousarray(rec).reshape(m.shape)
 
 
 def v_tile_slot(g: int, i: int) -> int:
@@ -302,6 +315,9 @@ def pack_v_tiles(codes, fmt: str) -> np.ndarray:
     el = _v_chunk_elements(tiles)                                  # [..., nt, 64, 64]
     if fmt == "turbo3":
         chunk = np.concatenate([pack_sub3(el[..., :32]), pack_sub3(el[..., 32:])], axis=-1)
+        # two 12-byte pieces (sub-blocks) per chunk: piece p of chunk c at tile byte 768 p + 12 c
+        pieces = np.swapaxes(chunk.reshape(chunk.shape[:-1] + (2, 12)), -3, -2)  # [.., nt, p, c, 12]
+        return np.ascontiguousarray(pieces).reshape(chunk.shape[:-2] + (-1,))
     elif fmt == "turbo4":
         chunk = np.concatenate([pack_oct4(el[..., 8 * nb:8 * nb + 8]) for nb in range(8)], axis=-1)
         # two 16-byte pieces per chunk: piece p of chunk c at tile byte 1024 p + 16 c
@@ -318,8 +334,9 @@ def unpack_v_tiles(tiles, fmt: str) -> np.ndarray:
     """Inverse of pack_v_tiles: bytes [nt, tile bytes] -> codes [nt*32, 128]."""
     t = np.asarray(tiles, dtype=np.uint8)
     cb = V_CHUNK_BYTES[fmt]
-    if fmt == "turbo4":   # pieces back into chunks
-        ch = np.swapaxes(t.reshape(t.shape[:-1] + (2, 64, 16)), -3, -2).reshape(t.shape[:-1] + (64, cb))
+    if fmt in ("turbo3", "turbo4"):   # pieces back into chunks
+        pb = cb // 2
+        ch = np.swapaxes(t.reshape(t.shape[:-1] + (2, 64, pb)), -3, -2).reshape(t.shape[:-1] + (64, cb))
     else:
         ch = t.reshape(t.shape[:-1] + (64, cb))
     if fmt == "turbo3":

@@ -183,6 +183,36 @@ __device__ inline void load_pieces(uint32_t (&w)[N], const uint8_t* p, size_t st
   }
 }
 
+// turbo3: the 4/P 12-byte pieces (sub-blocks) u0, u0 + 1, ... of this lane's token in
+// a 16-token K block at p (piece u at p + 384 (u % 2) + 192 (u / 2)), and the two pieces
+// of this lane's V chunk at p and p + 768.  Each load of the wave reads whole cache
+// lines, each byte once.
+template <int NP, int N>
+__device__ inline void load_k3_pieces(uint32_t (&w)[N], const uint8_t* p, int u0) {
+  static_assert(N == 3 * NP, "three words per piece");
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int u = u0 + i;
+    const u32x3 v = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(p + 384 * (u & 1) + 192 * (u >> 1)));
+    w[3 * i] = v.x;
+    w[3 * i + 1] = v.y;
+    w[3 * i + 2] = v.z;
+  }
+}
+template <int N>
+__device__ inline void load_v3_pieces(uint32_t (&w)[N], const uint8_t* p) {
+  static_assert(N == 6, "two pieces of three words");
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const u32x3 v = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(p + 768 * i));
+    w[3 * i] = v.x;
+    w[3 * i + 1] = v.y;
+    w[3 * i + 2] = v.z;
+  }
+}
+
 template <int N>
 __device__ inline void zero_words(uint32_t (&w)[N]) {
 #pragma unroll
@@ -424,13 +454,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
   // every column sees the tokens before t_all.
   const int t_all = min(t1, L - (a.q_len - 1));
   const int t_col = min(t1, L - (a.q_len - 1 - hn % a.q_len));
-  // turbo4 K: this lane's pieces part*(4/P) .. of token n of each 16-token block; turbo4
-  // V: pieces 0 and 1 of chunk `lane` of each tile; otherwise its contiguous share
-  const uint8_t* kbase = KFMT == kFmtTurbo4
-                             ? a.k_data + row * size_t(a.cap) * REC + n * 16 + part * (4 / P) * 256
-                             : a.k_data + row * size_t(a.cap) * REC + part * (REC / P);
+  // Quantised K: this lane's pieces part*(4/P) .. of token n of each 16-token block;
+  // quantised V: pieces 0 and 1 of chunk `lane` of each tile; fp16: its contiguous share
+  const uint8_t* kbase = KFMT == kFmtTurbo4   ? a.k_data + row * size_t(a.cap) * REC + n * 16 + part * (4 / P) * 256
+                         : KFMT == kFmtTurbo3 ? a.k_data + row * size_t(a.cap) * REC + n * 12
+                                              : a.k_data + row * size_t(a.cap) * REC + part * (REC / P);
   const uint8_t* vbase = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT) +
-                         (VFMT == kFmtTurbo4 ? lane * 16 : lane * (VW * 4));
+                         (VFMT == kFmtTurbo4 ? lane * 16 : VFMT == kFmtTurbo3 ? lane * 12 : lane * (VW * 4));
   const uint16_t* knorm = KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap);
   const uint16_t* vnorm = VFMT == kFmtF16 ? nullptr : a.v_norms + row * size_t(a.cap);
   __shared__ float qs[kMaxGroup][kDim];
@@ -469,6 +499,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       if constexpr (KFMT == kFmtTurbo4) load_pieces<KW / 4>(kw[rb], kbase + size_t((tk >> 4) + rb) * 1024, 256);
+      else if constexpr (KFMT == kFmtTurbo3)
+        load_k3_pieces<KW / 3>(kw[rb], kbase + size_t((tk >> 4) + rb) * 768, part * (4 / P));
       else load_words(kw[rb], kbase + size_t(tk + 16 * rb + n) * REC);
     }
     if (KFMT != kFmtF16) {
@@ -482,6 +514,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
     for (int sg = 0; sg < NS; ++sg) {
       const uint8_t* tile = vbase + size_t(min((base >> 5) + sg, last_tile)) * v_tile_bytes(VFMT);
       if constexpr (VFMT == kFmtTurbo4) load_pieces<2>(vw[sg], tile, 1024);
+      else if constexpr (VFMT == kFmtTurbo3) load_v3_pieces(vw[sg], tile);
       else load_words(vw[sg], tile);
     }
     const int tn = min((base >> 5) + sn, last_tile) << 5;

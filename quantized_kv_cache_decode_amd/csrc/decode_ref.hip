@@ -36,10 +36,9 @@ __device__ inline void v_code_pair(const uint8_t* v_row, int t, int d, uint32_t&
   const uint8_t* vt = v_row + size_t(tile) * v_tile_bytes(FMT);
   const int c = 16 * g + n;
   if (FMT == kFmtTurbo3) {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(vt + v_chunk_byte_offset(FMT, c, 0));
-    const int e0 = 8 * nb + i, e1 = e0 + 8;
-    c0 = sub3_get(w + 3 * (e0 >> 5), e0 & 31);
-    c1 = sub3_get(w + 3 * (e1 >> 5), e1 & 31);
+    const int e0 = 8 * nb + i, e1 = e0 + 8;   // sub-block e / 32 is piece e / 32 of the chunk
+    c0 = sub3_get(reinterpret_cast<const uint32_t*>(vt + v_chunk_byte_offset(FMT, c, 12 * (e0 >> 5))), e0 & 31);
+    c1 = sub3_get(reinterpret_cast<const uint32_t*>(vt + v_chunk_byte_offset(FMT, c, 12 * (e1 >> 5))), e1 & 31);
   } else {
     const uint32_t w0 = *reinterpret_cast<const uint32_t*>(vt + v_chunk_byte_offset(FMT, c, 4 * nb));
     const uint32_t w1 = *reinterpret_cast<const uint32_t*>(vt + v_chunk_byte_offset(FMT, c, 4 * nb + 4));

@@ -122,9 +122,13 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
       uint32_t w[6];
       sub3_pack(el, w);
       sub3_pack(el + 32, w + 3);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(vtile + v_chunk_byte_offset(VFMT, tid, 0));
 #pragma unroll
-      for (int i = 0; i < 6; ++i) dst[i] = w[i];
+      for (int p = 0; p < 2; ++p) {  // two 12-byte pieces (one sub-block each)
+        uint32_t* dst = reinterpret_cast<uint32_t*>(vtile + v_chunk_byte_offset(VFMT, tid, 12 * p));
+        dst[0] = w[3 * p];
+        dst[1] = w[3 * p + 1];
+        dst[2] = w[3 * p + 2];
+      }
     } else {
       uint32_t w[8];
 #pragma unroll

@@ -22,19 +22,27 @@ __host__ __device__ constexpr int v_chunk_bytes(int fmt) { return fmt == kFmtTur
 __host__ __device__ constexpr int v_tile_bytes(int fmt) { return 64 * v_chunk_bytes(fmt); }
 __host__ __device__ constexpr int levels(int fmt) { return fmt == kFmtTurbo3 ? 8 : 16; }
 
-// Byte order in memory.  turbo3 K records follow each other token by token (record
-// of token t at byte 48 t of its row) and turbo3 / fp16 V chunks chunk by chunk.
-// turbo4 bytes are stored in 16-byte pieces so that the 16 or 64 lanes reading the
-// same piece of neighbouring records / chunks read whole contiguous cache lines:
-// K records in blocks of 16 tokens, piece p (record bytes 16p..16p+15) of token
-// 16b + i at byte 1024 b + 256 p + 16 i; V chunk c's piece p (chunk bytes
-// 16p..16p+15) at tile byte 1024 p + 16 c.
+// Byte order in memory.  Quantised records and chunks are stored in pieces (turbo4:
+// 16 bytes, turbo3: 12 bytes, one sub-block) so that the lanes reading the same piece
+// of neighbouring records / chunks read whole contiguous cache lines:
+//  * turbo4 K, blocks of 16 tokens: piece p (record bytes 16p..16p+15) of token
+//    16b + i at byte 1024 b + 256 p + 16 i;
+//  * turbo3 K, blocks of 16 tokens: piece u (record bytes 12u..12u+11) of token
+//    16b + i at byte 768 b + 384 (u % 2) + 192 (u / 2) + 12 i, so pieces {0, 2} and
+//    {1, 3} each fill 384 contiguous bytes;
+//  * V chunk c's piece p at tile byte 1024 p + 16 c (turbo4) or 768 p + 12 c (turbo3);
+//  * fp16 K rows (256 bytes) and fp16 V chunks follow each other.
 __host__ __device__ inline size_t k_byte_offset(int fmt, size_t t, int byte) {
   if (fmt == kFmtTurbo4) return (t >> 4) * 1024 + size_t(byte >> 4) * 256 + (t & 15) * 16 + (byte & 15);
-  return t * size_t(fmt == kFmtTurbo3 ? 48 : 256) + byte;
+  if (fmt == kFmtTurbo3) {
+    const int u = byte / 12;
+    return (t >> 4) * 768 + size_t(384 * (u & 1) + 192 * (u >> 1)) + (t & 15) * 12 + byte % 12;
+  }
+  return t * 256 + byte;
 }
 __host__ __device__ inline int v_chunk_byte_offset(int fmt, int chunk, int byte) {
   if (fmt == kFmtTurbo4) return (byte >> 4) * 1024 + chunk * 16 + (byte & 15);
+  if (fmt == kFmtTurbo3) return (byte / 12) * 768 + chunk * 12 + byte % 12;
   return chunk * v_chunk_bytes(fmt) + byte;
 }
 

@@ -201,7 +201,6 @@ __device__ __forceinline__ void store_k_record(uint8_t* row_k, int t, const uint
   if (KFMT == kFmtTurbo4) {
     *reinterpret_cast<uint32_t*>(row_k + k_byte_offset(kFmtTurbo4, t, 4 * j)) = oct4_pack(code);
   } else {
-    uint8_t* rec = row_k + size_t(t) * k_record_bytes(KFMT);
     // Lanes 4q..4q+3 hold elements 8c..8c+7 (c = j % 4) of sub-block q.  Lanes with
     // c < 3 own word c outright (element 8c+i: byte i%4, bits 3*(i/4)); lane c = 3
     // holds elements 24..31, whose low two bits go to bits 6-7 of words A (24..27)
@@ -228,8 +227,8 @@ __device__ __forceinline__ void store_k_record(uint8_t* row_k, int t, const uint
     w[0] |= xor_lane16<2>(w[0]);
     w[1] |= xor_lane16<2>(w[1]);
     w[2] |= xor_lane16<2>(w[2]);
-    if ((j & 3) == 0) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(rec + 12 * (j >> 2));
+    if ((j & 3) == 0) {  // sub-block j / 4 is piece j / 4 of the record
+      uint32_t* dst = reinterpret_cast<uint32_t*>(row_k + k_byte_offset(kFmtTurbo3, t, 12 * (j >> 2)));
       dst[0] = w[0];
       dst[1] = w[1];
       dst[2] = w[2];
@@ -363,10 +362,14 @@ __device__ __forceinline__ uint16_t append_v_row(const EncodeArgs& a, size_t row
   if (VFMT == kFmtTurbo4) {  // two 16-byte pieces
     *reinterpret_cast<uint4*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 0)) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     *reinterpret_cast<uint4*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 16)) = make_uint4(cw[4], cw[5], cw[6], cw[7]);
-  } else {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 0));
+  } else {  // two 12-byte pieces (one sub-block each)
 #pragma unroll
-    for (int k = 0; k < v_chunk_bytes(VFMT) / 4; ++k) dst[k] = cw[k];
+    for (int p = 0; p < 2; ++p) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 12 * p));
+      dst[0] = cw[3 * p];
+      dst[1] = cw[3 * p + 1];
+      dst[2] = cw[3 * p + 2];
+    }
   }
   if (j == 0) a.v_norms[row * a.cap + t] = nbits;
   return nbits;

@@ -303,12 +303,13 @@ def test_v_tile_hand_worked_bytes():
     nz = np.nonzero(t)[0]
     assert list(nz) == [2010] and t[2010] == 0x10
     # turbo3: slot 2 = (g=0, i=2), dim 127 = (n=15, nb=7) -> chunk 15, element 58 = sub-block 1 element 26
-    # -> C word of that sub-block, bit 22 -> byte 15*24 + 12 + 8 + 2 = 382 = 0x40
+    # -> C word of that sub-block (piece bytes 8..11), bit 22 -> piece byte 10; piece 1 of chunk 15
+    # -> tile byte 768*1 + 12*15 + 10 = 958 = 0x40
     c = np.zeros((32, 128), dtype=int)
     c[2, 127] = 4
     t = codec.pack_v_tiles(c, "turbo3")[0]
     nz = np.nonzero(t)[0]
-    assert list(nz) == [382] and t[382] == 0x40
+    assert list(nz) == [958] and t[958] == 0x40
 
 
 def test_v_tile_slot_is_a_bijection():
@@ -337,15 +338,22 @@ def test_k_memory_order_hand_worked():
     mem = codec.k_records_to_memory(codec.pack_k_record(c, "turbo4"), "turbo4").reshape(-1)
     nz = np.nonzero(mem)[0]
     assert list(nz) == [2896] and mem[2896] == 0x20
-    # turbo3 records stay token by token: token 37's record starts at byte 37 * 48
+    # turbo3: token 37 = block 2, i = 5.  Dim 0 = sub-block 0 element 0 -> bits 0..2 of record byte 0,
+    # piece 0 -> memory byte 768*2 + 0 + 0 + 12*5 = 1596 holds 5.  Dim 100 = sub-block 3 element 4
+    # -> word A bits 3..5 -> record byte 36 = piece 3 byte 0 -> 768*2 + 384 + 192 + 12*5 = 2172 holds 5 << 3
     c3 = np.zeros((64, 128), dtype=int)
     c3[37, 0] = 5
     mem3 = codec.k_records_to_memory(codec.pack_k_record(c3, "turbo3"), "turbo3").reshape(-1)
-    assert list(np.nonzero(mem3)[0]) == [37 * 48] and mem3[37 * 48] == 5
+    assert list(np.nonzero(mem3)[0]) == [1596] and mem3[1596] == 5
+    c3 = np.zeros((64, 128), dtype=int)
+    c3[37, 100] = 5
+    mem3 = codec.k_records_to_memory(codec.pack_k_record(c3, "turbo3"), "turbo3").reshape(-1)
+    assert list(np.nonzero(mem3)[0]) == [2172] and mem3[2172] == 0x28
     # round trip
     rng = np.random.default_rng(2)
-    r = rng.integers(0, 256, (3, 48, 64), dtype=np.uint8)
-    np.testing.assert_array_equal(codec.k_memory_to_records(codec.k_records_to_memory(r, "turbo4"), "turbo4"), r)
+    for fmt, nbytes in (("turbo4", 64), ("turbo3", 48)):
+        r = rng.integers(0, 256, (3, 48, nbytes), dtype=np.uint8)
+        np.testing.assert_array_equal(codec.k_memory_to_records(codec.k_records_to_memory(r, fmt), fmt), r)
 
 
 @pytest.mark.parametrize("fmt,k", [("turbo3", 8), ("turbo4", 16)])

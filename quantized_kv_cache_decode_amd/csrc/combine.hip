@@ -14,7 +14,10 @@
 // keeps a running (m, l, o), and the four groups are merged with the gfx950 row
 // swaps (lane bit 4, then bit 5) -- no LDS, no barrier.  Every group then holds
 // the merged row in the 16-lane layout the in-register Walsh-Hadamard transform
-// wants; group 0 stores it.
+// wants; group 0 stores it.  When the call has few (sequence, head) rows (latency-
+// bound calls: a few dozen waves on a 256-CU chip), a row gets WAVES waves: lane group
+// sg of wave w takes splits 4w + sg, 4w + sg + 4 WAVES, ..., each wave merges its groups
+// as above, and wave 0 merges the waves' states through LDS (in wave order).
 #include <math.h>
 
 #include <algorithm>
@@ -22,11 +25,20 @@
 #include "tq_device.h"
 #include "tq_launch.h"
 
+#ifndef TQ_MERGE_FEW_ROWS
+#define TQ_MERGE_FEW_ROWS 256
+#endif
+#ifndef TQ_MERGE_ROW_WAVES
+#define TQ_MERGE_ROW_WAVES 4
+#endif
+
 namespace tq {
 namespace {
 
 constexpr int kGroups = 4;     // lane groups of 16 per wave
 constexpr int kMaxBatch = 17;  // splits per lane group per round (68 per round)
+constexpr int kFewRows = TQ_MERGE_FEW_ROWS;  // rows up to which a row gets kRowWaves waves
+constexpr int kRowWaves = TQ_MERGE_ROW_WAVES;
 
 __device__ inline float weight(float m, float M) { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M); }
 
@@ -77,8 +89,8 @@ __device__ inline Acc merge_across(const Acc& a) {
 
 // kBatch: splits per lane group per round, sized at launch to the call's longest
 // sequence so that short calls do not issue loads they then mask.
-template <bool INVERSE, int kBatch>
-__global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens) {
+template <bool INVERSE, int kBatch, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void combine_kernel(DecodeArgs a, SeqLens lens) {
   // No multiply-add contraction here: the normalised output must round the same
   // whether it goes to memory (then to the stand-alone inverse rotation) or
   // straight into the in-register rotation below.
@@ -93,7 +105,8 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens)
   const int nsplit = min((L + a.plan.chunk - 1) / a.plan.chunk, a.plan.max_splits);
   const int nparts = nsplit + (step ? 1 : 0);  // partial v lives in slot v, the step's last in slot max_splits
   const size_t p0 = partial_index(a, size_t(b) * a.hkv + h, 0, g);  // slot s: p0 + s*G
-  const int lane = threadIdx.x, j = lane & 15, sg = lane >> 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, sg = lane >> 4;
+  constexpr int kStride = kGroups * WAVES;  // lane groups of the work group
 
   // The V sign flips of this lane's 8 dims are requested first: the inverse rotation
   // at the end then waits for no memory round trip of its own.
@@ -115,7 +128,7 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens)
   acc.l = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc.o[i] = 0.f;
-  for (int s0 = sg; s0 < nparts; s0 += kGroups * kBatch) {
+  for (int s0 = kGroups * wave + sg; s0 < nparts; s0 += kStride * kBatch) {
     float ms[kBatch], ls[kBatch];
     float4 oa[kBatch], ob[kBatch];
     // Every load of the round is issued unconditionally (a partial past the end
@@ -123,7 +136,7 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens)
     // costs one memory round trip instead of one per partial.
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int v = s0 + kGroups * k;
+      const int v = s0 + kStride * k;
       const int slot = (v < nsplit ? v : a.plan.max_splits) * G;
       const float2 ml = *reinterpret_cast<const float2*>(ml_row + 2 * slot);
       const float4* src = reinterpret_cast<const float4*>(o_row + slot * kDim);
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens)
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {   // (branches the whole wave skips when every lane is in)
-      if (s0 + kGroups * k >= nparts) {
+      if (s0 + kStride * k >= nparts) {
         ms[k] = -INFINITY;
         ls[k] = 0.f;
         oa[k] = ob[k] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -159,7 +172,33 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens)
   }
 
   acc = merge_across<false>(acc);  // groups {0,1} and {2,3}
-  acc = merge_across<true>(acc);   // then the two halves: every lane holds the merged row
+  acc = merge_across<true>(acc);   // then the two halves: every lane holds the wave's merged row
+  if constexpr (WAVES > 1) {
+    __shared__ float st_o[WAVES][kDim];
+    __shared__ float st_ml[WAVES][2];
+    if (sg == 0) {
+      float4* d = reinterpret_cast<float4*>(&st_o[wave][8 * j]);
+      d[0] = make_float4(acc.o[0], acc.o[1], acc.o[2], acc.o[3]);
+      d[1] = make_float4(acc.o[4], acc.o[5], acc.o[6], acc.o[7]);
+      if (j == 0) {
+        st_ml[wave][0] = acc.m;
+        st_ml[wave][1] = acc.l;
+      }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {  // in wave order: every lane computes the same bits
+      Acc o;
+      o.m = st_ml[w][0];
+      o.l = st_ml[w][1];
+      const float4 x0 = reinterpret_cast<const float4*>(&st_o[w][8 * j])[0];
+      const float4 x1 = reinterpret_cast<const float4*>(&st_o[w][8 * j])[1];
+      o.o[0] = x0.x; o.o[1] = x0.y; o.o[2] = x0.z; o.o[3] = x0.w;
+      o.o[4] = x1.x; o.o[5] = x1.y; o.o[6] = x1.z; o.o[7] = x1.w;
+      acc = merge(acc, o);
+    }
+  }
   float v[8];
   const float inv = nparts > 0 ? 1.f / acc.l : 0.f;
 #pragma unroll
@@ -180,15 +219,15 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, SeqLens lens)
   }
 }
 
-template <bool INVERSE>
+template <bool INVERSE, int WAVES>
 void launch_batch(const DecodeArgs& a, const SeqLens& lens, int nb, int rounds, hipStream_t stream) {
-  const dim3 grid(a.hkv * a.group, nb), block(64);
-  if (rounds <= 1) hipLaunchKernelGGL((combine_kernel<INVERSE, 1>), grid, block, 0, stream, a, lens);
-  else if (rounds <= 2) hipLaunchKernelGGL((combine_kernel<INVERSE, 2>), grid, block, 0, stream, a, lens);
-  else if (rounds <= 3) hipLaunchKernelGGL((combine_kernel<INVERSE, 3>), grid, block, 0, stream, a, lens);
-  else if (rounds <= 5) hipLaunchKernelGGL((combine_kernel<INVERSE, 5>), grid, block, 0, stream, a, lens);
-  else if (rounds <= 9) hipLaunchKernelGGL((combine_kernel<INVERSE, 9>), grid, block, 0, stream, a, lens);
-  else hipLaunchKernelGGL((combine_kernel<INVERSE, kMaxBatch>), grid, block, 0, stream, a, lens);
+  const dim3 grid(a.hkv * a.group, nb), block(64 * WAVES);
+  if (rounds <= 1) hipLaunchKernelGGL((combine_kernel<INVERSE, 1, WAVES>), grid, block, 0, stream, a, lens);
+  else if (rounds <= 2) hipLaunchKernelGGL((combine_kernel<INVERSE, 2, WAVES>), grid, block, 0, stream, a, lens);
+  else if (rounds <= 3) hipLaunchKernelGGL((combine_kernel<INVERSE, 3, WAVES>), grid, block, 0, stream, a, lens);
+  else if (rounds <= 5) hipLaunchKernelGGL((combine_kernel<INVERSE, 5, WAVES>), grid, block, 0, stream, a, lens);
+  else if (rounds <= 9) hipLaunchKernelGGL((combine_kernel<INVERSE, 9, WAVES>), grid, block, 0, stream, a, lens);
+  else hipLaunchKernelGGL((combine_kernel<INVERSE, kMaxBatch, WAVES>), grid, block, 0, stream, a, lens);
 }
 
 }  // namespace
@@ -201,9 +240,17 @@ hipError_t launch_combine(const DecodeArgs& a, const SeqLens& lens, int batch, h
     most = std::max(most, std::min((L + a.plan.chunk - 1) / a.plan.chunk, a.plan.max_splits));
   }
   most += a.app.k_new != nullptr ? 1 : 0;
-  const int rounds = (most + kGroups - 1) / kGroups;
-  if (a.out) launch_batch<true>(a, lens, batch, rounds, stream);
-  else launch_batch<false>(a, lens, batch, rounds, stream);
+  // Few rows (at most kFewRows): kRowWaves waves per row share its splits.
+  const bool few = (long long)a.hkv * a.group * batch <= kFewRows;
+  const int groups = kGroups * (few ? kRowWaves : 1);
+  const int rounds = (most + groups - 1) / groups;
+  if (a.out) {
+    if (few) launch_batch<true, kRowWaves>(a, lens, batch, rounds, stream);
+    else launch_batch<true, 1>(a, lens, batch, rounds, stream);
+  } else {
+    if (few) launch_batch<false, kRowWaves>(a, lens, batch, rounds, stream);
+    else launch_batch<false, 1>(a, lens, batch, rounds, stream);
+  }
   return hipGetLastError();
 }
 

@@ -71,6 +71,8 @@ def parse(argv=None):
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--extra-cpu-seconds", type=float, default=5.0,
+                   help="budget of the oracle's timing on each of the other workloads (0 skips it)")
     p.add_argument("--no-extra", action="store_true", help="skip the per-workload records of the other workloads")
     p.add_argument("--v-skip-threshold", type=float, default=0.0,
                    help="sparse-V weight threshold of the decode calls (0 = exact attention)")
@@ -331,6 +333,23 @@ def time_calls(call, caches, n_calls):
     raise RuntimeError(f"the GPU sleep never outlasted the host's enqueueing of {n_calls} calls ({host_ms:.1f} ms)")
 
 
+def single_call_us(call, caches, n_calls=21):
+    """Latency of one call on its own: the GPU idle before it (synchronised), one HIP event pair
+    around it, a different cache copy each time; the median over n_calls (µs).  The events add
+    about 2 µs on calls this short."""
+    import torch
+    ts = []
+    for i in range(n_calls):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call(caches[(i + 1) % len(caches)])
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(ts))
+
+
 def calls_to_time(n_copies):
     """Back-to-back calls in one event-timed run: at least 8, at most 192 (more would fill the
     launch queue while the GPU sleeps, and the host would wait for the GPU), and no more than
@@ -387,8 +406,9 @@ def setup_copies(w, seed, copies_gib, min_copies=1):
     return caches, k_list, v_list, L, q_np
 
 
-def extra_workload(widx, seed, with_oracle, codebooks, ceiling_gbs):
-    """Call timing and parity of tq_decode_step on another workload (not the timed steps)."""
+def extra_workload(widx, seed, with_oracle, codebooks, ceiling_gbs, cpu_seconds):
+    """Call timing and parity of tq_decode_step on another workload (not the timed steps), and
+    the oracle's rate on the same workload (cpu_seconds of host time; 0 skips it)."""
     import torch
 
     import quantized_kv_cache_decode_amd as tq
@@ -413,15 +433,20 @@ def extra_workload(widx, seed, with_oracle, codebooks, ceiling_gbs):
     call_ms = time_calls(call, caches, n_calls)
     alg = algorithmic_bytes(w, L)
     achieved = alg / (call_ms * 1e-3) / 1e9
+    th = int(L.sum()) * w.num_kv_heads
     rec = {"call_us": call_ms * 1e3, "calls_timed": n_calls, "cache_copies": len(caches),
+           "single_call_us": single_call_us(call, caches),
            "algorithmic_bytes_per_call": alg, "achieved_GBs": achieved, "frac": achieved / HBM_PEAK_GBS,
            "frac_of_read_ceiling": achieved / ceiling_gbs,
-           "kv_token_heads_per_s": int(L.sum()) * w.num_kv_heads / (call_ms * 1e-3),
-           "traffic": recorded_traffic(w.name), "parity": None}
+           "kv_token_heads_per_s": th / (call_ms * 1e-3),
+           "q_token_heads_per_s": th * w.group / (call_ms * 1e-3),
+           "traffic": recorded_traffic(w.name), "parity": None, "cpu_baseline": None}
     if with_oracle:
         got = out.cpu().numpy()
         rec["parity"] = oracle_parity(caches[0], w, 0, int(L[0]), k_list[0], v_list[0], q_np[0], got[0],
                                       codebooks=codebooks)
+        if cpu_seconds > 0:
+            rec["cpu_baseline"], _ = cpu_baseline(w, widx, None, seed, cpu_seconds)
     del caches, k_list, v_list, kn, vn, q, out, ws
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -578,6 +603,7 @@ def main(argv=None):
     flush_infinity_cache()
     n_calls = calls_to_time(n_copies)
     dec_ms = time_calls(decode_call, caches, n_calls)
+    one_call_us = single_call_us(decode_call, caches)
     ms_per_step = (t1 - t0) * 1e3 / K
     token_heads = int(L.sum()) * w.num_kv_heads
     value = token_heads / (ms_per_step * 1e-3)
@@ -596,6 +622,7 @@ def main(argv=None):
             + " + combine_kernel)",
             "call_us": dec_ms * 1e3,
             "calls_timed": n_calls,
+            "single_call_us": one_call_us,
             "algorithmic_bytes_per_call": alg}
     exact = args.path != "chunk" and args.q_scale == 1.0 and not args.v_skip_threshold \
         and not args.k_skip_threshold
@@ -616,19 +643,23 @@ def main(argv=None):
     if not args.no_extra and args.workload == 1 and args.path == "step" and exact and not args.formats:
         del caches, k_list, v_list
         torch.cuda.empty_cache()
-        per_workload = {w.name: {"call_us": dec_ms * 1e3, "algorithmic_bytes_per_call": alg,
+        per_workload = {w.name: {"call_us": dec_ms * 1e3, "single_call_us": one_call_us,
+                                 "algorithmic_bytes_per_call": alg,
                                  "achieved_GBs": achieved, "frac": achieved / HBM_PEAK_GBS,
                                  "frac_of_read_ceiling": achieved / ceiling["achieved"],
                                  "kv_token_heads_per_s": token_heads / (dec_ms * 1e-3),
-                                 "traffic": roof["traffic"], "parity": parity}}
+                                 "q_token_heads_per_s": token_heads * w.group / (dec_ms * 1e-3),
+                                 "traffic": roof["traffic"], "parity": parity, "cpu_baseline": cpu}}
         for widx in EXTRA_WORKLOADS:
-            name, rec = extra_workload(widx, seed, not args.no_cpu_baseline, codebooks, ceiling["achieved"])
+            name, rec = extra_workload(widx, seed, not args.no_cpu_baseline, codebooks, ceiling["achieved"],
+                                       args.extra_cpu_seconds)
             per_workload[name] = rec
             print(f"bench.py: {name} {rec['call_us']:.1f} us per call, {rec['frac']:.3f} of 8 TB/s",
                   file=sys.stderr, flush=True)
     line = {
         "metric": METRIC, "value": value, "unit": "KV token-heads/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": ms_per_step,
+        "value_per_query_head": value * w.group,     # the same rate counted per query head (x G)
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u8 codes, f32 valu" if args.variant == 1 else "u8 codes, f16 mfma, f32 accumulate",
         "data": "synthetic (seeded; no model weights)",

@@ -91,6 +91,9 @@ tq_status check_lengths(const tq_cache* c, const int32_t* lens, int32_t extra) {
 #ifndef TQ_PLAN_FLOOR
 #define TQ_PLAN_FLOOR 200   // bandwidth-bound calls: chunk >= TQ_PLAN_FLOOR * group tokens
 #endif
+#ifndef TQ_PLAN_SHARE_BYTES
+#define TQ_PLAN_SHARE_BYTES (32LL << 10)     // small calls: a split streaming more than this keeps a unit to itself
+#endif
 
 // packed bytes per (token, KV head) of one side
 long long token_bytes(int fmt) { return fmt == TQ_FMT_TURBO3 ? 50 : fmt == TQ_FMT_TURBO4 ? 66 : 256; }
@@ -102,7 +105,11 @@ long long token_bytes(int fmt) { return fmt == TQ_FMT_TURBO3 ? 50 : fmt == TQ_FM
 // also even out ragged lengths).  Once the call is bandwidth-bound (>= 4M
 // token-heads) the chunk is also kept long enough that the partials (G x 130
 // floats, written then read) stay under ~4% of the packed bytes of the chunk.
-// Small calls (up to 32 MB of packed K and V) aim at one split per compute unit.
+// Small calls (up to 32 MB of packed K and V) aim at one split per compute unit; when a
+// split streams more than 32 KB (fp16 K), the decode step's two append work groups per row
+// are counted in, so that no two splits share a compute unit (two streaming waves on one
+// unit share its load pipe and both finish late: the fp16-K 16K step's slowest splits, on
+// its 257th-264th work groups and the units they share, ended 2 us after the median one).
 tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
   long long total = 0;
   int lmax = 0;
@@ -117,9 +124,16 @@ tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
   // small calls (a few tens of MB): about one work group per compute unit -- more
   // splits only add waves that compete for the same units' load pipes
   const long long bytes = total * (token_bytes(c->k_format) + token_bytes(c->v_format));
-  if (!bandwidth_bound && bytes <= TQ_PLAN_LATENCY_BYTES)
+  const long long tok_bytes = token_bytes(c->k_format) + token_bytes(c->v_format);
+  auto round_chunk = [](long long ch) { return std::max((long long)TQ_PLAN_MIN_CHUNK, (ch + 63) / 64 * 64); };
+  if (!bandwidth_bound && bytes <= TQ_PLAN_LATENCY_BYTES) {
     chunk = std::max(chunk, (total + TQ_PLAN_LATENCY_ITEMS - 1) / TQ_PLAN_LATENCY_ITEMS);
-  chunk = std::max((long long)TQ_PLAN_MIN_CHUNK, (chunk + 63) / 64 * 64);
+    const long long rows = (long long)c->batch * c->num_kv_heads;
+    const long long items = TQ_PLAN_LATENCY_ITEMS - 2 * rows;
+    if (round_chunk(chunk) * tok_bytes > TQ_PLAN_SHARE_BYTES && items >= TQ_PLAN_LATENCY_ITEMS / 2)
+      chunk = std::max(chunk, (total + items - 1) / items);
+  }
+  chunk = round_chunk(chunk);
   tq::DecodePlan p;
   p.chunk = (int)chunk;
   p.max_splits = std::max(1, (int)((lmax + chunk - 1) / chunk));

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
       double beta[levels(VQ) - 1];
       load_row_and_signs(a.v_new + src_off, a.v_signs, j, w4, sg);
       load_thresholds<VQ>(a.v_cb, beta);
-      const uint16_t nbits = encode_row<VQ>(w4, sg, beta, j, code);
+      const uint16_t nbits = encode_row<VQ, true>(w4, sg, beta, j, code);
       *reinterpret_cast<uint2*>(&vcodes[r][8 * j]) =
           make_uint2(uint32_t(code[0]) | uint32_t(code[1]) << 8 | uint32_t(code[2]) << 16 | uint32_t(code[3]) << 24,
                      uint32_t(code[4]) | uint32_t(code[5]) << 8 | uint32_t(code[6]) << 16 | uint32_t(code[7]) << 24);
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
       double beta[levels(KQ) - 1];
       load_row_and_signs(a.k_new + src_off, a.k_signs, j, w4, sg);
       load_thresholds<KQ>(a.k_cb, beta);
-      const uint16_t nbits = encode_row<KQ>(w4, sg, beta, j, code);
+      const uint16_t nbits = encode_row<KQ, true>(w4, sg, beta, j, code);
       if (j == 0) a.k_norms[slot] = nbits;
       store_k_record<KQ>(a.k_data + row * a.cap * k_record_bytes(KQ), t, code, j);
     }

@@ -110,10 +110,27 @@ __device__ __forceinline__ uint16_t exact_row_norm_fp16(const uint32_t (&w4)[4])
   return exact_norm_fp16(sA, sB, sC);
 }
 
+// Value of lane (lane ^ M) of the 16-lane row for a binary64 value.  LDS_EXCHANGE: xor 4
+// and 8 through ds_swizzle (one LDS-pipe instruction per 32-bit half, no VALU slot)
+// instead of two DPP moves per half -- for throughput-bound callers whose many
+// independent exchanges hide the LDS pipe's latency; xor 1 and 2 stay single DPP moves.
+template <int M, bool LDS_EXCHANGE>
+__device__ __forceinline__ double exchange_lane16(double v) {
+  if constexpr (LDS_EXCHANGE && (M == 4 || M == 8)) {
+    constexpr int kPattern = 0x1f | (M << 10);   // bit mode: lane ^ M within each group of 32
+    const uint64_t u = uint64_t(__double_as_longlong(v));
+    const uint32_t lo = uint32_t(__builtin_amdgcn_ds_swizzle(int(uint32_t(u)), kPattern));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_ds_swizzle(int(uint32_t(u >> 32)), kPattern));
+    return __longlong_as_double(int64_t(uint64_t(lo) | (uint64_t(hi) << 32)));
+  } else {
+    return xor_lane16<M>(v);
+  }
+}
+
 // Encode one 128-element row held by a 16-lane group (lane j: elements 8j..8j+7,
 // fp16 bits in w4, sign flips in sg).  Returns the fp16 norm bits (the same in all
 // 16 lanes) and this lane's 8 codes.  All 16 lanes of the group execute it together.
-template <int FMT>
+template <int FMT, bool LDS_EXCHANGE = false>
 __device__ __forceinline__ uint16_t encode_row(const uint32_t (&w4)[4], const float (&sg)[8],
                                       const double (&beta)[levels(FMT) - 1], int j, uint8_t (&code)[8]) {
   double x[8];
@@ -126,7 +143,7 @@ __device__ __forceinline__ uint16_t encode_row(const uint32_t (&w4)[4], const fl
   }
   auto sum_stage = [&](auto m_c) {
     constexpr int M = decltype(m_c)::value;
-    ss += xor_lane16<M>(ss);   // both lanes of a pair add the same two values: identical sums
+    ss += exchange_lane16<M, LDS_EXCHANGE>(ss);   // both lanes of a pair add the same two values: identical sums
   };
   sum_stage(std::integral_constant<int, 1>{});
   sum_stage(std::integral_constant<int, 2>{});
@@ -149,7 +166,7 @@ __device__ __forceinline__ uint16_t encode_row(const uint32_t (&w4)[4], const fl
     const double sgn = (j & M) ? -1.0 : 1.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double o = xor_lane16<M>(x[e]);
+      const double o = exchange_lane16<M, LDS_EXCHANGE>(x[e]);
       x[e] = fma(x[e], sgn, o);  // o - x or x + o, exactly
     }
   };

@@ -267,3 +267,32 @@ def test_noalloc_step_checks_before_touching_the_device(lib):
                                       None) == binding.TQ_EINVAL
     assert lib.tq_decode_step_noalloc(ctypes.byref(d), p, q, q, q, 0, 3, ctypes.c_float(0.1), q, None) == \
         binding.TQ_EINVAL
+
+
+@pytest.mark.parametrize("k_format,v_format,L,slots", [
+    # turbo3 8K layer: 32768 token-heads over 256 work items -> 128-token splits (12.8 KB of
+    # packed K+V each), 64 per row, plus the step's slot
+    (3, 3, 8192, 65),
+    # fp16-K 16K layer: 256-token splits would stream 82 KB each, so the decode step's two
+    # append groups per row are counted in: 248 items -> ceil(65536 / 248) = 265 tokens,
+    # rounded up to 320 -> 52 splits per row, plus the step's slot
+    (0, 4, 16384, 53),
+])
+def test_latency_plan_split_counts(lib, k_format, v_format, L, slots):
+    """The small-call split plan, read off the workspace size (B*Hkv*slots*G partials of
+    130 floats): one work group per compute unit, the append groups included when a split
+    streams more than 32 KB."""
+    fake = 0x10000
+    d = _desc(batch=1, num_kv_heads=4, capacity=16384, k_format=k_format, v_format=v_format,
+              k_norms=fake if k_format else 0)
+    a, p = _lens(L)
+    assert lib.tq_decode_workspace_size(ctypes.byref(d), 28, p) == 1 * 4 * slots * 7 * 130 * 4
+
+
+def test_latency_plan_keeps_its_items_when_rows_are_many(lib):
+    """With 2 append groups per row taking half the units or more, the plan does not shrink:
+    64 sequences x 2 KV heads of 512 fp16-K tokens (65536 token-heads, 21 MB) -> 256 items of
+    256 tokens (82 KB each), 2 per row, plus the step's slot."""
+    d = _desc(batch=64, num_kv_heads=2, capacity=512, k_format=0, v_format=4, k_norms=0)
+    a, p = _lens(*([512] * 64))
+    assert lib.tq_decode_workspace_size(ctypes.byref(d), 4, p) == 64 * 2 * 3 * 2 * 130 * 4

@@ -340,6 +340,21 @@ def test_full_size_sampled(index, codebooks):
         assert rel <= S.REL_L2_TOL and mx <= S.MAX_ABS_TOL, f"b={b}: rel-L2 {rel:.3e} max-abs {mx:.3e}"
 
 
+@pytest.mark.parametrize("variant", [0, "fused"])
+def test_one_row_of_many_splits(variant, codebooks):
+    """One (sequence, KV head) row of 262144 turbo4 tokens (35 MB: past the small-call plan,
+    short of the bandwidth-bound one) is cut into 2048 splits of 128 tokens: the merge gives the
+    row four waves (few rows) and each lane group folds 2048 / 16 = 128 partials over eight load
+    rounds of 17."""
+    w = S.scaled(get_workload(3), batch=1, num_kv_heads=1, num_q_heads=4)
+    lens = np.array([262144])
+    _say("[one row of many splits] generating + encoding")
+    cache, k_list, v_list, L, q = S.prefill_and_step(w, lengths=lens)
+    got = S.gpu_decode(cache, q, variant=variant)
+    rel, mx = S.assert_close(got[0], S.oracle_on_bytes(cache, 0, int(L[0]), q[0], codebooks), "on GPU bytes")
+    _say(f"[one row of many splits v{variant}] rel-L2 {rel:.2e} max-abs {mx:.2e}")
+
+
 @pytest.mark.timeout(600)
 def test_bandwidth_bound_step_edge_rows(codebooks):
     """A step large enough (>= 4M token-heads) that the row's first two splits append the token,

@@ -30,14 +30,16 @@ Byte layouts (the pages print none; these are this library's):
         C[8j+7] = c[28+j] >> 2
   * K record (one per token and KV head): turbo3 48 bytes = 4 sub-blocks for
     dims 32q..32q+31; turbo4 64 bytes = 16 octet words for dims 8w..8w+7.  In
-    memory turbo3 records follow each other token by token; turbo4 records are
-    kept in blocks of 16 tokens, 16-byte piece p (words 4p..4p+3) of the block's
-    token i at byte 256 p + 16 i of the block's 1024 bytes.
+    memory both are kept in blocks of 16 tokens, as pieces: turbo4 16-byte piece p
+    (words 4p..4p+3) of the block's token i at byte 256 p + 16 i of the block's 1024
+    bytes; turbo3 12-byte piece q (sub-block q) of token i at byte
+    384 (q % 2) + 192 (q // 2) + 12 i of the block's 768 bytes.
   * V tile (32 tokens of one KV head, token-tiled): 64 chunks, chunk 16g + n
     holds the 8 tokens of slot group g and the 8 dims 8n..8n+7; element
     e = 8*nb + i of a chunk is dim 8n + nb of the token in tile slot
     r = 16*(i // 4) + 4*g + (i % 4).  turbo3 chunk = 2 sub-blocks (24 bytes,
-    elements 0..31 then 32..63), chunk c at tile byte 24 c; turbo4 chunk = 8 octet
+    elements 0..31 then 32..63), sub-block p of chunk c at tile byte 768 p + 12 c;
+    turbo4 chunk = 8 octet
     words (32 bytes), word nb holding elements 8nb..8nb+7, stored as two 16-byte
     pieces: piece p (words 4p..4p+3) of chunk c at tile byte 1024 p + 16 c.  Tile =
     1536 (turbo3) or 2048 (turbo4) bytes.

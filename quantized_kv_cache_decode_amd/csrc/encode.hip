@@ -5,10 +5,10 @@
 // encode_append_kernel (any number of rows): one workgroup per (32-token V tile
 // touched by the append, KV head, sequence).  256 threads = 16 groups of 16
 // lanes; each group encodes one K or V row of a new token of the tile (lane j
-// holds dims 8j..8j+7).  K rows are written as token-major records; V codes are
-// staged in LDS and written as whole V-tile chunk words by one thread per chunk,
-// merging with the words of tokens already in the tile.  F16 K rows are copied
-// unchanged.
+// holds dims 8j..8j+7).  K records are written piece by piece into their 16-token
+// blocks; V codes are staged in LDS and written as whole V-tile chunk pieces by one
+// thread per chunk, merging with the words of tokens already in the tile.  F16 K
+// rows are copied unchanged.
 //
 // append_one_kernel (the decode step: at most one row per sequence): one 16-lane
 // group per row; waves 0-1 of a block encode the K rows of 8 (sequence, KV head)

@@ -233,6 +233,7 @@ def cpu_baseline(w, widx, formats, seed, budget_s):
              for h in range(H) for i in range(blocks)]
     ctx = mp.get_context("spawn")     # fresh interpreters: the parent holds a GPU context
     barrier, results = ctx.Barrier(len(tasks)), ctx.Queue()
+    wall0 = time.perf_counter()
     procs = [ctx.Process(target=_oracle_unit, args=(t, barrier, results), daemon=True) for t in tasks]
     for p in procs:
         p.start()
@@ -248,6 +249,7 @@ def cpu_baseline(w, widx, formats, seed, budget_s):
                 raise RuntimeError(f"CPU baseline workers failed (exit codes {dead}) or timed out")
     for p in procs:
         p.join(timeout=60)
+    wall_s = time.perf_counter() - wall0
     got.sort(key=lambda r: r[0])
     rate = sum(r[1] * r[3] / r[2] for r in got)        # token-heads per second (one KV head per unit)
     o = np.concatenate([att.combine([got[h * blocks + i][4] for i in range(blocks)]) for h in range(H)])
@@ -258,6 +260,7 @@ def cpu_baseline(w, widx, formats, seed, budget_s):
         "cores": len(procs),
         "host_cores": host_cores,
         "kind": "oracle",
+        "wall_s": wall_s,          # the pool's whole run: start-up, unit set-up, the timed repetitions
         "sample": f"sequence 0 of {w.name}: append 1 token + float64 full-dequant attention over {L} tokens x "
                   f"{H} KV heads x {w.group} query heads each, as {len(procs)} single-threaded worker processes "
                   f"(one per (KV head, token block) unit, {blocks} blocks per head), {budget_s:.0f} s each, "

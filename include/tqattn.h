@@ -131,10 +131,14 @@ typedef enum {
  *            are still read (bandwidth is not saved, VALU and MFMA work is).  It has
  *            no effect with F16 K (no stored norms) or in the VALU reference
  *            variant; the first iteration of every split is never skipped.
- * capacity must be a positive multiple of 32; head_dim must be 128.
+ * capacity must be a positive multiple of 32 and at most TQ_MAX_CAPACITY (2^24
+ * tokens: the decode kernel addresses one (sequence, KV head) row of quantised
+ * K records, V tiles and norms with 32-bit byte offsets); head_dim must be 128.
  * The decode kernels read whole 32-token tiles and mask the slots at or past a
  * sequence's length, whose V norms are multiplied by an exact zero weight: they
  * must hold finite fp16 values (zero-fill the arrays when allocating them). */
+#define TQ_MAX_CAPACITY (1 << 24)
+
 typedef struct tq_cache {
   int32_t batch;
   int32_t num_kv_heads;

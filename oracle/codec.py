@@ -9,7 +9,7 @@ and is reconstructed as  x_hat = s * H (n * c[idx]) / sqrt(128).
 item 1: dequant is "index -> table[index] x norm"; mlxcel PR #369 "Change":
 the codes live in the WHT-rotated basis.)
 
-Readings where the pages are silent (all listed in the design notes):
+Readings where the pages are silent:
   * the norm is the exact real ||x||_2 rounded to nearest-even fp16, saturated
     at 65504; it is computed here with integers, so no summation order matters;
   * decisions compare y_i against n * beta_j, beta_j the midpoints of adjacent

@@ -36,6 +36,9 @@ tq_status check_cache(const tq_cache* c) {
   if (c->head_dim != 128) return fail(TQ_EUNSUPPORTED, "head_dim %d: only 128 is supported", c->head_dim);
   if (c->batch <= 0 || c->num_kv_heads <= 0) return fail(TQ_EINVAL, "batch and num_kv_heads must be positive");
   if (c->capacity <= 0 || c->capacity % 32) return fail(TQ_EINVAL, "capacity %d must be a positive multiple of 32", c->capacity);
+  if (c->capacity > TQ_MAX_CAPACITY)
+    return fail(TQ_EINVAL, "capacity %d exceeds %d (a row's quantised K and V bytes must stay under 2^31)", c->capacity,
+                TQ_MAX_CAPACITY);
   if (!is_turbo(c->k_format) && c->k_format != TQ_FMT_F16)
     return fail(TQ_EUNSUPPORTED, "k_format %d: must be F16, TURBO3 or TURBO4", c->k_format);
   if (!is_turbo(c->v_format) && !(c->v_format == TQ_FMT_F16 && c->k_format == TQ_FMT_F16))

@@ -43,7 +43,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Build-time tuning knobs (defaults are the measured best; see the design notes).
+// Build-time tuning knobs (the defaults are the measured best).
 #ifndef TQ_MFMA_NS_SMALL_GROUP
 #define TQ_MFMA_NS_SMALL_GROUP 4   // token sets per MFMA for group sizes <= 4 (4 or 2)
 #endif
@@ -121,6 +121,25 @@ __device__ inline half8 dq_turbo4(uint32_t w, const ByteTable& mag) {
                perm(hiB, loB, 0x07030602u));
 }
 
+// Norm scaling in one instruction instead of a convert and a multiply: an fma with a
+// +0 addend, which the compiler emits as a mixed-precision v_fma_mix* reading the
+// fp16 half of w directly (the product is rounded once; a -0 product becomes +0).
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+// x times the fp16 half HI of w
+template <int HI>
+__device__ inline float mul_half(float x, uint32_t w) {
+  const half2v h = __builtin_bit_cast(half2v, w);
+  return __builtin_fmaf(x, float(HI ? h.y : h.x), 0.f);
+}
+// the fp16 pair (lo * half 0 of w, hi * half 1 of w)
+__device__ inline uint32_t mul_halves_pack(float lo, float hi, uint32_t w) {
+  const half2v h = __builtin_bit_cast(half2v, w);
+  half2v r;
+  r.x = _Float16(__builtin_fmaf(lo, float(h.x), 0.f));
+  r.y = _Float16(__builtin_fmaf(hi, float(h.y), 0.f));
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 __device__ inline floatx4 mfma(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -166,16 +185,23 @@ __device__ inline void load_words(uint32_t (&w)[N], const uint8_t* p) {
   }
 }
 
-// NP 16-byte pieces at p, p + stride, ... (turbo4 K records and V chunks): every
-// piece load of the wave reads whole contiguous cache lines, and each byte once, so
-// the loads are non-temporal.
+// Quantised K/V words are read through a buffer resource over the (sequence, KV head)
+// row -- its base in SGPRs, a 32-bit byte offset per lane (capacity is capped so a
+// row's bytes stay under 2^31) -- which keeps 64-bit address arithmetic out of the
+// loop.  Reads past the resource's size would return zeros; the kernel's never do.
+__device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+constexpr int kNonTemporal = 2;   // buffer-load cache-policy bits: nt (each byte is read once)
+
+// NP 16-byte pieces at off, off + stride, ... (turbo4 K records and V chunks): every
+// piece load of the wave reads whole contiguous cache lines.
 template <int NP, int N>
-__device__ inline void load_pieces(uint32_t (&w)[N], const uint8_t* p, size_t stride) {
+__device__ inline void load_pieces16(uint32_t (&w)[N], __amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t stride) {
   static_assert(N == 4 * NP, "four words per piece");
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * stride));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + i * stride, 0, kNonTemporal);
     w[4 * i] = v.x;
     w[4 * i + 1] = v.y;
     w[4 * i + 2] = v.z;
@@ -183,34 +209,39 @@ __device__ inline void load_pieces(uint32_t (&w)[N], const uint8_t* p, size_t st
   }
 }
 
-// turbo3: the 4/P 12-byte pieces (sub-blocks) u0, u0 + 1, ... of this lane's token in
-// a 16-token K block at p (piece u at p + 384 (u % 2) + 192 (u / 2)), and the two pieces
-// of this lane's V chunk at p and p + 768.  Each load of the wave reads whole cache
-// lines, each byte once.
+// turbo3: the NP 12-byte pieces (sub-blocks) u0, u0 + 1, ... of this lane's token in
+// a 16-token K block at off (piece u at off + 384 (u % 2) + 192 (u / 2)), and the two
+// pieces of this lane's V chunk at off and off + 768.  Each load of the wave reads
+// whole cache lines.
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 template <int NP, int N>
-__device__ inline void load_k3_pieces(uint32_t (&w)[N], const uint8_t* p, int u0) {
+__device__ inline void load_k3_pieces(uint32_t (&w)[N], __amdgpu_buffer_rsrc_t r, uint32_t off, int u0) {
   static_assert(N == 3 * NP, "three words per piece");
-  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int u = u0 + i;
-    const u32x3 v = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(p + 384 * (u & 1) + 192 * (u >> 1)));
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 384 * (u & 1) + 192 * (u >> 1), 0, kNonTemporal);
     w[3 * i] = v.x;
     w[3 * i + 1] = v.y;
     w[3 * i + 2] = v.z;
   }
 }
 template <int N>
-__device__ inline void load_v3_pieces(uint32_t (&w)[N], const uint8_t* p) {
+__device__ inline void load_v3_pieces(uint32_t (&w)[N], __amdgpu_buffer_rsrc_t r, uint32_t off) {
   static_assert(N == 6, "two pieces of three words");
-  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const u32x3 v = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(p + 768 * i));
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 768 * i, 0, kNonTemporal);
     w[3 * i] = v.x;
     w[3 * i + 1] = v.y;
     w[3 * i + 2] = v.z;
   }
+}
+// four fp16 norms at byte offset off
+__device__ inline uint2 load_norms4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v.x, v.y);
 }
 
 template <int N>
@@ -454,15 +485,20 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
   // every column sees the tokens before t_all.
   const int t_all = min(t1, L - (a.q_len - 1));
   const int t_col = min(t1, L - (a.q_len - 1 - hn % a.q_len));
-  // Quantised K: this lane's pieces part*(4/P) .. of token n of each 16-token block;
-  // quantised V: pieces 0 and 1 of chunk `lane` of each tile; fp16: its contiguous share
-  const uint8_t* kbase = KFMT == kFmtTurbo4   ? a.k_data + row * size_t(a.cap) * REC + n * 16 + part * (4 / P) * 256
-                         : KFMT == kFmtTurbo3 ? a.k_data + row * size_t(a.cap) * REC + n * 12
-                                              : a.k_data + row * size_t(a.cap) * REC + part * (REC / P);
-  const uint8_t* vbase = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT) +
-                         (VFMT == kFmtTurbo4 ? lane * 16 : VFMT == kFmtTurbo3 ? lane * 12 : lane * (VW * 4));
-  const uint16_t* knorm = KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap);
-  const uint16_t* vnorm = VFMT == kFmtF16 ? nullptr : a.v_norms + row * size_t(a.cap);
+  // The row's K records and V tiles: fp16 K/V by pointer (this lane's contiguous share);
+  // quantised K/V and norms through buffer resources over the row, with this lane's
+  // offsets (K: pieces part*(4/P) .. of token n of each 16-token block; V: pieces 0
+  // and 1 of chunk `lane` of each tile)
+  const uint8_t* krow = a.k_data + row * size_t(a.cap) * REC;
+  const uint8_t* vrow = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT);
+  const uint8_t* kbase = krow + part * (REC / P);
+  const uint8_t* vbase = vrow + lane * (VW * 4);
+  const __amdgpu_buffer_rsrc_t krs = row_rsrc(krow, uint32_t(a.cap) * REC);
+  const __amdgpu_buffer_rsrc_t vrs = row_rsrc(vrow, uint32_t(a.cap / kTileTokens) * v_tile_bytes(VFMT));
+  const __amdgpu_buffer_rsrc_t knrs = row_rsrc(KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap), uint32_t(a.cap) * 2);
+  const __amdgpu_buffer_rsrc_t vnrs = row_rsrc(VFMT == kFmtF16 ? nullptr : a.v_norms + row * size_t(a.cap), uint32_t(a.cap) * 2);
+  const uint32_t k_lane = KFMT == kFmtTurbo4 ? n * 16 + part * (4 / P) * 256 : n * 12;
+  const uint32_t v_lane = VFMT == kFmtTurbo4 ? lane * 16 : lane * 12;
   __shared__ float qs[kMaxGroup][kDim];
   if (append_wg) {
     // The append is one long dependent chain (binary64 butterflies, exact norm,
@@ -498,29 +534,29 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
     const int tk = min((base >> 5) + sig, last_tile) << 5;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      if constexpr (KFMT == kFmtTurbo4) load_pieces<KW / 4>(kw[rb], kbase + size_t((tk >> 4) + rb) * 1024, 256);
+      if constexpr (KFMT == kFmtTurbo4) load_pieces16<KW / 4>(kw[rb], krs, k_lane + uint32_t((tk >> 4) + rb) * 1024, 256);
       else if constexpr (KFMT == kFmtTurbo3)
-        load_k3_pieces<KW / 3>(kw[rb], kbase + size_t((tk >> 4) + rb) * 768, part * (4 / P));
+        load_k3_pieces<KW / 3>(kw[rb], krs, k_lane + uint32_t((tk >> 4) + rb) * 768, part * (4 / P));
       else load_words(kw[rb], kbase + size_t(tk + 16 * rb + n) * REC);
     }
     if (KFMT != kFmtF16) {
       const int tn = min((base >> 5) + sn, last_tile) << 5;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) nk[rb] = *reinterpret_cast<const uint2*>(knorm + tn + 16 * rb + 4 * g);
+      for (int rb = 0; rb < 2; ++rb) nk[rb] = load_norms4(knrs, uint32_t(tn + 16 * rb + 4 * g) * 2);
     }
   };
   auto load_v = [&](int base) {
 #pragma unroll
     for (int sg = 0; sg < NS; ++sg) {
-      const uint8_t* tile = vbase + size_t(min((base >> 5) + sg, last_tile)) * v_tile_bytes(VFMT);
-      if constexpr (VFMT == kFmtTurbo4) load_pieces<2>(vw[sg], tile, 1024);
-      else if constexpr (VFMT == kFmtTurbo3) load_v3_pieces(vw[sg], tile);
-      else load_words(vw[sg], tile);
+      const int tile = min((base >> 5) + sg, last_tile);
+      if constexpr (VFMT == kFmtTurbo4) load_pieces16<2>(vw[sg], vrs, v_lane + uint32_t(tile) * v_tile_bytes(VFMT), 1024);
+      else if constexpr (VFMT == kFmtTurbo3) load_v3_pieces(vw[sg], vrs, v_lane + uint32_t(tile) * v_tile_bytes(VFMT));
+      else load_words(vw[sg], vbase + size_t(tile) * v_tile_bytes(VFMT));
     }
     const int tn = min((base >> 5) + sn, last_tile) << 5;
     if (VFMT != kFmtF16) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) nv[rb] = *reinterpret_cast<const uint2*>(vnorm + tn + 16 * rb + 4 * g);
+      for (int rb = 0; rb < 2; ++rb) nv[rb] = load_norms4(vnrs, uint32_t(tn + 16 * rb + 4 * g) * 2);
     }
   };
   // q rows first, then the first iteration's words: waiting for q (the oldest
@@ -600,18 +636,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
 
   // Scores of the TOK tokens from `base` (log2 units, K norms applied, not yet
   // masked) into S; the next iteration's K words and norms are requested as soon
-  // as this one's are turned into MFMA operands.
+  // as this one's are turned into MFMA operands and the norms applied (the norms
+  // are read straight from their fp16 words, whose registers the request reuses).
   auto score_phase = [&](int base, floatx4 (&S)[2]) {
     // ---- scores (dequant of each operand right before its MFMA)
-    float z[8];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = j < 2 ? nk[rb].x : nk[rb].y;
-        z[4 * rb + j] = KFMT != kFmtF16 ? half_bits_to_float(uint16_t(w >> (16 * (j & 1)))) : 1.f;
-      }
-    }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       S[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -636,12 +664,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
         S[rb] = mfma(A, qk, S[rb]);
       }
     }
-    load_k(base + TOK);     // next iteration's K words and K norms
+    if constexpr (KFMT != kFmtF16) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[rb][j] *= z[4 * rb + j];
+      for (int rb = 0; rb < 2; ++rb) {
+        S[rb][0] = mul_half<0>(S[rb][0], nk[rb].x);
+        S[rb][1] = mul_half<1>(S[rb][1], nk[rb].x);
+        S[rb][2] = mul_half<0>(S[rb][2], nk[rb].y);
+        S[rb][3] = mul_half<1>(S[rb][3], nk[rb].y);
+      }
     }
+    load_k(base + TOK);     // next iteration's K words and K norms
   };
 
   // Softmax and values of the TOK tokens from `base` whose scores are in S.  TAIL:
@@ -675,22 +707,20 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
     m_run = m_new;
     // p = 2^(z - m); a masked slot has z = -inf and p = +0 exactly, and so does
     // p * n_V (norms are finite), so no select is needed.
-    float psum = 0.f;
+    float pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_use);
+    float psum = pr[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) psum += pr[i];
     half8 pb;
+    if constexpr (VFMT == kFmtF16) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * rb + j;
-        const float p = __builtin_amdgcn_exp2f(z[i] - m_use);
-        psum += p;
-        if constexpr (VFMT == kFmtF16) {
-          pb[i] = _Float16(p);
-        } else {
-          const uint32_t w = j < 2 ? nv[rb].x : nv[rb].y;
-          pb[i] = _Float16(p * half_bits_to_float(uint16_t(w >> (16 * (j & 1)))));
-        }
-      }
+      for (int i = 0; i < 8; ++i) pb[i] = _Float16(pr[i]);
+    } else {
+      const uint32_t pw[4] = {mul_halves_pack(pr[0], pr[1], nv[0].x), mul_halves_pack(pr[2], pr[3], nv[0].y),
+                              mul_halves_pack(pr[4], pr[5], nv[1].x), mul_halves_pack(pr[6], pr[7], nv[1].y)};
+      pb = pack8(pw[0], pw[1], pw[2], pw[3]);
     }
     l_run += psum;
 

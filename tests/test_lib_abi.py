@@ -67,6 +67,7 @@ def _err(lib):
     (dict(head_dim=64), binding.TQ_EUNSUPPORTED),
     (dict(capacity=48), binding.TQ_EINVAL),
     (dict(capacity=0), binding.TQ_EINVAL),
+    (dict(capacity=(1 << 24) + 32), binding.TQ_EINVAL),
     (dict(v_format=0), binding.TQ_EUNSUPPORTED),
     (dict(k_format=7), binding.TQ_EUNSUPPORTED),
     (dict(v_data=0), binding.TQ_EINVAL),

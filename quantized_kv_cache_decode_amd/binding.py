@@ -21,6 +21,7 @@ TQ_FMT = {"f16": 0, "turbo3": 3, "turbo4": 4}
 K_RECORD_BYTES = {"turbo3": 48, "turbo4": 64}
 V_TILE_BYTES = {"turbo3": 1536, "turbo4": 2048, "f16": 8192}
 NOALLOC_SCRATCH_BYTES = 64 << 20   # TQ_NOALLOC_SCRATCH_BYTES: the no-allocation step's partials, per GPU
+MAX_CAPACITY = 1 << 24             # TQ_MAX_CAPACITY: tokens per (sequence, KV head) row
 EXPORTED = (
     "tq_encode_append", "tq_rotate_q", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_decode_attention_variant", "tq_decode_attention_fused", "tq_decode_chunk_fused", "tq_decode_step",
@@ -162,8 +163,8 @@ class Cache:
 
     def __init__(self, batch, num_kv_heads, capacity, k_format, v_format, k_signs, v_signs, device="cuda"):
         import torch
-        if capacity % 32:
-            raise ValueError("capacity must be a multiple of 32")
+        if capacity <= 0 or capacity % 32 or capacity > MAX_CAPACITY:
+            raise ValueError(f"capacity {capacity} must be a positive multiple of 32, at most {MAX_CAPACITY}")
         self.batch, self.num_kv_heads, self.capacity = batch, num_kv_heads, capacity
         self.k_format, self.v_format = k_format, v_format
         dev = torch.device(device)

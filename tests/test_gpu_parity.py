@@ -355,6 +355,46 @@ def test_one_row_of_many_splits(variant, codebooks):
     _say(f"[one row of many splits v{variant}] rel-L2 {rel:.2e} max-abs {mx:.2e}")
 
 
+@pytest.mark.parametrize("variant", [0, "fused"])
+@pytest.mark.parametrize("fmt,hq", [("turbo4", 4), ("turbo3", 8)])
+def test_row_at_maximum_capacity(fmt, hq, variant, codebooks):
+    """A (sequence, KV head) row at the largest capacity the library accepts (2^24 tokens; the
+    decode kernel addresses a row's K records, V tiles and norms with 32-bit byte offsets, here
+    up to 2^30).  A 256-token block is encoded once and its bytes copied over the whole row on
+    the device, with the V norms of every odd copy doubled (exact in fp16).  The copies' keys
+    are identical, so are their softmax weights, and attention over all 2^24 tokens is 1.5
+    times the oracle's attention over the one block; a read that lands on the wrong copy, or
+    past the row (zeros), shows in that factor."""
+    import torch
+
+    import quantized_kv_cache_decode_amd as tq
+    cap, blk = tq.binding.MAX_CAPACITY, 256
+    w = S.scaled(get_workload(0), batch=1, num_kv_heads=1, num_q_heads=hq, k_format=fmt, v_format=fmt)
+    k_list, v_list = S.gen_kv(w, 0, [blk], "k"), S.gen_kv(w, 0, [blk], "v")
+    _say(f"[maximum capacity {fmt}] encoding {blk} tokens, copying them over {cap}")
+    cache = S.encode_on_gpu(w, k_list, v_list, [blk], cap)
+    reps = cap // blk
+    k, kn = cache.k_data[0, 0], cache.k_norms[0, 0]
+    v, vn = cache.v_data[0, 0], cache.v_norms[0, 0]
+    k.view(reps, blk, -1)[1:] = k[:blk]
+    kn.view(reps, blk)[1:] = kn[:blk]
+    v.view(reps, blk // 32, -1)[1:] = v[:blk // 32]
+    vn.view(reps, blk)[1:] = vn[:blk]
+    vn.view(torch.float16).view(reps, blk)[1::2] *= 2
+    cache.seq_lens.fill_(cap)
+    cache.lengths[:] = cap
+    q = queries(w, 0)
+    got = S.gpu_decode(cache, q, variant=variant)
+    d = {"k_rec": cache.k_data[0][:, :blk].cpu().numpy(),
+         "k_norms": cache.k_norms[0][:, :blk].cpu().numpy().view(np.float16),
+         "v_tiles": cache.v_data[0][:, :blk // 32].cpu().numpy(),
+         "v_norms": cache.v_norms[0][:, :blk].cpu().numpy().view(np.float16)}
+    k_hat, v_hat = S.oracle_dequant_download(d, fmt, fmt, blk, codebooks)
+    want = 1.5 * reference.decode_sequence(q[0], k_hat, v_hat, blk)
+    rel, mx = S.assert_close(got[0], want, "copies of one block")
+    _say(f"[maximum capacity {fmt} v{variant}] rel-L2 {rel:.2e} max-abs {mx:.2e}")
+
+
 @pytest.mark.timeout(600)
 def test_bandwidth_bound_step_edge_rows(codebooks):
     """A step large enough (>= 4M token-heads) that the row's first two splits append the token,

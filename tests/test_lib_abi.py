@@ -297,3 +297,20 @@ def test_latency_plan_keeps_its_items_when_rows_are_many(lib):
     d = _desc(batch=64, num_kv_heads=2, capacity=512, k_format=0, v_format=4, k_norms=0)
     a, p = _lens(*([512] * 64))
     assert lib.tq_decode_workspace_size(ctypes.byref(d), 4, p) == 64 * 2 * 3 * 2 * 130 * 4
+
+
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's size limits are the header's values."""
+    import os
+    import re
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "tqattn.h")).read()
+    defs = {k: eval(v.replace("(size_t)", "")) for k, v in re.findall(r"^#define (TQ_\w+) (.+)$", text, re.M)}
+    assert defs["TQ_MAX_CAPACITY"] == binding.MAX_CAPACITY
+    assert defs["TQ_NOALLOC_SCRATCH_BYTES"] == binding.NOALLOC_SCRATCH_BYTES
+
+
+def test_cache_capacity_checked_in_the_binding():
+    with pytest.raises(ValueError):
+        binding.Cache(1, 1, binding.MAX_CAPACITY + 32, "turbo4", "turbo4", None, None, device="cpu")
+    with pytest.raises(ValueError):
+        binding.Cache(1, 1, 48, "turbo4", "turbo4", None, None, device="cpu")

@@ -17,7 +17,8 @@
 // wants; group 0 stores it.  When the call has few (sequence, head) rows (latency-
 // bound calls: a few dozen waves on a 256-CU chip), a row gets WAVES waves: lane group
 // sg of wave w takes splits 4w + sg, 4w + sg + 4 WAVES, ..., each wave merges its groups
-// as above, and wave 0 merges the waves' states through LDS (in wave order).
+// as above, and wave 0 merges the waves' states, left in LDS, against their common
+// maximum.
 #include <math.h>
 
 #include <algorithm>
@@ -187,16 +188,32 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(DecodeArgs a, SeqLe
     }
     __syncthreads();
     if (wave != 0) return;
+    // The waves' states against their common maximum, summed in wave order (every
+    // lane computes the same bits): one reduction instead of a chain of pairwise merges.
+    float ms[WAVES], ls[WAVES];
+    float4 xa[WAVES], xb[WAVES];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) {  // in wave order: every lane computes the same bits
-      Acc o;
-      o.m = st_ml[w][0];
-      o.l = st_ml[w][1];
-      const float4 x0 = reinterpret_cast<const float4*>(&st_o[w][8 * j])[0];
-      const float4 x1 = reinterpret_cast<const float4*>(&st_o[w][8 * j])[1];
-      o.o[0] = x0.x; o.o[1] = x0.y; o.o[2] = x0.z; o.o[3] = x0.w;
-      o.o[4] = x1.x; o.o[5] = x1.y; o.o[6] = x1.z; o.o[7] = x1.w;
-      acc = merge(acc, o);
+    for (int w = 0; w < WAVES; ++w) {
+      ms[w] = st_ml[w][0];
+      ls[w] = st_ml[w][1];
+      xa[w] = reinterpret_cast<const float4*>(&st_o[w][8 * j])[0];
+      xb[w] = reinterpret_cast<const float4*>(&st_o[w][8 * j])[1];
+    }
+    float M = ms[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) M = fmaxf(M, ms[w]);
+    acc.m = M;
+    acc.l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc.o[i] = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float c = weight(ms[w], M);
+        acc.l += c * ls[w];
+        acc.o[0] += c * xa[w].x; acc.o[1] += c * xa[w].y; acc.o[2] += c * xa[w].z; acc.o[3] += c * xa[w].w;
+        acc.o[4] += c * xb[w].x; acc.o[5] += c * xb[w].y; acc.o[6] += c * xb[w].z; acc.o[7] += c * xb[w].w;
+      }
     }
   }
   float v[8];

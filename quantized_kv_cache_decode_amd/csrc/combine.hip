@@ -88,6 +88,44 @@ __device__ inline Acc merge_across(const Acc& a) {
   return merge(lo, hi);
 }
 
+// The inverse rotation of the merged row spread over the whole wave, two elements per
+// lane: lane (j, sg) takes elements 8j + 2sg and 8j + 2sg + 1 (every lane group holds the
+// whole row on entry).  The butterflies and their order (element bits 0..6) are
+// fwht128_row's, so the result has the bits of the stand-alone inverse rotation, on a
+// shorter chain: one in-lane stage, two lane-group swaps and four DPP stages of two
+// values instead of three in-lane stages and four DPP stages of eight.
+__device__ inline uint32_t inverse_rotate_pair_f16(float x, float y, float s0, float s1, int lane) {
+  {
+    const float a = x, b = y;   // element bit 0
+    x = a + b;
+    y = a - b;
+  }
+  auto swap_stage = [&](auto bit5_c) {   // element bits 1 and 2: lane bits 4 and 5
+    constexpr bool B5 = decltype(bit5_c)::value;
+    const bool upper = (lane & (B5 ? 32 : 16)) != 0;
+    float lo, hi;
+    swap_pair<B5>(x, lo, hi);
+    x = upper ? lo - hi : lo + hi;
+    swap_pair<B5>(y, lo, hi);
+    y = upper ? lo - hi : lo + hi;
+  };
+  swap_stage(std::false_type{});
+  swap_stage(std::true_type{});
+  auto dpp_stage = [&](auto m_c) {       // element bits 3..6: lane bits 0..3
+    constexpr int M = decltype(m_c)::value;
+    const float ox = xor_lane16<M>(x), oy = xor_lane16<M>(y);
+    x = (lane & M) ? (ox - x) : (x + ox);
+    y = (lane & M) ? (oy - y) : (y + oy);
+  };
+  dpp_stage(std::integral_constant<int, 1>{});
+  dpp_stage(std::integral_constant<int, 2>{});
+  dpp_stage(std::integral_constant<int, 4>{});
+  dpp_stage(std::integral_constant<int, 8>{});
+  const float x0 = x * kInvSqrtD * s0;
+  const float x1 = y * kInvSqrtD * s1;
+  return uint32_t(__half_as_ushort(__float2half_rn(x0))) | (uint32_t(__half_as_ushort(__float2half_rn(x1))) << 16);
+}
+
 // kBatch: splits per lane group per round, sized at launch to the call's longest
 // sequence so that short calls do not issue loads they then mask.
 template <bool INVERSE, int kBatch, int WAVES>
@@ -223,11 +261,18 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(DecodeArgs a, SeqLe
   // the step's length update, once every reader of the old length has finished
   if (step && hq == 0 && lane == 0) a.app.seq_lens[b] = L + 1;
   const size_t row = size_t(b) * a.hkv * G + hq;
-  if (INVERSE) {
-    uint32_t w[4];
+  if (INVERSE && a.v_rotated) {
+    // lane (j, sg) rotates and stores elements 8j + 2sg and 8j + 2sg + 1
     const float s8[8] = {sgn0.x, sgn0.y, sgn0.z, sgn0.w, sgn1.x, sgn1.y, sgn1.z, sgn1.w};
-    if (a.v_rotated) rotate_row_inverse_f16_s8(v, s8, j, w);  // every row of 16 lanes, the same bits
-    else round_row_f16(v, w);                                         // fp16 V: already the original basis
+    const float x = sg == 0 ? v[0] : sg == 1 ? v[2] : sg == 2 ? v[4] : v[6];
+    const float y = sg == 0 ? v[1] : sg == 1 ? v[3] : sg == 2 ? v[5] : v[7];
+    const float s0 = sg == 0 ? s8[0] : sg == 1 ? s8[2] : sg == 2 ? s8[4] : s8[6];
+    const float s1 = sg == 0 ? s8[1] : sg == 1 ? s8[3] : sg == 2 ? s8[5] : s8[7];
+    const uint32_t wv = inverse_rotate_pair_f16(x, y, s0, s1, lane);
+    *reinterpret_cast<uint32_t*>(a.out + row * kDim + 8 * j + 2 * sg) = wv;
+  } else if (INVERSE) {   // fp16 V: already the original basis
+    uint32_t w[4];
+    round_row_f16(v, w);
     if (sg == 0) *reinterpret_cast<uint4*>(a.out + row * kDim + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
   } else if (sg == 0) {
     float4* dst = reinterpret_cast<float4*>(a.out_rot + row * kDim + 8 * j);

@@ -129,7 +129,8 @@ tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
   const long long bytes = total * (token_bytes(c->k_format) + token_bytes(c->v_format));
   const long long tok_bytes = token_bytes(c->k_format) + token_bytes(c->v_format);
   auto round_chunk = [](long long ch) { return std::max((long long)TQ_PLAN_MIN_CHUNK, (ch + 63) / 64 * 64); };
-  if (!bandwidth_bound && bytes <= TQ_PLAN_LATENCY_BYTES) {
+  const bool latency = !bandwidth_bound && bytes <= TQ_PLAN_LATENCY_BYTES;
+  if (latency) {
     chunk = std::max(chunk, (total + TQ_PLAN_LATENCY_ITEMS - 1) / TQ_PLAN_LATENCY_ITEMS);
     const long long rows = (long long)c->batch * c->num_kv_heads;
     const long long items = TQ_PLAN_LATENCY_ITEMS - 2 * rows;
@@ -142,6 +143,7 @@ tq::DecodePlan make_plan(const tq_cache* c, const int32_t* lens, int group) {
   p.max_splits = std::max(1, (int)((lmax + chunk - 1) / chunk));
   p.slots = p.max_splits + 1;
   p.bandwidth_bound = bandwidth_bound;
+  p.latency = latency;
   return p;
 }
 
@@ -268,6 +270,7 @@ tq_status decode_setup(const tq_cache* cache, const int32_t* seq_lens_host, int3
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + partial_floats(cache, num_q_heads, plan) * 128;
   a.col0 = 0;
+  a.appends_last = 0;
   a.split_append = 0;
   a.v_skip_log2 = cache->v_skip_threshold > 0.f ? std::log2(cache->v_skip_threshold) : -INFINITY;
   // the K-side bound needs the stored norms of a quantised K format
@@ -275,6 +278,18 @@ tq_status decode_setup(const tq_cache* cache, const int32_t* seq_lens_host, int3
                                                                             : -INFINITY;
   a.q_len = 1;
   return TQ_OK;
+}
+
+// Compute units of the current device (cached per device).
+int compute_units() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
 }
 
 // Launch the decode kernel (variant 1: the VALU reference) and the split merge for
@@ -297,6 +312,8 @@ tq_status launch_decode_and_merge(const tq_cache* cache, const int32_t* seq_lens
     a.step = step;
     a.col0 = step && !a.plan.bandwidth_bound ? 2 : 0;
     a.split_append = step && a.plan.bandwidth_bound;
+    a.appends_last = variant != 1 && a.col0 == 2 &&
+                     (long long)nb * cache->num_kv_heads * (a.col0 + a.plan.max_splits) > compute_units();
     const hipError_t e = variant == 1 ? tq::launch_decode_reference(a, lens, nb, s)
                                       : tq::launch_decode_mfma(a, lens, nb, s);
     if ((st = hip_status(e, "decode launch")) != TQ_OK) return st;

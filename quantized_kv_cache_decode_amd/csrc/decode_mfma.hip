@@ -398,12 +398,13 @@ __device__ __forceinline__ void q_pin(QRaw& q) {
   pin4(q.s1);
 }
 
+// (Passes kfirst, kfirst + kstep, ... only: the waves of a work group share the rows.)
 __device__ __forceinline__ void q_finish(const DecodeArgs& a, float (*qs)[kDim], int lane, const QRaw& q,
-                                         bool rotate) {
+                                         bool rotate, int kfirst = 0, int kstep = 1) {
   const int G = a.group, j = lane & 15, r0 = lane >> 4;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    if (4 * k + r0 < G) {  // whole 16-lane segments
+    if ((k - kfirst) % kstep == 0 && k >= kfirst && 4 * k + r0 < G) {  // whole 16-lane segments
       float v[8];
       const uint32_t w[8] = {q.lo[k].x, q.lo[k].y, q.lo[k].z, q.lo[k].w, q.hi[k].x, q.hi[k].y, q.hi[k].z, q.hi[k].w};
       if (a.q_fp32) {
@@ -452,27 +453,57 @@ __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[k
 
 // SPARSE: the sparse-V and sparse-K skips are compiled in (their branches cost the
 // exact route a few percent of scheduling freedom, so that route goes without them).
-template <int KFMT, int VFMT, int NS, bool SPARSE>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
+// DS: waves per split.  With DS = 2 (latency-bound calls, where most SIMDs have no
+// wave) the split's head dims are shared: wave w scores against K dims
+// 64w .. 64w + 63 and accumulates the value blocks 4w .. 4w + 3 (output dims 8r + 4w
+// .. 8r + 4w + 3), reading only those bytes of each K record and V chunk; the two
+// partial scores meet in LDS once per iteration, so both waves run the same softmax
+// (and take the same sparse skips: their norms, maxima and thresholds are the same).
+template <int KFMT, int VFMT, int NS, bool SPARSE, int DS = 1>
+__global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   constexpr int P = 4 / NS;                  // lane groups per set in the score MFMA
   constexpr int Gp = 16 / NS;                // columns (padded heads) per set
   constexpr int TOK = 32 * NS;               // tokens per iteration
   constexpr int REC = KFMT == kFmtF16 ? 256 : k_record_bytes(KFMT);
-  constexpr int KW = REC / 4 / P;            // K words per lane per token
-  constexpr int NKK = 4 * NS;                // score MFMAs per 16-token row block
-  constexpr int VW = v_chunk_bytes(VFMT) / 4;  // V words per lane per tile
+  constexpr int KW = REC / 4 / P / DS;       // K words per lane per token
+  constexpr int NKK = 4 * NS / DS;           // score MFMAs per 16-token row block
+  constexpr int VW = v_chunk_bytes(VFMT) / 4 / DS;  // V words per lane per tile
+  constexpr int NACC = 8 / DS;               // value MFMA blocks of this wave
+  static_assert(DS == 1 || (DS == 2 && P * DS <= 4 && VFMT != kFmtF16),
+                "dims are shared only in whole 32-dim pieces, with quantised V");
 
-  // decode step: grid columns 0 and 1 (when col0 = 2) append the new token (K, V)
-  // and attend to it alone; the splits follow
-  const int s = int(blockIdx.x) - a.col0;
-  const int h = blockIdx.y, b = a.b0 + blockIdx.z;
+  // Work group -> (row, column): column c < col0 appends the new token (K, V) and
+  // attends to it alone, the others are the splits.  When the decode step's grid has
+  // more work groups than the chip has compute units (appends_last), it is taken in
+  // dispatch order as every row's splits, then every row's two append work groups, so
+  // the work groups that must share a unit are the append ones (one busy wave each),
+  // not splits.
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if (a.appends_last) {
+    const int ms = int(gridDim.x) - 2, rows = int(gridDim.y * gridDim.z);
+    const int lin = int(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    int r, c;
+    if (lin < rows * ms) {
+      r = lin / ms;
+      c = 2 + lin % ms;
+    } else {
+      r = (lin - rows * ms) >> 1;
+      c = (lin - rows * ms) & 1;
+    }
+    bx = c;
+    by = r % int(gridDim.y);
+    bz = r / int(gridDim.y);
+  }
+  const int s = bx - a.col0;
+  const int h = by, b = a.b0 + bz;
   const int G = a.group;
-  const int L = min(lens.len[blockIdx.z], a.cap);  // decode step: the length before the append
+  const int L = min(lens.len[bz], a.cap);  // decode step: the length before the append
   const int chunk = a.plan.chunk;
   const int nsplit = min((L + chunk - 1) / chunk, a.plan.max_splits);
   const bool append_wg = s < 0;
   if (s >= nsplit && !(a.split_append && s < 2)) return;
-  const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int dw = DS == 1 ? 0 : int(threadIdx.x >> 6);   // this wave's share of the dims
   const int t0 = s * chunk;
   const int t1 = (s == nsplit - 1) ? L : t0 + chunk;
 
@@ -491,16 +522,22 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
   // and 1 of chunk `lane` of each tile)
   const uint8_t* krow = a.k_data + row * size_t(a.cap) * REC;
   const uint8_t* vrow = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT);
-  const uint8_t* kbase = krow + part * (REC / P);
+  const uint8_t* kbase = krow + dw * (REC / DS) + part * (REC / P / DS);
   const uint8_t* vbase = vrow + lane * (VW * 4);
   const __amdgpu_buffer_rsrc_t krs = row_rsrc(krow, uint32_t(a.cap) * REC);
   const __amdgpu_buffer_rsrc_t vrs = row_rsrc(vrow, uint32_t(a.cap / kTileTokens) * v_tile_bytes(VFMT));
   const __amdgpu_buffer_rsrc_t knrs = row_rsrc(KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap), uint32_t(a.cap) * 2);
   const __amdgpu_buffer_rsrc_t vnrs = row_rsrc(VFMT == kFmtF16 ? nullptr : a.v_norms + row * size_t(a.cap), uint32_t(a.cap) * 2);
-  const uint32_t k_lane = KFMT == kFmtTurbo4 ? n * 16 + part * (4 / P) * 256 : n * 12;
+  constexpr int KPC = 4 / P / DS;            // 32-dim K pieces per lane
+  const int kp0 = dw * (4 / DS) + part * KPC;   // this lane's first K piece
+  const uint32_t k_lane = KFMT == kFmtTurbo4 ? n * 16 + kp0 * 256 : n * 12;
   const uint32_t v_lane = VFMT == kFmtTurbo4 ? lane * 16 : lane * 12;
   __shared__ float qs[kMaxGroup][kDim];
   if (append_wg) {
+    if (dw != 0) {   // one wave appends; the other meets its one barrier (K side) and ends
+      if (s == -2) __syncthreads();
+      return;
+    }
     // The append is one long dependent chain (binary64 butterflies, exact norm,
     // thresholds) sharing its SIMD with streaming decode waves: let it issue first.
     __builtin_amdgcn_s_setprio(3);
@@ -508,7 +545,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
     else append_k_work<KFMT, VFMT>(a, qs, row, L, lane);
     return;
   }
-  if (a.split_append && s < 2) {
+  if (DS == 1 && a.split_append && s < 2) {
     // Bandwidth-bound step: two extra work groups would not fit in the one round of
     // splits, so the first two splits of the row append the token before their own
     // tokens (the kernel's other waves keep streaming meanwhile).
@@ -536,7 +573,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
     for (int rb = 0; rb < 2; ++rb) {
       if constexpr (KFMT == kFmtTurbo4) load_pieces16<KW / 4>(kw[rb], krs, k_lane + uint32_t((tk >> 4) + rb) * 1024, 256);
       else if constexpr (KFMT == kFmtTurbo3)
-        load_k3_pieces<KW / 3>(kw[rb], krs, k_lane + uint32_t((tk >> 4) + rb) * 768, part * (4 / P));
+        load_k3_pieces<KW / 3>(kw[rb], krs, k_lane + uint32_t((tk >> 4) + rb) * 768, kp0);
       else load_words(kw[rb], kbase + size_t(tk + 16 * rb + n) * REC);
     }
     if (KFMT != kFmtF16) {
@@ -549,8 +586,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
 #pragma unroll
     for (int sg = 0; sg < NS; ++sg) {
       const int tile = min((base >> 5) + sg, last_tile);
-      if constexpr (VFMT == kFmtTurbo4) load_pieces16<2>(vw[sg], vrs, v_lane + uint32_t(tile) * v_tile_bytes(VFMT), 1024);
-      else if constexpr (VFMT == kFmtTurbo3) load_v3_pieces(vw[sg], vrs, v_lane + uint32_t(tile) * v_tile_bytes(VFMT));
+      // piece dw of the chunk (its value blocks 4dw .. 4dw + 3) when the dims are shared
+      const uint32_t voff = v_lane + uint32_t(tile) * v_tile_bytes(VFMT);
+      if constexpr (VFMT == kFmtTurbo4) load_pieces16<2 / DS>(vw[sg], vrs, voff + 1024 * dw, 1024);
+      else if constexpr (VFMT == kFmtTurbo3 && DS == 1) load_v3_pieces(vw[sg], vrs, voff);
+      else if constexpr (VFMT == kFmtTurbo3) load_k3_pieces<1>(vw[sg], vrs, voff + 768 * dw, 0);
       else load_words(vw[sg], vbase + size_t(tile) * v_tile_bytes(VFMT));
     }
     const int tn = min((base >> 5) + sn, last_tile) << 5;
@@ -592,7 +632,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
     vtab = make_table(c);
   }
 
-  q_finish(a, qs, lane, qraw, a.q_rotate != 0);
+  q_finish(a, qs, lane, qraw, a.q_rotate != 0, dw, DS);
   __syncthreads();
 
   // Sparse K: kbound * n is an upper bound on this lane's column's score (log2
@@ -613,13 +653,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
     kbound = a.scale * kLog2e * sqrtf(ss) * sqrtf(float(kDim)) * cmax * (1.f + 0x1p-8f);
   }
 
-  // q in this lane's score-MFMA B slots: q[hn][part*128/P + 8kk + t] * scale*log2(e),
+  // q in this lane's score-MFMA B slots: q[hn][32 kp0 + 8kk + t] * scale*log2(e),
   // zero unless the lane's k-slots belong to its column's set.
   // Kept in VGPRs: reading these operands from LDS inside the loop measured slower.
   half8 qb[NKK];
   {
     const bool use = hn < G && sig == sn;
-    const float* qrow = &qs[min(hn, G - 1)][part * (kDim / P)];
+    const float* qrow = &qs[min(hn, G - 1)][32 * kp0];
     const float f = use ? a.scale * kLog2e : 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -629,10 +669,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
                      _Float16(x1.x * f), _Float16(x1.y * f), _Float16(x1.z * f), _Float16(x1.w * f)};
     }
   }
-  floatx4 acc[8];
+  floatx4 acc[NACC];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NACC; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  // DS = 2: the waves' partial scores, double-buffered by iteration (one barrier each)
+  __shared__ float4 xs[DS == 2 ? 2 : 1][DS][2][64];
+  int it = 0;
 
   // Scores of the TOK tokens from `base` (log2 units, K norms applied, not yet
   // masked) into S; the next iteration's K words and norms are requested as soon
@@ -664,16 +707,43 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
         S[rb] = mfma(A, qk, S[rb]);
       }
     }
-    if constexpr (KFMT != kFmtF16) {
+    if constexpr (DS == 2) {
+      // the next iteration's K words go out first; then the two waves' partial sums
+      // (over their halves of the dims) meet in LDS, wave 0's first in both waves
+      const uint2 nk0 = nk[0], nk1 = nk[1];
+      load_k(base + TOK);
+      float4 (*x)[2][64] = xs[it & 1];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) x[dw][rb][lane] = make_float4(S[rb][0], S[rb][1], S[rb][2], S[rb][3]);
+      __syncthreads();
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        S[rb][0] = mul_half<0>(S[rb][0], nk[rb].x);
-        S[rb][1] = mul_half<1>(S[rb][1], nk[rb].x);
-        S[rb][2] = mul_half<0>(S[rb][2], nk[rb].y);
-        S[rb][3] = mul_half<1>(S[rb][3], nk[rb].y);
+        const float4 u = x[0][rb][lane], w = x[1][rb][lane];
+        S[rb] = floatx4{u.x + w.x, u.y + w.y, u.z + w.z, u.w + w.w};
       }
+      ++it;
+      if constexpr (KFMT != kFmtF16) {
+        const uint2 nkr[2] = {nk0, nk1};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          S[rb][0] = mul_half<0>(S[rb][0], nkr[rb].x);
+          S[rb][1] = mul_half<1>(S[rb][1], nkr[rb].x);
+          S[rb][2] = mul_half<0>(S[rb][2], nkr[rb].y);
+          S[rb][3] = mul_half<1>(S[rb][3], nkr[rb].y);
+        }
+      }
+    } else {
+      if constexpr (KFMT != kFmtF16) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          S[rb][0] = mul_half<0>(S[rb][0], nk[rb].x);
+          S[rb][1] = mul_half<1>(S[rb][1], nk[rb].x);
+          S[rb][2] = mul_half<0>(S[rb][2], nk[rb].y);
+          S[rb][3] = mul_half<1>(S[rb][3], nk[rb].y);
+        }
+      }
+      load_k(base + TOK);     // next iteration's K words and K norms
     }
-    load_k(base + TOK);     // next iteration's K words and K norms
   };
 
   // Softmax and values of the TOK tokens from `base` whose scores are in S.  TAIL:
@@ -702,7 +772,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+      for (int i = 0; i < NACC; ++i) acc[i] *= alpha;
     }
     m_run = m_new;
     // p = 2^(z - m); a masked slot has z = -inf and p = +0 exactly, and so does
@@ -736,7 +806,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
       const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
       const half8 bsg = (sn == sg) ? pb : zero8;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
+      for (int nb = 0; nb < NACC; ++nb) {
         half8 A;
         if constexpr (VFMT == kFmtF16) {
           A = pack8(vw[sg][4 * nb], vw[sg][4 * nb + 1], vw[sg][4 * nb + 2], vw[sg][4 * nb + 3]);
@@ -808,7 +878,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
     const float fs = m_fin == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_fin - M);
     const float fo = m_o == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_o - M);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NACC; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float o = xor_lane16<STP>(acc[i][j]);
@@ -828,11 +898,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a, SeqLens l
     float* o = a.part_o + pidx * kDim;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int d0 = 8 * (4 * g + j);
-      reinterpret_cast<float4*>(o + d0)[0] = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
-      reinterpret_cast<float4*>(o + d0)[1] = make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
+      const int d0 = 8 * (4 * g + j);   // value block nb holds dims d0 + nb (this wave's: 4dw + nb)
+      reinterpret_cast<float4*>(o + d0 + 4 * dw)[0] = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+      if constexpr (DS == 1)
+        reinterpret_cast<float4*>(o + d0)[1] = make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
     }
-    if (g == 0) {
+    if (g == 0 && dw == 0) {   // (m, l) are the same in both waves
       a.part_ml[pidx * 2] = m_fin;  // log2 units
       a.part_ml[pidx * 2 + 1] = l_tot;
     }
@@ -843,6 +914,17 @@ template <int KF, int VF, bool SPARSE>
 void launch_sets(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
   // decode step: the appended token's two work groups (if any) come first
   const dim3 grid(a.col0 + a.plan.max_splits, a.hkv, batch), block(64);
+  // latency-bound calls (most SIMDs idle): two waves per split share its dims
+  if constexpr (VF != kFmtF16) {
+    if (a.plan.latency && !a.split_append && a.group <= 8) {
+      const dim3 block2(128);
+      if (a.group <= 16 / TQ_MFMA_NS_SMALL_GROUP)
+        hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, TQ_MFMA_NS_SMALL_GROUP, SPARSE, 2>), grid, block2, 0, stream, a,
+                           lens);
+      else hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 2, SPARSE, 2>), grid, block2, 0, stream, a, lens);
+      return;
+    }
+  }
   if constexpr (VF == kFmtF16)  // 128-byte V chunks: one token set keeps the registers in bounds
     hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 1, SPARSE>), grid, block, 0, stream, a, lens);
   else if (a.group <= 16 / TQ_MFMA_NS_SMALL_GROUP)

@@ -55,6 +55,7 @@ struct DecodePlan {
   int max_splits;
   int slots;
   int bandwidth_bound;  // >= 4M token-heads: long enough that HBM, not latency, sets the time
+  int latency;          // a small call (the latency plan: about one split per compute unit)
 };
 
 struct DecodeArgs {
@@ -67,6 +68,8 @@ struct DecodeArgs {
   const uint16_t* v_norms;
   int b0;                   // first sequence of the launch (blockIdx z / y counts from it)
   int col0;                 // decode kernel grid: columns 0..col0-1 append the step's token (0 or 2)
+  int appends_last;         // col0 = 2 and more work groups than compute units: the MFMA kernel
+                            // takes its grid as every row's splits first, the append work groups last
   int split_append;         // decode step with col0 = 0: split 0 appends K and split 1 (split 0 when
                             // max_splits = 1) appends V, each before its own split
   const uint16_t* k_cb;

@@ -518,8 +518,8 @@ __global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqL
   const int t_col = min(t1, L - (a.q_len - 1 - hn % a.q_len));
   // The row's K records and V tiles: fp16 K/V by pointer (this lane's contiguous share);
   // quantised K/V and norms through buffer resources over the row, with this lane's
-  // offsets (K: pieces part*(4/P) .. of token n of each 16-token block; V: pieces 0
-  // and 1 of chunk `lane` of each tile)
+  // offsets (K: 32-dim pieces kp0 .. kp0 + KPC - 1 of token n of each 16-token block;
+  // V: pieces 0 and 1 of chunk `lane` of each tile, or piece dw with two waves)
   const uint8_t* krow = a.k_data + row * size_t(a.cap) * REC;
   const uint8_t* vrow = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT);
   const uint8_t* kbase = krow + dw * (REC / DS) + part * (REC / P / DS);

@@ -251,8 +251,9 @@ __device__ inline void zero_words(uint32_t (&w)[N]) {
 }
 
 // Decode step, two extra work groups of (sequence b, KV head h), at grid columns
-// 0 (K) and 1 (V) so they start first: lanes 0-15 encode the new token's K or V row
-// at slot L straight into the cache, then write that side of the token's own
+// 0 (K) and 1 (V): one wave encodes the new token's K or V row (a quantised row over
+// all 64 lanes, two elements each; an fp16 row on lanes 0-15) at slot L straight
+// into the cache, then writes that side of the token's own
 // partial for the G query heads -- K: score z_g = scale * q_g . k_hat (k_hat =
 // n_K * c_K[idx] in K's basis, or the fp16 row) as m, and l = 1; V: o = v_hat =
 // n_V * c_V[idx] in V's basis.  The regular splits cover the L earlier tokens and
@@ -260,58 +261,47 @@ __device__ inline void zero_words(uint32_t (&w)[N]) {
 // partial in like any other split.
 template <int KFMT, int VFMT>
 __device__ __forceinline__ void append_v_partial(const DecodeArgs& a, size_t row, int L, int lane) {
-  const int j = lane & 15;
-  if (lane >= 16) return;  // one 16-lane group
-  float x[8];
+  const size_t p0 = partial_index(a, row, a.plan.max_splits, 0);
   if constexpr (VFMT == kFmtF16) {  // stored as it comes; the partial is the row itself
+    const int j = lane & 15;
+    if (lane >= 16) return;  // one 16-lane group
+    float x[8];
     const uint4 v = *reinterpret_cast<const uint4*>(a.app.v_new + row * kDim + 8 * j);
     store_f16_v_row(a.app, row, L, v, j);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = half_bits_to_float(uint16_t(w[e >> 1] >> (16 * (e & 1))));
-  } else {
-    VRowInputs<VFMT> in;
-    load_v_inputs<VFMT>(a.app, row, L, a.app.v_new + row * kDim, j, in);
-    uint8_t code[8];
-    const float nv = half_bits_to_float(append_v_row<VFMT>(a.app, row, L, in, j, code));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = nv * codebook_at<VFMT>(in.row.tab, code[e]);
-  }
-  const size_t p0 = partial_index(a, row, a.plan.max_splits, 0);
-  for (int g = 0; g < a.group; ++g) {
-    float4* o = reinterpret_cast<float4*>(a.part_o + (p0 + g) * kDim + 8 * j);
-    o[0] = make_float4(x[0], x[1], x[2], x[3]);
-    o[1] = make_float4(x[4], x[5], x[6], x[7]);
+    for (int g = 0; g < a.group; ++g) {
+      float4* o = reinterpret_cast<float4*>(a.part_o + (p0 + g) * kDim + 8 * j);
+      o[0] = make_float4(x[0], x[1], x[2], x[3]);
+      o[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+  } else {  // the whole wave, two dims per lane
+    WaveVInputs<VFMT> in;
+    load_wave_v_inputs<VFMT>(a.app, row, L, a.app.v_new + row * kDim, lane, in);
+    uint32_t code[2];
+    const float nv = half_bits_to_float(append_v_row_wave<VFMT>(a.app, row, L, in, lane, code));
+    const float x0 = nv * codebook_at<VFMT>(in.row.tab, code[0]), x1 = nv * codebook_at<VFMT>(in.row.tab, code[1]);
+    const int e0 = wave_row_elem(lane);
+    for (int g = 0; g < a.group; ++g) {
+      float* o = a.part_o + (p0 + g) * kDim + e0;
+      o[0] = x0;
+      o[4] = x1;
+    }
   }
 }
 
-// K side: `kin` (quantised K) or `kraw` (F16 K) were requested before the q
-// staging, so their memory round trip overlaps it.  qs holds the caller's q
-// unrotated; the reconstructed K row is rotated back instead, since the rotation
-// is orthonormal (q_rot . k_hat = q . s_K H(k_hat) / sqrt(128)).
-template <int KFMT, int VFMT>
-__device__ __forceinline__ void append_k_partial(const DecodeArgs& a, const float (*qs)[kDim], size_t row, int L, int lane,
-                                 const RowInputs<KFMT == kFmtF16 ? kFmtTurbo3 : KFMT>& kin, const uint4& kraw,
-                                 const float (&ksign)[8]) {
+// K side, F16 K: lanes 0-15 copy the row (requested before the q staging, so its
+// memory round trip overlaps it) and score it against the unrotated q rows in qs.
+__device__ __forceinline__ void append_k_partial_f16(const DecodeArgs& a, const float (*qs)[kDim], size_t row, int L,
+                                                     int lane, const uint4& kraw) {
   const int j = lane & 15;
   if (lane >= 16) return;  // one 16-lane group
-  constexpr int KQ = KFMT == kFmtF16 ? kFmtTurbo3 : KFMT;
   float x[8];
-  if (KFMT == kFmtF16) {
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.app.k_data) + (row * a.cap + L) * kDim + 8 * j) = kraw;
-    const uint32_t w[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
+  *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.app.k_data) + (row * a.cap + L) * kDim + 8 * j) = kraw;
+  const uint32_t w[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = half_bits_to_float(uint16_t(w[e >> 1] >> (16 * (e & 1))));
-  } else {
-    uint8_t code[8];
-    const float nk = half_bits_to_float(append_k_row<KQ>(a.app, row, L, kin, j, code));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = nk * codebook_at<KQ>(kin.tab, code[e]);
-    // back to the original basis, k = s_K * H(k_hat) / sqrt(128): then q_rot . k_hat = q . k
-    fwht128_row(x, j);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = x[e] * kInvSqrtD * ksign[e];
-  }
+  for (int e = 0; e < 8; ++e) x[e] = half_bits_to_float(uint16_t(w[e >> 1] >> (16 * (e & 1))));
   // this lane's share of every head's dot product, then one 16-lane reduction for all
   const int G = a.group;
   float d[kMaxGroup];
@@ -341,6 +331,87 @@ __device__ __forceinline__ void append_k_partial(const DecodeArgs& a, const floa
       a.part_ml[(p0 + g) * 2 + 1] = 1.f;
     }
   }
+}
+
+// The G scores z_g = scale * q_g . k of the token's own partial, from this lane's two
+// K elements x0, x1 (e0, e0 + 4 of the whole-wave layout): the sums over the wave run
+// by halving -- the row swap over lane bit 5 sums head k with itself across the bit
+// in lanes without it and head k + NV/2 in lanes with it, the swap over bit 4 halves
+// again, and DPP sums over lane bits 0-3 finish NV/4 heads per 16-lane row: row r
+// ends with heads NV/4 * r .. NV/4 * r + NV/4 - 1 (NV = G rounded up to 4, 8 or 16).
+template <int NV>
+__device__ __forceinline__ void store_head_scores_wave(const DecodeArgs& a, const float (*qs)[kDim], size_t row,
+                                                       int lane, int e0, float x0, float x1) {
+  const int G = a.group;
+  float d[NV];
+#pragma unroll
+  for (int g = 0; g < NV; ++g) d[g] = g < G ? qs[g][e0] * x0 + qs[g][e0 + 4] * x1 : 0.f;
+  float e[NV / 2];
+#pragma unroll
+  for (int k = 0; k < NV / 2; ++k) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(d[k]), __float_as_uint(d[k + NV / 2]), false, false);
+    e[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  float f[NV / 4];
+#pragma unroll
+  for (int k = 0; k < NV / 4; ++k) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(e[k]), __float_as_uint(e[k + NV / 4]), false, false);
+    f[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  auto sum_stage = [&](auto m_c) {
+    constexpr int M = decltype(m_c)::value;
+#pragma unroll
+    for (int k = 0; k < NV / 4; ++k) f[k] += xor_lane16<M>(f[k]);
+  };
+  sum_stage(std::integral_constant<int, 1>{});
+  sum_stage(std::integral_constant<int, 2>{});
+  sum_stage(std::integral_constant<int, 4>{});
+  sum_stage(std::integral_constant<int, 8>{});
+  const int k = lane & 15, g = (NV / 4) * (lane >> 4) + k;
+  if (k < NV / 4 && g < G) {
+    float z = f[0];
+#pragma unroll
+    for (int i = 1; i < NV / 4; ++i) z = k == i ? f[i] : z;
+    const size_t pidx = partial_index(a, row, a.plan.max_splits, g);
+    a.part_ml[pidx * 2] = a.scale * kLog2e * z;  // log2 units, like the splits' m
+    a.part_ml[pidx * 2 + 1] = 1.f;
+  }
+}
+
+// K side, quantised K, over the whole wave: encode and store the row, rebuild
+// k = s_K * H(n_K * c_K[idx]) / sqrt(128) two elements per lane (q stays unrotated:
+// q_rot . k_hat = q . k, the rotation being orthonormal) and score it.
+template <int KFMT>
+__device__ __forceinline__ void append_k_partial_wave(const DecodeArgs& a, const float (*qs)[kDim], size_t row, int L,
+                                                      int lane, const WaveRowInputs<KFMT>& kin) {
+  uint32_t code[2];
+  const uint16_t nbits = encode_wave_row<KFMT>(kin, lane, code);
+  if (lane == 0) a.app.k_norms[row * a.app.cap + L] = nbits;
+  store_k_record_wave<KFMT>(a.app.k_data + row * a.app.cap * k_record_bytes(KFMT), L, code, lane);
+  const float nk = half_bits_to_float(nbits);
+  float x0 = nk * codebook_at<KFMT>(kin.tab, code[0]), x1 = nk * codebook_at<KFMT>(kin.tab, code[1]);
+  {
+    const float u = x0, v = x1;   // element bit 2, in-lane
+    x0 = u + v;
+    x1 = u - v;
+  }
+  auto stage = [&](auto b_c) {
+    constexpr int B = decltype(b_c)::value;
+    x0 = wave_butterfly<B>(x0, lane);
+    x1 = wave_butterfly<B>(x1, lane);
+  };
+  stage(std::integral_constant<int, 0>{});
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 3>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 5>{});
+  x0 = x0 * kInvSqrtD * kin.sg[0];
+  x1 = x1 * kInvSqrtD * kin.sg[1];
+  const int e0 = wave_row_elem(lane);
+  if (a.group <= 4) store_head_scores_wave<4>(a, qs, row, lane, e0, x0, x1);
+  else if (a.group <= 8) store_head_scores_wave<8>(a, qs, row, lane, e0, x0, x1);
+  else store_head_scores_wave<16>(a, qs, row, lane, e0, x0, x1);
 }
 
 // The G query rows of KV head row `row` into LDS qs, in two phases so the rows'
@@ -426,28 +497,29 @@ __device__ __forceinline__ void q_finish(const DecodeArgs& a, float (*qs)[kDim],
 }
 
 // Decode step, K side as a whole: request the row and thresholds, stage q while
-// they arrive, then encode, store and score.
+// they arrive, then encode, store and score.  All 64 lanes of the wave.
 template <int KFMT, int VFMT>
 __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[kDim], size_t row, int L, int lane) {
-  constexpr int KQ = KFMT == kFmtF16 ? kFmtTurbo3 : KFMT;
   QRaw q;
-  q_request<KFMT != kFmtF16>(a, row, lane, q);
+  q_request<false>(a, row, lane, q);   // q stays unrotated: the K row is taken back out of the codec basis
   __builtin_amdgcn_sched_barrier(0);
-  RowInputs<KQ> kin;
-  uint4 kraw = make_uint4(0, 0, 0, 0);
-  if (lane < 16) {
-    const uint16_t* src = a.app.k_new + row * kDim;
-    if (KFMT == kFmtF16) kraw = *reinterpret_cast<const uint4*>(src + 8 * lane);
-    else load_row_inputs<KQ>(src, a.app.k_signs, a.app.k_cb, lane, kin);
+  if constexpr (KFMT == kFmtF16) {
+    uint4 kraw = make_uint4(0, 0, 0, 0);
+    if (lane < 16) kraw = *reinterpret_cast<const uint4*>(a.app.k_new + row * kDim + 8 * lane);
+    __builtin_amdgcn_sched_barrier(0);
+    q_pin(q);
+    q_finish(a, qs, lane, q, false);
+    __syncthreads();
+    append_k_partial_f16(a, qs, row, L, lane, kraw);
+  } else {
+    WaveRowInputs<KFMT> kin;
+    load_wave_row_inputs<KFMT>(a.app.k_new + row * kDim, a.app.k_signs, a.app.k_cb, lane, kin);
+    __builtin_amdgcn_sched_barrier(0);
+    q_pin(q);
+    q_finish(a, qs, lane, q, false);
+    __syncthreads();
+    append_k_partial_wave<KFMT>(a, qs, row, L, lane, kin);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  q_pin(q);
-  // q stays unrotated: the token's K row is taken back out of the codec basis
-  // instead (one transform rather than one per query row)
-  q_finish(a, qs, lane, q, false);
-  __syncthreads();
-  const float s8[8] = {q.s0.x, q.s0.y, q.s0.z, q.s0.w, q.s1.x, q.s1.y, q.s1.z, q.s1.w};
-  append_k_partial<KFMT, VFMT>(a, qs, row, L, lane, kin, kraw, s8);
 }
 
 

@@ -129,6 +129,80 @@ __device__ __forceinline__ double xor_lane16(double v) {
   return __longlong_as_double(int64_t(xor_lane16<M>(uint64_t(__double_as_longlong(v)))));
 }
 
+// Exchanges across any lane bit B = 0..5 of the wave, for values spread over all 64
+// lanes: bits 0-3 through the DPP moves above, bits 4 and 5 through the gfx950 row
+// swaps (permlane16_swap(v, v) hands each lane the values of lanes i & ~16 and
+// i | 16; permlane32_swap the same for bit 5).  wave_sum gives both lanes of a pair
+// the same sum; wave_butterfly gives the lower lane lo + hi and the upper lo - hi.
+// Every lane of the wave must execute them together.
+template <int B>
+__device__ __forceinline__ void wave_pair_u32(uint32_t v, int lane, uint32_t& lo, uint32_t& hi) {
+  static_assert(B >= 0 && B <= 5, "lane bit of a 64-lane wave");
+  if constexpr (B == 5) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    lo = r[0];
+    hi = r[1];
+  } else if constexpr (B == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    lo = r[0];
+    hi = r[1];
+  } else {
+    const uint32_t o = xor_lane16<(1 << B)>(v);
+    const bool upper = (lane >> B) & 1;
+    lo = upper ? o : v;
+    hi = upper ? v : o;
+  }
+}
+template <int B>
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v, int lane) {
+  if constexpr (B < 4) {
+    return v + xor_lane16<(1 << B)>(v);
+  } else {
+    uint32_t l0, h0, l1, h1;
+    wave_pair_u32<B>(uint32_t(v), lane, l0, h0);
+    wave_pair_u32<B>(uint32_t(v >> 32), lane, l1, h1);
+    return (uint64_t(l0) | (uint64_t(l1) << 32)) + (uint64_t(h0) | (uint64_t(h1) << 32));
+  }
+}
+template <int B>
+__device__ __forceinline__ double wave_sum(double v, int lane) {
+  if constexpr (B < 4) {
+    return v + xor_lane16<(1 << B)>(v);
+  } else {
+    uint32_t l0, h0, l1, h1;
+    const uint64_t u = uint64_t(__double_as_longlong(v));
+    wave_pair_u32<B>(uint32_t(u), lane, l0, h0);
+    wave_pair_u32<B>(uint32_t(u >> 32), lane, l1, h1);
+    return __longlong_as_double(int64_t(uint64_t(l0) | (uint64_t(l1) << 32))) +
+           __longlong_as_double(int64_t(uint64_t(h0) | (uint64_t(h1) << 32)));
+  }
+}
+template <int B>
+__device__ __forceinline__ double wave_butterfly(double v, int lane) {
+  const double sgn = ((lane >> B) & 1) ? -1.0 : 1.0;
+  if constexpr (B < 4) {
+    return fma(v, sgn, xor_lane16<(1 << B)>(v));   // o - v or v + o, one rounding
+  } else {
+    uint32_t l0, h0, l1, h1;
+    const uint64_t u = uint64_t(__double_as_longlong(v));
+    wave_pair_u32<B>(uint32_t(u), lane, l0, h0);
+    wave_pair_u32<B>(uint32_t(u >> 32), lane, l1, h1);
+    return fma(__longlong_as_double(int64_t(uint64_t(h0) | (uint64_t(h1) << 32))), sgn,
+               __longlong_as_double(int64_t(uint64_t(l0) | (uint64_t(l1) << 32))));
+  }
+}
+template <int B>
+__device__ __forceinline__ float wave_butterfly(float v, int lane) {
+  const float sgn = ((lane >> B) & 1) ? -1.f : 1.f;
+  if constexpr (B < 4) {
+    return __builtin_fmaf(v, sgn, xor_lane16<(1 << B)>(v));
+  } else {
+    uint32_t lo, hi;
+    wave_pair_u32<B>(__float_as_uint(v), lane, lo, hi);
+    return __builtin_fmaf(__uint_as_float(hi), sgn, __uint_as_float(lo));
+  }
+}
+
 // Unnormalised 128-point Walsh-Hadamard transform of one row held by 16 lanes,
 // 8 elements per lane (element 8*j + i in lane j = lane16, slot i).  Stages over
 // element bits 0..2 are in-lane butterflies; stages over bits 3..6 exchange with

@@ -296,16 +296,16 @@ struct RowInputs {
   uint32_t tab[levels(FMT) / 2];
 };
 
+// Decision thresholds (binary64) and v_perm byte tables of an fp16 codebook.
 template <int FMT>
-__device__ __forceinline__ void load_row_inputs(const uint16_t* src, const float* signs, const uint16_t* cb, int j,
-                                                RowInputs<FMT>& in) {
-  load_row_and_signs(src + 8 * j, signs, j, in.w4, in.sg);
+__device__ __forceinline__ void load_codebook(const uint16_t* cb, double (&beta)[levels(FMT) - 1],
+                                              uint32_t (&tab)[levels(FMT) / 2]) {
   uint32_t c[levels(FMT)];
 #pragma unroll
   for (int i = 0; i < levels(FMT); ++i) c[i] = cb[i];
 #pragma unroll
   for (int i = 0; i < levels(FMT) - 1; ++i)
-    in.beta[i] = 0.5 * (double(half_bits_to_float(uint16_t(c[i]))) + double(half_bits_to_float(uint16_t(c[i + 1]))));
+    beta[i] = 0.5 * (double(half_bits_to_float(uint16_t(c[i]))) + double(half_bits_to_float(uint16_t(c[i + 1]))));
 #pragma unroll
   for (int h = 0; h < levels(FMT) / 8; ++h) {
     uint32_t lo0 = 0, lo1 = 0, hi0 = 0, hi1 = 0;
@@ -316,11 +316,18 @@ __device__ __forceinline__ void load_row_inputs(const uint16_t* src, const float
       hi0 |= (c[8 * h + i] >> 8) << (8 * i);
       hi1 |= (c[8 * h + 4 + i] >> 8) << (8 * i);
     }
-    in.tab[4 * h] = lo0;
-    in.tab[4 * h + 1] = lo1;
-    in.tab[4 * h + 2] = hi0;
-    in.tab[4 * h + 3] = hi1;
+    tab[4 * h] = lo0;
+    tab[4 * h + 1] = lo1;
+    tab[4 * h + 2] = hi0;
+    tab[4 * h + 3] = hi1;
   }
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_row_inputs(const uint16_t* src, const float* signs, const uint16_t* cb, int j,
+                                                RowInputs<FMT>& in) {
+  load_row_and_signs(src + 8 * j, signs, j, in.w4, in.sg);
+  load_codebook<FMT>(cb, in.beta, in.tab);
 }
 
 // Codebook entry at a 3- or 4-bit index, as fp32, from the byte tables.
@@ -443,6 +450,205 @@ __device__ __forceinline__ uint16_t append_row(const EncodeArgs& a, size_t row, 
   RowInputs<KQ> in;
   load_row_inputs<KQ>(src, a.k_signs, a.k_cb, j, in);
   return append_k_row<KQ>(a, row, t, in, j, code);
+}
+
+// ---- One row over a whole wave (the decode step's single-row K append).  Lane
+// l = 16q + 4c + b holds elements e0 = 32q + 8c + b and e0 + 4: element bits 0-1 are
+// lane bits 0-1, bit 2 is the lane's pair, bits 3-4 are lane bits 2-3 and bits 5-6
+// lane bits 4-5.  The arithmetic is encode_row's (the same exact binary64
+// transform, the same norm decision, the same thresholds), so codes and norms are
+// bit-identical to it; each stage handles two values per lane instead of eight.
+// All 64 lanes of the wave execute these routines together.
+__device__ __forceinline__ int wave_row_elem(int lane) {
+  return ((lane >> 4) << 5) | (((lane >> 2) & 3) << 3) | (lane & 3);
+}
+
+template <int FMT>
+struct WaveRowInputs {
+  uint32_t h01;          // fp16 bits of elements e0 (low half) and e0 + 4 (high half)
+  float sg[2];           // their sign flips
+  double beta[levels(FMT) - 1];
+  uint32_t tab[levels(FMT) / 2];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_wave_row_inputs(const uint16_t* src, const float* signs, const uint16_t* cb,
+                                                     int lane, WaveRowInputs<FMT>& in) {
+  const int e0 = wave_row_elem(lane);
+  in.h01 = uint32_t(src[e0]) | (uint32_t(src[e0 + 4]) << 16);
+  in.sg[0] = signs[e0];
+  in.sg[1] = signs[e0 + 4];
+  load_codebook<FMT>(cb, in.beta, in.tab);
+}
+
+// The exact norm (integer method) of a row spread over the wave.
+__device__ __forceinline__ uint16_t exact_wave_row_norm_fp16(uint32_t h01, int lane) {
+  uint64_t sA = 0, sB = 0, sC = 0;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const double xv = double(half_bits_to_float(uint16_t(h01 >> (16 * e))));
+    const uint64_t m = uint64_t(fabs(xv) * 16777216.0);  // exact integer < 2^40
+    const uint64_t mh = m >> 20, ml = m & 0xfffffull;
+    sA += mh * mh;
+    sB += mh * ml;
+    sC += ml * ml;
+  }
+  auto stage = [&](auto b_c) {
+    constexpr int B = decltype(b_c)::value;
+    sA = wave_sum<B>(sA, lane);
+    sB = wave_sum<B>(sB, lane);
+    sC = wave_sum<B>(sC, lane);
+  };
+  stage(std::integral_constant<int, 0>{});
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 3>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 5>{});
+  return exact_norm_fp16(sA, sB, sC);
+}
+
+// Codes of elements e0 and e0 + 4 and the row's fp16 norm bits (the same in every
+// lane).  The sum of squares takes 7 roundings at most along any path (one in-lane
+// add, six exchange stages), within the 11 the norm decision allows for.
+template <int FMT>
+__device__ __forceinline__ uint16_t encode_wave_row(const WaveRowInputs<FMT>& in, int lane, uint32_t (&code)[2]) {
+  const double x0 = double(half_bits_to_float(uint16_t(in.h01))), x1 = double(half_bits_to_float(uint16_t(in.h01 >> 16)));
+  double ss = fma(x1, x1, x0 * x0);   // x0 * x0 is exact
+  double x[2] = {x0 * double(in.sg[0]), x1 * double(in.sg[1])};
+  {
+    const double u = x[0], v = x[1];   // element bit 2, in-lane
+    x[0] = u + v;
+    x[1] = u - v;
+  }
+  auto stage = [&](auto b_c) {
+    constexpr int B = decltype(b_c)::value;
+    ss = wave_sum<B>(ss, lane);
+    x[0] = wave_butterfly<B>(x[0], lane);
+    x[1] = wave_butterfly<B>(x[1], lane);
+  };
+  stage(std::integral_constant<int, 0>{});
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 3>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 5>{});
+  uint32_t nb = fast_norm_fp16(ss);
+  if (nb == 0xffffu) nb = exact_wave_row_norm_fp16(in.h01, lane);   // uniform over the wave
+  const uint16_t nbits = uint16_t(nb);
+  const double nd = double(half_bits_to_float(nbits));
+  constexpr int K = levels(FMT), Hf = K / 2;
+  double U[Hf - 1];
+#pragma unroll
+  for (int k = 1; k < Hf; ++k) U[k - 1] = (nd * in.beta[Hf - 1 + k]) * kSqrtD;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const double a = fabs(x[e]);
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < Hf - 1; ++k) cnt += a > U[k] ? 1 : 0;
+    const int c = x[e] > 0.0 ? Hf + cnt : Hf - 1 - cnt;
+    code[e] = uint32_t(nd == 0.0 ? 0 : c);
+  }
+  return nbits;
+}
+
+// Write token t's K record from the wave's codes.  turbo4: elements e0 and e0 + 4 are
+// nibbles b and 4 + b of octet word 4q + c, i.e. record byte l.  turbo3: lane 12 + b
+// of each sub-block's 16 lanes (elements 24 + b and 28 + b) owns bits 6-7 of byte b
+// of words A, B and C; the other lanes own bits 0-5 of byte b of word c and fetch
+// their bits 6-7 from it (ds_swizzle: lane l | 12 within each 32).
+template <int KFMT>
+__device__ __forceinline__ void store_k_record_wave(uint8_t* row_k, int t, const uint32_t (&code)[2], int lane) {
+  if constexpr (KFMT == kFmtTurbo4) {
+    const uint32_t byte = t4_nibble_of_index(code[0]) | (t4_nibble_of_index(code[1]) << 4);
+    row_k[k_byte_offset(kFmtTurbo4, t, lane)] = uint8_t(byte);
+  } else {
+    const int c = (lane >> 2) & 3, b = lane & 3;
+    const uint32_t top = ((code[0] & 3u) << 6) | ((code[1] & 3u) << 14) | (((code[0] >> 2) & 1u) << 22) |
+                         (((code[1] >> 2) & 1u) << 23);
+    constexpr int kFromLane12 = 0x1f | (0x0c << 5);   // bit mode: and 0x1f, or 12, xor 0
+    const uint32_t from = uint32_t(__builtin_amdgcn_ds_swizzle(int(top), kFromLane12));
+    if (c < 3) {
+      const uint32_t byte = (code[0] & 7u) | ((code[1] & 7u) << 3) | ((from >> (8 * c)) & 0xc0u);
+      row_k[k_byte_offset(kFmtTurbo3, t, 12 * (lane >> 4) + 4 * c + b)] = uint8_t(byte);
+    }
+  }
+}
+
+// The V side over the whole wave: this lane's two dims 8j + b and 8j + 4 + b (j = 4q + c)
+// sit in chunk 16 g + j of the token's tile (g its slot group), in chunk words b and
+// 4 + b (turbo4) or word b of the chunk's two sub-blocks (turbo3), where the token's
+// field is chunk element 8 * (dim % 4) + ei.  turbo3: the fields of dims 8j + 3 and
+// 8j + 7 (sub-block elements 24 + ei) are split over words 0-2, so lane 3 of each
+// quad writes nothing and lanes 0-2 take its codes (a quad broadcast) into the words
+// they rewrite.  Every other slot's fields are kept.
+template <int VFMT>
+struct WaveVInputs {
+  WaveRowInputs<VFMT> row;
+  uint32_t cw[2];            // the two chunk words this lane rewrites
+  uint32_t off[2];           // their byte offsets in the tile
+  uint8_t* tile;
+  int ei;                    // chunk element of the token's slot
+};
+
+template <int VFMT>
+__device__ __forceinline__ void load_wave_v_inputs(const EncodeArgs& a, size_t row, int t, const uint16_t* src, int lane,
+                                                   WaveVInputs<VFMT>& in) {
+  const int r = t % kTileTokens, g = slot_group(r);
+  in.ei = slot_elem(r);
+  in.tile = a.v_data + (row * (a.cap / kTileTokens) + t / kTileTokens) * v_tile_bytes(VFMT);
+  const int chunk = 16 * g + (wave_row_elem(lane) >> 3);
+  if constexpr (VFMT == kFmtTurbo4) {
+    in.off[0] = v_chunk_byte_offset(VFMT, chunk, 4 * (lane & 3));
+    in.off[1] = v_chunk_byte_offset(VFMT, chunk, 16 + 4 * (lane & 3));
+  } else {
+    const int w = min(lane & 3, 2);  // lane 3 of a quad rewrites nothing (its words are lane 0-2's)
+    in.off[0] = v_chunk_byte_offset(VFMT, chunk, 4 * w);
+    in.off[1] = v_chunk_byte_offset(VFMT, chunk, 12 + 4 * w);
+  }
+  // a token in slot 0 starts the tile: the other slots hold nothing visible yet
+#pragma unroll
+  for (int i = 0; i < 2; ++i) in.cw[i] = r == 0 ? 0u : *reinterpret_cast<const uint32_t*>(in.tile + in.off[i]);
+  load_wave_row_inputs<VFMT>(src, a.v_signs, a.v_cb, lane, in.row);
+}
+
+template <int VFMT>
+__device__ __forceinline__ uint16_t append_v_row_wave(const EncodeArgs& a, size_t row, int t, WaveVInputs<VFMT>& in,
+                                                      int lane, uint32_t (&code)[2]) {
+  const uint16_t nbits = encode_wave_row<VFMT>(in.row, lane, code);
+  const int b = lane & 3;
+  if constexpr (VFMT == kFmtTurbo4) {
+    const int sh = oct4_bit(in.ei);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) in.cw[i] = (in.cw[i] & ~(15u << sh)) | (t4_nibble_of_index(code[i]) << sh);
+  } else {
+    const uint32_t c3 = dpp_u32<0xff>(code[0] | (code[1] << 8));   // quad_perm [3,3,3,3]
+    const int jj = in.ei & 3, up = in.ei >> 2;
+    const int sh = 8 * jj + 3 * up;      // own field (sub-block element 8b + ei, b < 3)
+    const int s2 = 8 * jj + 6;           // low two bits of element 24 + ei, in word `up`
+    const int s1 = 8 * jj + 6 + up;      // its top bit, in word 2
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t c = code[i], d = (c3 >> (8 * i)) & 0xffu;
+      uint32_t m = 7u << sh, v = (c & 7u) << sh;
+      if (b == up) {
+        m |= 3u << s2;
+        v |= (d & 3u) << s2;
+      }
+      if (b == 2) {
+        m |= 1u << s1;
+        v |= ((d >> 2) & 1u) << s1;
+      }
+      in.cw[i] = (in.cw[i] & ~m) | v;
+    }
+  }
+  if (VFMT == kFmtTurbo4 || b < 3) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint32_t*>(in.tile + in.off[i]) = in.cw[i];
+  }
+  if (lane == 0) a.v_norms[row * a.cap + t] = nbits;
+  return nbits;
 }
 
 }  // namespace tq

@@ -525,24 +525,22 @@ __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[k
 
 // SPARSE: the sparse-V and sparse-K skips are compiled in (their branches cost the
 // exact route a few percent of scheduling freedom, so that route goes without them).
-// DS: waves per split.  With DS = 2 (latency-bound calls, where most SIMDs have no
-// wave) the split's head dims are shared: wave w scores against K dims
-// 64w .. 64w + 63 and accumulates the value blocks 4w .. 4w + 3 (output dims 8r + 4w
-// .. 8r + 4w + 3), reading only those bytes of each K record and V chunk; the two
-// partial scores meet in LDS once per iteration, so both waves run the same softmax
-// (and take the same sparse skips: their norms, maxima and thresholds are the same).
-template <int KFMT, int VFMT, int NS, bool SPARSE, int DS = 1>
-__global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
+// TS: waves per split.  With TS = 4 (latency-bound calls, where most SIMDs would have
+// no wave) the split's tokens are shared: each wave streams a quarter of them in
+// whole iterations with its own softmax state, the four share the staging of q, and
+// they merge their states in LDS at the end, each wave storing a quarter of the
+// split's partial -- one partial per split, as with one wave.
+template <int KFMT, int VFMT, int NS, bool SPARSE, int TS = 1>
+__global__ __launch_bounds__(64 * TS) void decode_mfma_kernel(DecodeArgs a, SeqLens lens) {
   constexpr int P = 4 / NS;                  // lane groups per set in the score MFMA
   constexpr int Gp = 16 / NS;                // columns (padded heads) per set
   constexpr int TOK = 32 * NS;               // tokens per iteration
   constexpr int REC = KFMT == kFmtF16 ? 256 : k_record_bytes(KFMT);
-  constexpr int KW = REC / 4 / P / DS;       // K words per lane per token
-  constexpr int NKK = 4 * NS / DS;           // score MFMAs per 16-token row block
-  constexpr int VW = v_chunk_bytes(VFMT) / 4 / DS;  // V words per lane per tile
-  constexpr int NACC = 8 / DS;               // value MFMA blocks of this wave
-  static_assert(DS == 1 || (DS == 2 && P * DS <= 4 && VFMT != kFmtF16),
-                "dims are shared only in whole 32-dim pieces, with quantised V");
+  constexpr int KW = REC / 4 / P;            // K words per lane per token
+  constexpr int NKK = 4 * NS;                // score MFMAs per 16-token row block
+  constexpr int VW = v_chunk_bytes(VFMT) / 4;  // V words per lane per tile
+  constexpr int NACC = 8;                    // value MFMA blocks
+  static_assert(TS == 1 || TS == 4, "one wave per split, or four sharing its tokens");
 
   // Work group -> (row, column): column c < col0 appends the new token (K, V) and
   // attends to it alone, the others are the splits.  When the decode step's grid has
@@ -575,9 +573,17 @@ __global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqL
   const bool append_wg = s < 0;
   if (s >= nsplit && !(a.split_append && s < 2)) return;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int dw = DS == 1 ? 0 : int(threadIdx.x >> 6);   // this wave's share of the dims
-  const int t0 = s * chunk;
-  const int t1 = (s == nsplit - 1) ? L : t0 + chunk;
+  const int wv = int(threadIdx.x >> 6);
+  // This wave's tokens [t0, t1): the split's, or with TS waves per split its TS-th
+  // share in whole iterations (a wave left without tokens gets t0 = t1 = the split's end).
+  int t0 = s * chunk;
+  int t1 = (s == nsplit - 1) ? L : t0 + chunk;
+  if constexpr (TS > 1) {
+    const int per = ((t1 - t0 + TOK - 1) / TOK + TS - 1) / TS * TOK;
+    const int end = t1;
+    t0 = min(t0 + wv * per, end);
+    t1 = min(t0 + per, end);
+  }
 
   const int sig = g / P, part = g % P;       // score-MFMA set and part of this lane
   const int sn = n / Gp, hn = n % Gp;        // this lane's column: set and head
@@ -591,22 +597,22 @@ __global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqL
   // The row's K records and V tiles: fp16 K/V by pointer (this lane's contiguous share);
   // quantised K/V and norms through buffer resources over the row, with this lane's
   // offsets (K: 32-dim pieces kp0 .. kp0 + KPC - 1 of token n of each 16-token block;
-  // V: pieces 0 and 1 of chunk `lane` of each tile, or piece dw with two waves)
+  // V: pieces 0 and 1 of chunk `lane` of each tile)
   const uint8_t* krow = a.k_data + row * size_t(a.cap) * REC;
   const uint8_t* vrow = a.v_data + row * size_t(a.cap / kTileTokens) * v_tile_bytes(VFMT);
-  const uint8_t* kbase = krow + dw * (REC / DS) + part * (REC / P / DS);
+  const uint8_t* kbase = krow + part * (REC / P);
   const uint8_t* vbase = vrow + lane * (VW * 4);
   const __amdgpu_buffer_rsrc_t krs = row_rsrc(krow, uint32_t(a.cap) * REC);
   const __amdgpu_buffer_rsrc_t vrs = row_rsrc(vrow, uint32_t(a.cap / kTileTokens) * v_tile_bytes(VFMT));
   const __amdgpu_buffer_rsrc_t knrs = row_rsrc(KFMT == kFmtF16 ? nullptr : a.k_norms + row * size_t(a.cap), uint32_t(a.cap) * 2);
   const __amdgpu_buffer_rsrc_t vnrs = row_rsrc(VFMT == kFmtF16 ? nullptr : a.v_norms + row * size_t(a.cap), uint32_t(a.cap) * 2);
-  constexpr int KPC = 4 / P / DS;            // 32-dim K pieces per lane
-  const int kp0 = dw * (4 / DS) + part * KPC;   // this lane's first K piece
+  constexpr int KPC = 4 / P;                 // 32-dim K pieces per lane
+  const int kp0 = part * KPC;                // this lane's first K piece
   const uint32_t k_lane = KFMT == kFmtTurbo4 ? n * 16 + kp0 * 256 : n * 12;
   const uint32_t v_lane = VFMT == kFmtTurbo4 ? lane * 16 : lane * 12;
   __shared__ float qs[kMaxGroup][kDim];
   if (append_wg) {
-    if (dw != 0) {   // one wave appends; the other meets its one barrier (K side) and ends
+    if (wv != 0) {   // one wave appends; the others meet its one barrier (K side) and end
       if (s == -2) __syncthreads();
       return;
     }
@@ -617,7 +623,7 @@ __global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqL
     else append_k_work<KFMT, VFMT>(a, qs, row, L, lane);
     return;
   }
-  if (DS == 1 && a.split_append && s < 2) {
+  if (TS == 1 && a.split_append && s < 2) {
     // Bandwidth-bound step: two extra work groups would not fit in the one round of
     // splits, so the first two splits of the row append the token before their own
     // tokens (the kernel's other waves keep streaming meanwhile).
@@ -658,11 +664,9 @@ __global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqL
 #pragma unroll
     for (int sg = 0; sg < NS; ++sg) {
       const int tile = min((base >> 5) + sg, last_tile);
-      // piece dw of the chunk (its value blocks 4dw .. 4dw + 3) when the dims are shared
       const uint32_t voff = v_lane + uint32_t(tile) * v_tile_bytes(VFMT);
-      if constexpr (VFMT == kFmtTurbo4) load_pieces16<2 / DS>(vw[sg], vrs, voff + 1024 * dw, 1024);
-      else if constexpr (VFMT == kFmtTurbo3 && DS == 1) load_v3_pieces(vw[sg], vrs, voff);
-      else if constexpr (VFMT == kFmtTurbo3) load_k3_pieces<1>(vw[sg], vrs, voff + 768 * dw, 0);
+      if constexpr (VFMT == kFmtTurbo4) load_pieces16<2>(vw[sg], vrs, voff, 1024);
+      else if constexpr (VFMT == kFmtTurbo3) load_v3_pieces(vw[sg], vrs, voff);
       else load_words(vw[sg], vbase + size_t(tile) * v_tile_bytes(VFMT));
     }
     const int tn = min((base >> 5) + sn, last_tile) << 5;
@@ -704,7 +708,7 @@ __global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqL
     vtab = make_table(c);
   }
 
-  q_finish(a, qs, lane, qraw, a.q_rotate != 0, dw, DS);
+  q_finish(a, qs, lane, qraw, a.q_rotate != 0, wv, TS);
   __syncthreads();
 
   // Sparse K: kbound * n is an upper bound on this lane's column's score (log2
@@ -745,9 +749,6 @@ __global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqL
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  // DS = 2: the waves' partial scores, double-buffered by iteration (one barrier each)
-  __shared__ float4 xs[DS == 2 ? 2 : 1][DS][2][64];
-  int it = 0;
 
   // Scores of the TOK tokens from `base` (log2 units, K norms applied, not yet
   // masked) into S; the next iteration's K words and norms are requested as soon
@@ -779,43 +780,16 @@ __global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqL
         S[rb] = mfma(A, qk, S[rb]);
       }
     }
-    if constexpr (DS == 2) {
-      // the next iteration's K words go out first; then the two waves' partial sums
-      // (over their halves of the dims) meet in LDS, wave 0's first in both waves
-      const uint2 nk0 = nk[0], nk1 = nk[1];
-      load_k(base + TOK);
-      float4 (*x)[2][64] = xs[it & 1];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) x[dw][rb][lane] = make_float4(S[rb][0], S[rb][1], S[rb][2], S[rb][3]);
-      __syncthreads();
+    if constexpr (KFMT != kFmtF16) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const float4 u = x[0][rb][lane], w = x[1][rb][lane];
-        S[rb] = floatx4{u.x + w.x, u.y + w.y, u.z + w.z, u.w + w.w};
+        S[rb][0] = mul_half<0>(S[rb][0], nk[rb].x);
+        S[rb][1] = mul_half<1>(S[rb][1], nk[rb].x);
+        S[rb][2] = mul_half<0>(S[rb][2], nk[rb].y);
+        S[rb][3] = mul_half<1>(S[rb][3], nk[rb].y);
       }
-      ++it;
-      if constexpr (KFMT != kFmtF16) {
-        const uint2 nkr[2] = {nk0, nk1};
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          S[rb][0] = mul_half<0>(S[rb][0], nkr[rb].x);
-          S[rb][1] = mul_half<1>(S[rb][1], nkr[rb].x);
-          S[rb][2] = mul_half<0>(S[rb][2], nkr[rb].y);
-          S[rb][3] = mul_half<1>(S[rb][3], nkr[rb].y);
-        }
-      }
-    } else {
-      if constexpr (KFMT != kFmtF16) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          S[rb][0] = mul_half<0>(S[rb][0], nk[rb].x);
-          S[rb][1] = mul_half<1>(S[rb][1], nk[rb].x);
-          S[rb][2] = mul_half<0>(S[rb][2], nk[rb].y);
-          S[rb][3] = mul_half<1>(S[rb][3], nk[rb].y);
-        }
-      }
-      load_k(base + TOK);     // next iteration's K words and K norms
     }
+    load_k(base + TOK);     // next iteration's K words and K norms
   };
 
   // Softmax and values of the TOK tokens from `base` whose scores are in S.  TAIL:
@@ -962,6 +936,56 @@ __global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqL
   };
   if constexpr (Gp <= 4) merge_sets(std::integral_constant<int, 4>{});
   if constexpr (Gp <= 8) merge_sets(std::integral_constant<int, 8>{});
+  if constexpr (TS > 1) {
+    // The split's waves meet in LDS: every wave leaves (m, l) and its o there, then
+    // wave w merges and stores the quarter of each column's o in its j = w value
+    // blocks (dims 8(4g + w) + nb), weighing every wave's state by 2^(m_v - M), M the
+    // largest m (an empty state weighs 0).
+    static_assert(TS == 4 && NACC == 8, "four waves, one value-block quarter each");
+    __shared__ float2 stml[TS][64];
+    __shared__ float4 sto[TS][4][2][64];
+    stml[wv][lane] = make_float2(m_fin, l_tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sto[wv][j][0][lane] = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+      sto[wv][j][1][lane] = make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
+    }
+    __syncthreads();
+    float2 ml[TS];
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < TS; ++v) {
+      ml[v] = stml[v][lane];
+      M = fmaxf(M, ml[v].x);
+    }
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+#pragma unroll
+    for (int v = 0; v < TS; ++v) {
+      const float f = ml[v].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[v].x - M);
+      const float4 lo = sto[v][wv][0][lane], hi = sto[v][wv][1][lane];
+      l += ml[v].y * f;
+      o[0] += lo.x * f;
+      o[1] += lo.y * f;
+      o[2] += lo.z * f;
+      o[3] += lo.w * f;
+      o[4] += hi.x * f;
+      o[5] += hi.y * f;
+      o[6] += hi.z * f;
+      o[7] += hi.w * f;
+    }
+    if (n < Gp && hn < G) {
+      const size_t pidx = partial_index(a, row, s, hn);
+      float4* dst = reinterpret_cast<float4*>(a.part_o + pidx * kDim + 8 * (4 * g + wv));
+      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+      if (g == 0 && wv == 0) {
+        a.part_ml[pidx * 2] = M;  // log2 units
+        a.part_ml[pidx * 2 + 1] = l;
+      }
+    }
+    return;
+  }
   // Partial of this split (unnormalised o, log2-domain m, l); the splits are merged
   // by a separate kernel: a release/acquire hand-off between waves of this kernel
   // would need an L2 write-back per wave, which measured far slower.
@@ -970,12 +994,11 @@ __global__ __launch_bounds__(64 * DS) void decode_mfma_kernel(DecodeArgs a, SeqL
     float* o = a.part_o + pidx * kDim;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int d0 = 8 * (4 * g + j);   // value block nb holds dims d0 + nb (this wave's: 4dw + nb)
-      reinterpret_cast<float4*>(o + d0 + 4 * dw)[0] = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
-      if constexpr (DS == 1)
-        reinterpret_cast<float4*>(o + d0)[1] = make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
+      const int d0 = 8 * (4 * g + j);   // value block nb holds dims d0 + nb
+      reinterpret_cast<float4*>(o + d0)[0] = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+      reinterpret_cast<float4*>(o + d0)[1] = make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
     }
-    if (g == 0 && dw == 0) {   // (m, l) are the same in both waves
+    if (g == 0) {
       a.part_ml[pidx * 2] = m_fin;  // log2 units
       a.part_ml[pidx * 2 + 1] = l_tot;
     }
@@ -986,16 +1009,10 @@ template <int KF, int VF, bool SPARSE>
 void launch_sets(const DecodeArgs& a, const SeqLens& lens, int batch, hipStream_t stream) {
   // decode step: the appended token's two work groups (if any) come first
   const dim3 grid(a.col0 + a.plan.max_splits, a.hkv, batch), block(64);
-  // latency-bound calls (most SIMDs idle): two waves per split share its dims
-  if constexpr (VF != kFmtF16) {
-    if (a.plan.latency && !a.split_append && a.group <= 8) {
-      const dim3 block2(128);
-      if (a.group <= 16 / TQ_MFMA_NS_SMALL_GROUP)
-        hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, TQ_MFMA_NS_SMALL_GROUP, SPARSE, 2>), grid, block2, 0, stream, a,
-                           lens);
-      else hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 2, SPARSE, 2>), grid, block2, 0, stream, a, lens);
-      return;
-    }
+  // latency-bound calls (most SIMDs would be idle): four waves per split share its tokens
+  if (a.plan.latency && !a.split_append) {
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 1, SPARSE, 4>), grid, dim3(256), 0, stream, a, lens);
+    return;
   }
   if constexpr (VF == kFmtF16)  // 128-byte V chunks: one token set keeps the registers in bounds
     hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, 1, SPARSE>), grid, block, 0, stream, a, lens);

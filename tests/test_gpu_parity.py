@@ -622,6 +622,26 @@ def test_f16_cache_parity(group, variant, codebooks):
         S.assert_close(got[b], want, f"fp16 cache {variant} G={group} b={b} L={int(L[b])}")
 
 
+@pytest.mark.parametrize("group,k_format,v_format", [(7, "turbo3", "turbo3"), (7, "f16", "turbo4"),
+                                                     (16, "turbo4", "turbo3"), (16, "f16", "f16")])
+@pytest.mark.parametrize("variant", [0, "fused", "step"])
+def test_split_waves_with_few_or_no_tokens(group, k_format, v_format, variant, codebooks):
+    """Small calls run four waves per 128-token split, each streaming a quarter of its tokens
+    in 32-token iterations: lengths that leave one, two, three or all four waves with tokens
+    (and splits of one token) give the same outputs as the oracle."""
+    lens = np.array([1, 31, 32, 33, 64, 96, 97, 128, 129, 200, 255, 257, 383])
+    w = S.scaled(get_workload(0), batch=len(lens), num_q_heads=2 * group, num_kv_heads=2, k_format=k_format,
+                 v_format=v_format)
+    if variant == "step":
+        cache, k_list, v_list, L, q, got = S.prefill_then_decode_step(w, lengths=lens)
+    else:
+        cache, k_list, v_list, L, q = S.prefill_and_step(w, lengths=lens)
+        got = S.gpu_decode(cache, q, variant=variant)
+    for b in range(len(lens)):
+        want = S.oracle_end_to_end(w, k_list[b], v_list[b], int(L[b]), q[b], codebooks)
+        S.assert_close(got[b], want, f"{variant} G={group} {k_format}/{v_format} L={int(L[b])}")
+
+
 # ----------------------------------------------------------------------------- many sequences
 
 @pytest.mark.parametrize("variant", ["fused", "step"])

@@ -385,10 +385,7 @@ template <int KFMT>
 __device__ __forceinline__ void append_k_partial_wave(const DecodeArgs& a, const float (*qs)[kDim], size_t row, int L,
                                                       int lane, const WaveRowInputs<KFMT>& kin) {
   uint32_t code[2];
-  const uint16_t nbits = encode_wave_row<KFMT>(kin, lane, code);
-  if (lane == 0) a.app.k_norms[row * a.app.cap + L] = nbits;
-  store_k_record_wave<KFMT>(a.app.k_data + row * a.app.cap * k_record_bytes(KFMT), L, code, lane);
-  const float nk = half_bits_to_float(nbits);
+  const float nk = half_bits_to_float(append_k_row_wave<KFMT>(a.app, row, L, kin, lane, code));
   float x0 = nk * codebook_at<KFMT>(kin.tab, code[0]), x1 = nk * codebook_at<KFMT>(kin.tab, code[1]);
   {
     const float u = x0, v = x1;   // element bit 2, in-lane

@@ -10,10 +10,11 @@
 // thread per chunk, merging with the words of tokens already in the tile.  F16 K
 // rows are copied unchanged.
 //
-// append_one_kernel (the decode step: at most one row per sequence): one 16-lane
-// group per row; waves 0-1 of a block encode the K rows of 8 (sequence, KV head)
-// pairs and waves 2-3 their V rows, so no wave mixes the two paths; every load is
-// issued up front (one memory round trip, no barrier).
+// append_one_kernel (one new row per sequence at most): a work group of two waves per
+// (sequence, KV head), wave 0 the K row and wave 1 the V row, each a quantised row
+// over all 64 lanes (two elements per lane, the wave-wide encoder; fp16 rows are
+// copied by 16 lanes); every load is issued up front (one memory round trip, no
+// barrier).
 #include "tq_encode.h"
 
 namespace tq {
@@ -141,26 +142,42 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, Append
 }
 
 template <int KFMT, int VFMT>
-__global__ __launch_bounds__(256) void append_one_kernel(EncodeArgs a, AppendStarts starts, int nb) {
-  const int j = threadIdx.x & 15;
-  const int pair = blockIdx.x * 8 + ((threadIdx.x >> 4) & 7);
-  const bool is_v = threadIdx.x >= 128;
-  const int i = pair / a.hkv, h = pair % a.hkv;
-  if (i >= nb || starts.count[i] == 0) return;  // whole 16-lane groups
+__global__ __launch_bounds__(128) void append_one_kernel(EncodeArgs a, AppendStarts starts) {
+  const int lane = threadIdx.x & 63;
+  const bool is_v = threadIdx.x >= 64;
+  const int i = blockIdx.x / a.hkv, h = blockIdx.x % a.hkv;
+  if (starts.count[i] == 0) return;  // the whole work group
   const int b = a.b0 + i;
   const int t = starts.start[i];
   const size_t row = size_t(b) * a.hkv + h;
   const uint16_t* src = (is_v ? a.v_new : a.k_new) + row * a.t_new * kDim;  // token 0 of the new rows
-  uint8_t code[8];
-  append_row<KFMT, VFMT>(a, row, t, is_v, src, j, code);
-  if (!is_v && h == 0 && j == 0) a.seq_lens[b] = t + 1;
+  if (is_v) {
+    if constexpr (VFMT == kFmtF16) {
+      if (lane < 16) store_f16_v_row(a, row, t, *reinterpret_cast<const uint4*>(src + 8 * lane), lane);
+    } else {
+      WaveVInputs<VFMT> in;
+      load_wave_v_inputs<VFMT>(a, row, t, src, lane, in);
+      uint32_t code[2];
+      append_v_row_wave<VFMT>(a, row, t, in, lane, code);
+    }
+  } else {
+    if constexpr (KFMT == kFmtF16) {
+      if (lane < 16) append_f16_k_row(a, row, t, src, lane);
+    } else {
+      WaveRowInputs<KFMT> in;
+      load_wave_row_inputs<KFMT>(src, a.k_signs, a.k_cb, lane, in);
+      uint32_t code[2];
+      append_k_row_wave<KFMT>(a, row, t, in, lane, code);
+    }
+    if (h == 0 && lane == 0) a.seq_lens[b] = t + 1;
+  }
 }
 
 template <int KF, int VF>
 void launch_one(const EncodeArgs& a, const AppendStarts& s, int nb, int max_tiles, bool single,
                 hipStream_t stream) {
   if (single)
-    hipLaunchKernelGGL((append_one_kernel<KF, VF>), dim3((nb * a.hkv + 7) / 8), dim3(256), 0, stream, a, s, nb);
+    hipLaunchKernelGGL((append_one_kernel<KF, VF>), dim3(nb * a.hkv), dim3(128), 0, stream, a, s);
   else
     hipLaunchKernelGGL((encode_append_kernel<KF, VF>), dim3(max_tiles, a.hkv, nb), dim3(256), 0, stream, a, s);
 }

@@ -4,7 +4,9 @@
 // Would Actually Work", item 1: a value is the codebook entry at its index times
 // the group norm).
 //
-// Per 128-element row x (fp16), held by a 16-lane group (lane j: elements 8j..8j+7):
+// Per 128-element row x (fp16), held by a 16-lane group (lane j: elements 8j..8j+7)
+// in the bulk encoder, or by a whole wave, two elements per lane, in the single-row
+// appends (see the wave-wide section below):
 //   norm  n = RNE_fp16(sqrt(sum x_i^2)), bit-exact: the sum of squares is taken in
 //         binary64 (every square is exact; 11 roundings at most along any path of
 //         the 16-lane sum), so sqrt is known to a relative 2^-49; the fp16 rounding
@@ -253,49 +255,6 @@ __device__ __forceinline__ void store_k_record(uint8_t* row_k, int t, const uint
   }
 }
 
-// Replace code e (0..31) of a turbo3 sub-block (words w0, w1, w2 = A, B, C) with c.
-// `e` may differ per call but the word each field lands in is chosen by selects,
-// never by a run-time register index.
-__device__ __forceinline__ void sub3_set(uint32_t& w0, uint32_t& w1, uint32_t& w2, int e, uint32_t c) {
-  const int jj = e & 3;
-  if (e < 24) {
-    const int sh = 8 * jj + ((e >> 2) & 1) * 3;
-    const uint32_t m = 7u << sh, v = (c & 7u) << sh;
-    const int word = e >> 3;
-    if (word == 0) w0 = (w0 & ~m) | v;
-    else if (word == 1) w1 = (w1 & ~m) | v;
-    else w2 = (w2 & ~m) | v;
-  } else {
-    const int upper = e >= 28 ? 1 : 0;
-    const int sh = 8 * jj + 6;
-    const uint32_t m = 3u << sh, v = (c & 3u) << sh;
-    if (upper) w1 = (w1 & ~m) | v;
-    else w0 = (w0 & ~m) | v;
-    const int hb = sh + upper;
-    w2 = (w2 & ~(1u << hb)) | (((c >> 2) & 1u) << hb);
-  }
-}
-
-// Append one new token (slot t) of one (sequence, KV head) row: a 16-lane group
-// encodes the row's K or V vector and writes it into the cache.  Split in two so a
-// caller can request every input first and do other work while they arrive: the
-// *_inputs loaders only issue loads; append_k_row / append_v_row encode and store,
-// leave the lane's 8 codes in `code` and return the norm bits.  V codes go
-// straight into the 64 V-tile chunks of the token's tile: lane j rewrites the 8
-// fields of its chunk 16*g + j that belong to the token's slot (group g, element
-// i), keeping the other slots' fields.  src: the group's fp16 row (element 8j is
-// at src + 8j).
-template <int FMT>
-struct RowInputs {
-  uint32_t w4[4];
-  float sg[8];
-  double beta[levels(FMT) - 1];
-  // the codebook's fp16 bits as byte tables (entries 8h..8h+7 in tab[4h..4h+3]:
-  // low bytes of entries 0-3, 4-7, high bytes of 0-3, 4-7), looked up with v_perm
-  // so dequantising needs no memory read and no run-time register index
-  uint32_t tab[levels(FMT) / 2];
-};
-
 // Decision thresholds (binary64) and v_perm byte tables of an fp16 codebook.
 template <int FMT>
 __device__ __forceinline__ void load_codebook(const uint16_t* cb, double (&beta)[levels(FMT) - 1],
@@ -323,13 +282,6 @@ __device__ __forceinline__ void load_codebook(const uint16_t* cb, double (&beta)
   }
 }
 
-template <int FMT>
-__device__ __forceinline__ void load_row_inputs(const uint16_t* src, const float* signs, const uint16_t* cb, int j,
-                                                RowInputs<FMT>& in) {
-  load_row_and_signs(src + 8 * j, signs, j, in.w4, in.sg);
-  load_codebook<FMT>(cb, in.beta, in.tab);
-}
-
 // Codebook entry at a 3- or 4-bit index, as fp32, from the byte tables.
 template <int FMT>
 __device__ __forceinline__ float codebook_at(const uint32_t (&tab)[levels(FMT) / 2], uint32_t idx) {
@@ -341,73 +293,6 @@ __device__ __forceinline__ float codebook_at(const uint32_t (&tab)[levels(FMT) /
     hi = (idx & 8u) ? hi8 : hi;
   }
   return half_bits_to_float(uint16_t((lo & 0xffu) | ((hi & 0xffu) << 8)));
-}
-
-template <int VFMT>
-struct VRowInputs {
-  RowInputs<VFMT> row;
-  uint32_t cw[v_chunk_bytes(VFMT) / 4];  // the chunk words the token's fields go into
-  uint8_t* tile;
-  int chunk;                             // chunk 16 g + j of the tile
-  int ei;                                // chunk element of the token's slot
-};
-
-template <int VFMT>
-__device__ __forceinline__ void load_v_inputs(const EncodeArgs& a, size_t row, int t, const uint16_t* src, int j,
-                                     VRowInputs<VFMT>& in) {
-  const int r = t % kTileTokens, g = slot_group(r);
-  in.ei = slot_elem(r);
-  in.tile = a.v_data + (row * (a.cap / kTileTokens) + t / kTileTokens) * v_tile_bytes(VFMT);
-  in.chunk = 16 * g + j;
-  // a token in slot 0 starts the tile: the other slots hold nothing visible yet
-#pragma unroll
-  for (int k = 0; k < v_chunk_bytes(VFMT) / 4; ++k)
-    in.cw[k] = r == 0 ? 0u
-                      : *reinterpret_cast<const uint32_t*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 4 * k));
-  load_row_inputs<VFMT>(src, a.v_signs, a.v_cb, j, in.row);
-}
-
-template <int VFMT>
-__device__ __forceinline__ uint16_t append_v_row(const EncodeArgs& a, size_t row, int t, VRowInputs<VFMT>& in, int j,
-                                        uint8_t (&code)[8]) {
-  const uint16_t nbits = encode_row<VFMT>(in.row.w4, in.row.sg, in.row.beta, j, code);
-  uint32_t* cw = in.cw;
-  // chunk element 8*n8 + ei is dim 8j + n8 of this token
-#pragma unroll
-  for (int n8 = 0; n8 < 8; ++n8) {
-    if (VFMT == kFmtTurbo4) {
-      const int sh = oct4_bit(in.ei);
-      cw[n8] = (cw[n8] & ~(15u << sh)) | (t4_nibble_of_index(code[n8]) << sh);
-    } else {
-      const int sb = n8 >> 2;  // sub-block of element 8*n8 + ei
-      sub3_set(cw[3 * sb], cw[3 * sb + 1], cw[3 * sb + 2], 8 * (n8 & 3) + in.ei, code[n8]);
-    }
-  }
-  if (VFMT == kFmtTurbo4) {  // two 16-byte pieces
-    *reinterpret_cast<uint4*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 0)) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-    *reinterpret_cast<uint4*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 16)) = make_uint4(cw[4], cw[5], cw[6], cw[7]);
-  } else {  // two 12-byte pieces (one sub-block each)
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(in.tile + v_chunk_byte_offset(VFMT, in.chunk, 12 * p));
-      dst[0] = cw[3 * p];
-      dst[1] = cw[3 * p + 1];
-      dst[2] = cw[3 * p + 2];
-    }
-  }
-  if (j == 0) a.v_norms[row * a.cap + t] = nbits;
-  return nbits;
-}
-
-// K side of a quantised K format (F16 K rows are copied by the callers).
-template <int KFMT>
-__device__ __forceinline__ uint16_t append_k_row(const EncodeArgs& a, size_t row, int t, const RowInputs<KFMT>& in, int j,
-                                        uint8_t (&code)[8]) {
-  const uint16_t nbits = encode_row<KFMT>(in.w4, in.sg, in.beta, j, code);
-  const size_t slot = row * a.cap + t;
-  if (j == 0) a.k_norms[slot] = nbits;
-  store_k_record<KFMT>(a.k_data + row * a.cap * k_record_bytes(KFMT), t, code, j);
-  return nbits;
 }
 
 // Copy an F16 K row (lane j: elements 8j..8j+7).
@@ -428,31 +313,8 @@ __device__ __forceinline__ void store_f16_v_row(const EncodeArgs& a, size_t row,
   for (int nb = 0; nb < 8; ++nb) chunk[8 * nb] = uint16_t(w[nb >> 1] >> (16 * (nb & 1)));
 }
 
-// Both sides in one call (loads, then encode and store).
-template <int KFMT, int VFMT>
-__device__ __forceinline__ uint16_t append_row(const EncodeArgs& a, size_t row, int t, bool is_v, const uint16_t* src,
-                                      int j, uint8_t (&code)[8]) {
-  if (is_v) {
-    if constexpr (VFMT == kFmtF16) {
-      store_f16_v_row(a, row, t, *reinterpret_cast<const uint4*>(src + 8 * j), j);
-      return 0;
-    } else {
-      VRowInputs<VFMT> in;
-      load_v_inputs<VFMT>(a, row, t, src, j, in);
-      return append_v_row<VFMT>(a, row, t, in, j, code);
-    }
-  }
-  if (KFMT == kFmtF16) {
-    append_f16_k_row(a, row, t, src, j);
-    return 0;
-  }
-  constexpr int KQ = KFMT == kFmtF16 ? kFmtTurbo3 : KFMT;  // (F16 K returned above)
-  RowInputs<KQ> in;
-  load_row_inputs<KQ>(src, a.k_signs, a.k_cb, j, in);
-  return append_k_row<KQ>(a, row, t, in, j, code);
-}
-
-// ---- One row over a whole wave (the decode step's single-row K append).  Lane
+// ---- One row over a whole wave (the single-row appends: the decode step's and the
+// one-row append kernel's).  Lane
 // l = 16q + 4c + b holds elements e0 = 32q + 8c + b and e0 + 4: element bits 0-1 are
 // lane bits 0-1, bit 2 is the lane's pair, bits 3-4 are lane bits 2-3 and bits 5-6
 // lane bits 4-5.  The arithmetic is encode_row's (the same exact binary64
@@ -574,6 +436,16 @@ __device__ __forceinline__ void store_k_record_wave(uint8_t* row_k, int t, const
       row_k[k_byte_offset(kFmtTurbo3, t, 12 * (lane >> 4) + 4 * c + b)] = uint8_t(byte);
     }
   }
+}
+
+// Encode token t's K row over the whole wave and write its norm and record.
+template <int KFMT>
+__device__ __forceinline__ uint16_t append_k_row_wave(const EncodeArgs& a, size_t row, int t,
+                                                      const WaveRowInputs<KFMT>& in, int lane, uint32_t (&code)[2]) {
+  const uint16_t nbits = encode_wave_row<KFMT>(in, lane, code);
+  if (lane == 0) a.k_norms[row * a.cap + t] = nbits;
+  store_k_record_wave<KFMT>(a.k_data + row * a.cap * k_record_bytes(KFMT), t, code, lane);
+  return nbits;
 }
 
 // The V side over the whole wave: this lane's two dims 8j + b and 8j + 4 + b (j = 4q + c)

@@ -117,6 +117,31 @@ def test_decode_parity(name, variant, codebooks):
     _say(f"[{name} v{variant}] worst rel-L2 {worst[0]:.2e} max-abs {worst[1]:.2e}")
 
 
+@pytest.mark.parametrize("k_format,v_format", [("turbo3", "turbo3"), ("turbo4", "turbo4"), ("turbo4", "turbo3"),
+                                               ("f16", "turbo3"), ("f16", "f16")])
+def test_one_token_appends_bit_exact(k_format, v_format, codebooks):
+    """tq_encode_append of one token per sequence (the one-row kernel, each row encoded over
+    a whole wave) into every kind of V-tile slot -- a fresh tile, mid-tile, its last slot --
+    after prefills of 0 to 100 tokens: codes and norms against the oracle's encode of the same
+    rows, the earlier tokens' codes kept."""
+    import quantized_kv_cache_decode_amd as tq
+    from synth import kv_slice, new_token_kv
+    pre = [0, 1, 5, 31, 32, 33, 63, 64, 100]
+    w = S.scaled(get_workload(0), batch=len(pre), num_q_heads=4, num_kv_heads=2, k_format=k_format,
+                 v_format=v_format)
+    k = [np.stack([kv_slice(w, 0, "k", b, h, n) for h in range(2)]) for b, n in enumerate(pre)]
+    v = [np.stack([kv_slice(w, 0, "v", b, h, n) for h in range(2)]) for b, n in enumerate(pre)]
+    cache = S.encode_on_gpu(w, k, v, pre, 128)
+    kn = [np.stack([new_token_kv(w, 0, "k", b, h, 0) for h in range(2)]) for b in range(len(pre))]
+    vn = [np.stack([new_token_kv(w, 0, "v", b, h, 0) for h in range(2)]) for b in range(len(pre))]
+    tq.tq_encode_append(cache, S.padded_tensor(kn, 1), S.padded_tensor(vn, 1))
+    np.testing.assert_array_equal(cache.seq_lens.cpu().numpy(), np.array(pre) + 1)
+    for b, n in enumerate(pre):
+        k_all = np.concatenate([k[b], kn[b]], axis=1)
+        v_all = np.concatenate([v[b], vn[b]], axis=1)
+        S.compare_codes(cache, b, k_all, v_all, n + 1, w, codebooks)
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_sixteen_decode_steps_gqa_4_over_2(variant, codebooks):
     """The parity shape of mlxcel PR #369 ("Result"): GQA 4 query heads over 2 KV heads,

@@ -13,12 +13,11 @@
 // is independent (one memory round trip for up to 4 * kBatch splits); each group
 // keeps a running (m, l, o), and the four groups are merged with the gfx950 row
 // swaps (lane bit 4, then bit 5) -- no LDS, no barrier.  Every group then holds
-// the merged row in the 16-lane layout the in-register Walsh-Hadamard transform
-// wants; group 0 stores it.  When the call has few (sequence, head) rows (latency-
-// bound calls: a few dozen waves on a 256-CU chip), a row gets WAVES waves: lane group
-// sg of wave w takes splits 4w + sg, 4w + sg + 4 WAVES, ..., each wave merges its groups
-// as above, and wave 0 merges the waves' states, left in LDS, against their common
-// maximum.
+// the merged row; the inverse rotation spreads it over the wave.  When the call has
+// few (sequence, head) rows (latency-bound calls: a few dozen waves on a 256-CU
+// chip), a row gets WAVES waves: lane group sg of wave w takes splits 4w + sg,
+// 4w + sg + 4 WAVES, ..., every group leaves its state in LDS, and wave 0 merges all
+// 4 WAVES of them against their common maximum in one step.
 #include <math.h>
 
 #include <algorithm>
@@ -210,74 +209,82 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(DecodeArgs a, SeqLe
     acc.m = mn;
   }
 
-  acc = merge_across<false>(acc);  // groups {0,1} and {2,3}
-  acc = merge_across<true>(acc);   // then the two halves: every lane holds the wave's merged row
-  if constexpr (WAVES > 1) {
-    __shared__ float st_o[WAVES][kDim];
-    __shared__ float st_ml[WAVES][2];
-    if (sg == 0) {
-      float4* d = reinterpret_cast<float4*>(&st_o[wave][8 * j]);
-      d[0] = make_float4(acc.o[0], acc.o[1], acc.o[2], acc.o[3]);
-      d[1] = make_float4(acc.o[4], acc.o[5], acc.o[6], acc.o[7]);
-      if (j == 0) {
-        st_ml[wave][0] = acc.m;
-        st_ml[wave][1] = acc.l;
-      }
+  // the step's length update, once every reader of the old length has finished
+  if (step && hq == 0 && threadIdx.x == 0) a.app.seq_lens[b] = L + 1;
+  const size_t row = size_t(b) * a.hkv * G + hq;
+  if constexpr (WAVES == 1) {
+    acc = merge_across<false>(acc);  // groups {0,1} and {2,3}
+    acc = merge_across<true>(acc);   // then the two halves: every lane holds the merged row
+    float v[8];
+    const float inv = nparts > 0 ? 1.f / acc.l : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = nparts > 0 ? acc.o[i] * inv : 0.f;
+    if (INVERSE && a.v_rotated) {
+      // lane (j, sg) rotates and stores elements 8j + 2sg and 8j + 2sg + 1
+      const float s8[8] = {sgn0.x, sgn0.y, sgn0.z, sgn0.w, sgn1.x, sgn1.y, sgn1.z, sgn1.w};
+      const float x = sg == 0 ? v[0] : sg == 1 ? v[2] : sg == 2 ? v[4] : v[6];
+      const float y = sg == 0 ? v[1] : sg == 1 ? v[3] : sg == 2 ? v[5] : v[7];
+      const float s0 = sg == 0 ? s8[0] : sg == 1 ? s8[2] : sg == 2 ? s8[4] : s8[6];
+      const float s1 = sg == 0 ? s8[1] : sg == 1 ? s8[3] : sg == 2 ? s8[5] : s8[7];
+      const uint32_t wv = inverse_rotate_pair_f16(x, y, s0, s1, lane);
+      *reinterpret_cast<uint32_t*>(a.out + row * kDim + 8 * j + 2 * sg) = wv;
+    } else if (INVERSE) {   // fp16 V: already the original basis
+      uint32_t w[4];
+      round_row_f16(v, w);
+      if (sg == 0) *reinterpret_cast<uint4*>(a.out + row * kDim + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if (sg == 0) {
+      float4* dst = reinterpret_cast<float4*>(a.out_rot + row * kDim + 8 * j);
+      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
     }
+  } else {
+    // Few rows: every lane group's state goes to LDS, and wave 0 merges all of them
+    // against their common maximum in one step, summed in group order (so every dim
+    // uses the same weights), lane (j, sg) taking dims 8j + 2sg and 8j + 2sg + 1 --
+    // the layout the wave-wide inverse rotation takes.
+    constexpr int NG = kGroups * WAVES;
+    __shared__ float st_o[NG][kDim];
+    __shared__ float2 st_ml[NG];
+    const int gi = kGroups * wave + sg;
+    float4* d = reinterpret_cast<float4*>(&st_o[gi][8 * j]);
+    d[0] = make_float4(acc.o[0], acc.o[1], acc.o[2], acc.o[3]);
+    d[1] = make_float4(acc.o[4], acc.o[5], acc.o[6], acc.o[7]);
+    if (j == 0) st_ml[gi] = make_float2(acc.m, acc.l);
     __syncthreads();
     if (wave != 0) return;
-    // The waves' states against their common maximum, summed in wave order (every
-    // lane computes the same bits): one reduction instead of a chain of pairwise merges.
-    float ms[WAVES], ls[WAVES];
-    float4 xa[WAVES], xb[WAVES];
+    const int d0 = 8 * j + 2 * sg;
+    float2 ml[NG];
+    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      ms[w] = st_ml[w][0];
-      ls[w] = st_ml[w][1];
-      xa[w] = reinterpret_cast<const float4*>(&st_o[w][8 * j])[0];
-      xb[w] = reinterpret_cast<const float4*>(&st_o[w][8 * j])[1];
+    for (int i = 0; i < NG; ++i) {
+      ml[i] = st_ml[i];
+      M = fmaxf(M, ml[i].x);
     }
-    float M = ms[0];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) M = fmaxf(M, ms[w]);
-    acc.m = M;
-    acc.l = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc.o[i] = 0.f;
+    float l = 0.f, x = 0.f, y = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) {
-        const float c = weight(ms[w], M);
-        acc.l += c * ls[w];
-        acc.o[0] += c * xa[w].x; acc.o[1] += c * xa[w].y; acc.o[2] += c * xa[w].z; acc.o[3] += c * xa[w].w;
-        acc.o[4] += c * xb[w].x; acc.o[5] += c * xb[w].y; acc.o[6] += c * xb[w].z; acc.o[7] += c * xb[w].w;
+      for (int i = 0; i < NG; ++i) {
+        const float c = weight(ml[i].x, M);
+        const float2 o = *reinterpret_cast<const float2*>(&st_o[i][d0]);
+        l += c * ml[i].y;
+        x += c * o.x;
+        y += c * o.y;
       }
     }
-  }
-  float v[8];
-  const float inv = nparts > 0 ? 1.f / acc.l : 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = nparts > 0 ? acc.o[i] * inv : 0.f;
-  // the step's length update, once every reader of the old length has finished
-  if (step && hq == 0 && lane == 0) a.app.seq_lens[b] = L + 1;
-  const size_t row = size_t(b) * a.hkv * G + hq;
-  if (INVERSE && a.v_rotated) {
-    // lane (j, sg) rotates and stores elements 8j + 2sg and 8j + 2sg + 1
-    const float s8[8] = {sgn0.x, sgn0.y, sgn0.z, sgn0.w, sgn1.x, sgn1.y, sgn1.z, sgn1.w};
-    const float x = sg == 0 ? v[0] : sg == 1 ? v[2] : sg == 2 ? v[4] : v[6];
-    const float y = sg == 0 ? v[1] : sg == 1 ? v[3] : sg == 2 ? v[5] : v[7];
-    const float s0 = sg == 0 ? s8[0] : sg == 1 ? s8[2] : sg == 2 ? s8[4] : s8[6];
-    const float s1 = sg == 0 ? s8[1] : sg == 1 ? s8[3] : sg == 2 ? s8[5] : s8[7];
-    const uint32_t wv = inverse_rotate_pair_f16(x, y, s0, s1, lane);
-    *reinterpret_cast<uint32_t*>(a.out + row * kDim + 8 * j + 2 * sg) = wv;
-  } else if (INVERSE) {   // fp16 V: already the original basis
-    uint32_t w[4];
-    round_row_f16(v, w);
-    if (sg == 0) *reinterpret_cast<uint4*>(a.out + row * kDim + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else if (sg == 0) {
-    float4* dst = reinterpret_cast<float4*>(a.out_rot + row * kDim + 8 * j);
-    dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-    dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+    const float inv = nparts > 0 ? 1.f / l : 0.f;
+    x = nparts > 0 ? x * inv : 0.f;
+    y = nparts > 0 ? y * inv : 0.f;
+    if (INVERSE && a.v_rotated) {
+      const float s8[8] = {sgn0.x, sgn0.y, sgn0.z, sgn0.w, sgn1.x, sgn1.y, sgn1.z, sgn1.w};
+      const float s0 = sg == 0 ? s8[0] : sg == 1 ? s8[2] : sg == 2 ? s8[4] : s8[6];
+      const float s1 = sg == 0 ? s8[1] : sg == 1 ? s8[3] : sg == 2 ? s8[5] : s8[7];
+      *reinterpret_cast<uint32_t*>(a.out + row * kDim + d0) = inverse_rotate_pair_f16(x, y, s0, s1, lane);
+    } else if (INVERSE) {   // fp16 V: already the original basis
+      *reinterpret_cast<uint32_t*>(a.out + row * kDim + d0) =
+          uint32_t(__half_as_ushort(__float2half_rn(x))) | (uint32_t(__half_as_ushort(__float2half_rn(y))) << 16);
+    } else {
+      *reinterpret_cast<float2*>(a.out_rot + row * kDim + d0) = make_float2(x, y);
+    }
   }
 }
 

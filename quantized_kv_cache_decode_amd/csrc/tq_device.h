@@ -101,9 +101,9 @@ constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 
 // Value of lane (lane ^ M) within the same aligned 16-lane row, M in {1, 2, 4, 8},
 // through DPP moves (VALU data paths, no LDS round trip): quad_perm covers xor 1
-// and 2; xor 4 = half-row mirror (i ^ 7) then quad reversal (i ^ 3); xor 8 = row
-// mirror (i ^ 15) then half-row mirror (i ^ 7).  All 16 lanes of the row must be
-// active.
+// and 2; xor 4 = half-row mirror (i ^ 7) then quad reversal (i ^ 3); xor 8 = the
+// row rotated by 8 lanes ((i + 8) mod 16 = i ^ 8).  All 16 lanes of the row must
+// be active.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xf, 0xf, false));
@@ -114,7 +114,7 @@ __device__ __forceinline__ uint32_t xor_lane16(uint32_t v) {
   if constexpr (M == 1) return dpp_u32<0xb1>(v);                 // quad_perm [1,0,3,2]
   else if constexpr (M == 2) return dpp_u32<0x4e>(v);            // quad_perm [2,3,0,1]
   else if constexpr (M == 4) return dpp_u32<0x1b>(dpp_u32<0x141>(v));  // half mirror, quad_perm [3,2,1,0]
-  else return dpp_u32<0x141>(dpp_u32<0x140>(v));                 // row mirror, half mirror
+  else return dpp_u32<0x128>(v);                                // row_ror:8
 }
 template <int M>
 __device__ __forceinline__ float xor_lane16(float v) {

@@ -466,13 +466,12 @@ __device__ __forceinline__ void q_pin(QRaw& q) {
   pin4(q.s1);
 }
 
-// (Passes kfirst, kfirst + kstep, ... only: the waves of a work group share the rows.)
 __device__ __forceinline__ void q_finish(const DecodeArgs& a, float (*qs)[kDim], int lane, const QRaw& q,
-                                         bool rotate, int kfirst = 0, int kstep = 1) {
+                                         bool rotate) {
   const int G = a.group, j = lane & 15, r0 = lane >> 4;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    if ((k - kfirst) % kstep == 0 && k >= kfirst && 4 * k + r0 < G) {  // whole 16-lane segments
+    if (4 * k + r0 < G) {  // whole 16-lane segments
       float v[8];
       const uint32_t w[8] = {q.lo[k].x, q.lo[k].y, q.lo[k].z, q.lo[k].w, q.hi[k].x, q.hi[k].y, q.hi[k].z, q.hi[k].w};
       if (a.q_fp32) {
@@ -490,6 +489,100 @@ __device__ __forceinline__ void q_finish(const DecodeArgs& a, float (*qs)[kDim],
       d[0] = make_float4(v[0], v[1], v[2], v[3]);
       d[1] = make_float4(v[4], v[5], v[6], v[7]);
     }
+  }
+}
+
+// Four waves sharing a split stage its q rows two at a time: wave w takes rows
+// 2w + lane / 32 (and 8 more for G > 8), each over 32 lanes of four elements
+// (4 (lane % 32) .. + 3).  The rotation runs fwht128_row's butterflies in its order
+// -- element bits 0-1 in-lane, bits 2-5 across lanes xor 1, 2, 4, 8, bit 6 across the
+// row swap -- each the same single add or subtract, so q comes out with the same bits
+// as from the 16-lane routine, on half its chain.  Rows past G re-read row G - 1 and
+// are rotated but never stored (no lane of the wave is left out of an exchange).
+struct QRawW {
+  uint4 w[2];    // fp32 q: four floats; fp16 q: four halves in .x, .y
+  float4 s;      // this lane's K sign flips (elements 4 (lane % 32) .. + 3)
+};
+
+template <bool SIGNS>
+__device__ __forceinline__ void q_request_w(const DecodeArgs& a, size_t row, int lane, int wave, QRawW& q) {
+  const int G = a.group, j = lane & 31;
+  const bool f32 = a.q_fp32 != 0;
+  const size_t esz = f32 ? 4 : 2;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {   // 16 bytes (fp32) or 8 (fp16, read twice): no branch around a load
+    const size_t r = row * G + min(8 * k + 2 * wave + (lane >> 5), G - 1);
+    const uint8_t* p = static_cast<const uint8_t*>(a.q_in) + (r * kDim + 4 * j) * esz;
+    const uint2 lo = *reinterpret_cast<const uint2*>(p);
+    const uint2 hi = *reinterpret_cast<const uint2*>(p + (f32 ? 8 : 0));
+    q.w[k] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  q.s = SIGNS ? reinterpret_cast<const float4*>(a.k_signs)[j] : make_float4(1.f, 1.f, 1.f, 1.f);
+}
+
+__device__ __forceinline__ void q_pin_w(QRawW& q) {
+  pin4(q.w[0]);
+  pin4(q.w[1]);
+  pin4(q.s);
+}
+
+__device__ __forceinline__ void q_finish_w(const DecodeArgs& a, float (*qs)[kDim], int lane, int wave, const QRawW& q,
+                                           bool rotate) {
+  const int G = a.group, j = lane & 31;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (8 * k >= G) break;   // (uniform)
+    float v[4];
+    if (a.q_fp32) {
+      v[0] = __uint_as_float(q.w[k].x);
+      v[1] = __uint_as_float(q.w[k].y);
+      v[2] = __uint_as_float(q.w[k].z);
+      v[3] = __uint_as_float(q.w[k].w);
+    } else {
+      v[0] = half_bits_to_float(uint16_t(q.w[k].x));
+      v[1] = half_bits_to_float(uint16_t(q.w[k].x >> 16));
+      v[2] = half_bits_to_float(uint16_t(q.w[k].y));
+      v[3] = half_bits_to_float(uint16_t(q.w[k].y >> 16));
+    }
+    if (rotate) {
+      v[0] *= q.s.x;
+      v[1] *= q.s.y;
+      v[2] *= q.s.z;
+      v[3] *= q.s.w;
+#pragma unroll
+      for (int h = 1; h < 4; h <<= 1) {   // element bits 0, 1
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (!(i & h)) {
+            const float x = v[i], y = v[i + h];
+            v[i] = x + y;
+            v[i + h] = x - y;
+          }
+        }
+      }
+      auto stage = [&](auto m_c) {        // element bits 2..5: lanes xor 1, 2, 4, 8
+        constexpr int M = decltype(m_c)::value;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float o = xor_lane16<M>(v[i]);
+          v[i] = (lane & M) ? (o - v[i]) : (v[i] + o);
+        }
+      };
+      stage(std::integral_constant<int, 1>{});
+      stage(std::integral_constant<int, 2>{});
+      stage(std::integral_constant<int, 4>{});
+      stage(std::integral_constant<int, 8>{});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {         // element bit 6: lanes xor 16 (row swap)
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i]), false, false);
+        const float lo = __uint_as_float(r[0]), hi = __uint_as_float(r[1]);
+        v[i] = (lane & 16) ? (lo - hi) : (lo + hi);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] *= kInvSqrtD;
+    }
+    const int r = 8 * k + 2 * wave + (lane >> 5);
+    if (r < G) reinterpret_cast<float4*>(&qs[r][4 * j])[0] = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -675,7 +768,9 @@ __global__ __launch_bounds__(64 * TS) void decode_mfma_kernel(DecodeArgs a, SeqL
   // q rows first, then the first iteration's words: waiting for q (the oldest
   // requests) leaves the K/V words in flight while q is rotated and staged.
   QRaw qraw;
-  q_request<KFMT != kFmtF16>(a, row, lane, qraw);
+  QRawW qrw;
+  if constexpr (TS > 1) q_request_w<KFMT != kFmtF16>(a, row, lane, wv, qrw);
+  else q_request<KFMT != kFmtF16>(a, row, lane, qraw);
   // the 8 fp16 codebook entries each side's byte table needs (turbo4: the 8
   // magnitudes, entries 8..15); none for an fp16 side
   uint4 cbraw[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
@@ -685,7 +780,8 @@ __global__ __launch_bounds__(64 * TS) void decode_mfma_kernel(DecodeArgs a, SeqL
   load_k(t0);
   load_v(t0);
   __builtin_amdgcn_sched_barrier(0);  // ... and every K/V request ahead of the wait for q
-  q_pin(qraw);
+  if constexpr (TS > 1) q_pin_w(qrw);
+  else q_pin(qraw);
   pin4(cbraw[0]);
   pin4(cbraw[1]);
 
@@ -705,7 +801,8 @@ __global__ __launch_bounds__(64 * TS) void decode_mfma_kernel(DecodeArgs a, SeqL
     vtab = make_table(c);
   }
 
-  q_finish(a, qs, lane, qraw, a.q_rotate != 0, wv, TS);
+  if constexpr (TS > 1) q_finish_w(a, qs, lane, wv, qrw, a.q_rotate != 0);
+  else q_finish(a, qs, lane, qraw, a.q_rotate != 0);
   __syncthreads();
 
   // Sparse K: kbound * n is an upper bound on this lane's column's score (log2

@@ -908,7 +908,9 @@ __global__ __launch_bounds__(64 * TS) void decode_mfma_kernel(DecodeArgs a, SeqL
     mt = xmax4(mt);
     const float m_new = fmaxf(m_run, mt);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    if (!TQ_MFMA_LAZY_RESCALE || __any(m_new > m_run)) {   // rescale only when a running max grew
+    // rescale only when a running max grew, and not from -inf: while a column's max is
+    // -inf its l and o are still exactly 0 (every weight so far was 2^-inf = 0)
+    if (!TQ_MFMA_LAZY_RESCALE || __any(m_new > m_run && m_run > -INFINITY)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       l_run *= alpha;
 #pragma unroll

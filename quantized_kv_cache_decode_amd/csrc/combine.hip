@@ -239,10 +239,11 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(DecodeArgs a, SeqLe
     }
   } else {
     // Few rows: every lane group's state goes to LDS, and wave 0 merges all of them
-    // against their common maximum in one step, summed in group order (so every dim
-    // uses the same weights), lane (j, sg) taking dims 8j + 2sg and 8j + 2sg + 1 --
-    // the layout the wave-wide inverse rotation takes.
+    // against their common maximum in one step (every dim with the same weights),
+    // lane (j, sg) taking dims 8j + 2sg and 8j + 2sg + 1 -- the layout the wave-wide
+    // inverse rotation takes.
     constexpr int NG = kGroups * WAVES;
+    static_assert((NG & (NG - 1)) == 0, "pairwise trees over a power of two of states");
     __shared__ float st_o[NG][kDim];
     __shared__ float2 st_ml[NG];
     const int gi = kGroups * wave + sg;
@@ -254,23 +255,39 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(DecodeArgs a, SeqLe
     if (wave != 0) return;
     const int d0 = 8 * j + 2 * sg;
     float2 ml[NG];
-    float M = -INFINITY;
+    float mx[NG];
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       ml[i] = st_ml[i];
-      M = fmaxf(M, ml[i].x);
+      mx[i] = ml[i].x;
     }
-    float l = 0.f, x = 0.f, y = 0.f;
-    if (M != -INFINITY) {
+    // the maximum and the three sums as fixed pairwise trees (log2 NG levels instead
+    // of NG - 1 dependent steps; the same order in every lane and on every call)
 #pragma unroll
-      for (int i = 0; i < NG; ++i) {
-        const float c = weight(ml[i].x, M);
-        const float2 o = *reinterpret_cast<const float2*>(&st_o[i][d0]);
-        l += c * ml[i].y;
-        x += c * o.x;
-        y += c * o.y;
+    for (int w = 1; w < NG; w *= 2)
+#pragma unroll
+      for (int i = 0; i < NG; i += 2 * w) mx[i] = fmaxf(mx[i], mx[i + w]);
+    const float M = mx[0];
+    float pl[NG], px[NG], py[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const float c = weight(ml[i].x, M);   // (0 for an empty state)
+      const float2 o = *reinterpret_cast<const float2*>(&st_o[i][d0]);
+      pl[i] = c * ml[i].y;
+      px[i] = c * o.x;
+      py[i] = c * o.y;
+    }
+#pragma unroll
+    for (int w = 1; w < NG; w *= 2) {
+#pragma unroll
+      for (int i = 0; i < NG; i += 2 * w) {
+        pl[i] += pl[i + w];
+        px[i] += px[i + w];
+        py[i] += py[i + w];
       }
     }
+    const float l = pl[0];
+    float x = px[0], y = py[0];
     const float inv = nparts > 0 ? 1.f / l : 0.f;
     x = nparts > 0 ? x * inv : 0.f;
     y = nparts > 0 ? y * inv : 0.f;

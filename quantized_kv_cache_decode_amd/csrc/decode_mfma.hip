@@ -1,6 +1,7 @@
 // MFMA split-K decode attention for gfx950 (the default decode kernel, variant 0).
 //
-// One wave per work item (split s of KV head h of sequence b).  Both
+// One wave per work item (split s of KV head h of sequence b); on latency-bound
+// calls four waves per split, each taking a quarter of its tokens.  Both
 // contractions run on v_mfma_f32_16x16x32_f16 with fp32 accumulation; the VALU
 // only dequantises codes into MFMA operands and runs the online softmax.
 //

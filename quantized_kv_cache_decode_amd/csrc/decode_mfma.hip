@@ -64,21 +64,19 @@ struct ByteTable {
   uint32_t lo0, lo1, hi0, hi1;
 };
 
-__device__ inline ByteTable make_table(const uint16_t* v8) {
+__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) { return __builtin_amdgcn_perm(hi, lo, sel); }
+
+// The byte tables of 8 fp16 entries held as four words (entry 2i in the low half of
+// w[i]): the low bytes of entries 0-3 are bytes 0, 2 of w[0], w[1], their high bytes
+// bytes 1, 3; entries 4-7 likewise from w[2], w[3].  One byte gather each.
+__device__ inline ByteTable make_table(const uint32_t (&w)[4]) {
   ByteTable t;
-  t.lo0 = t.lo1 = t.hi0 = t.hi1 = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t a = v8[i], b = v8[4 + i];
-    t.lo0 |= (a & 0xffu) << (8 * i);
-    t.hi0 |= (a >> 8) << (8 * i);
-    t.lo1 |= (b & 0xffu) << (8 * i);
-    t.hi1 |= (b >> 8) << (8 * i);
-  }
+  t.lo0 = perm(w[1], w[0], 0x06040200u);
+  t.hi0 = perm(w[1], w[0], 0x07050301u);
+  t.lo1 = perm(w[3], w[2], 0x06040200u);
+  t.hi1 = perm(w[3], w[2], 0x07050301u);
   return t;
 }
-
-__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) { return __builtin_amdgcn_perm(hi, lo, sel); }
 
 // four table lookups (selector bytes 0..7) -> two dwords of fp16 pairs
 __device__ inline void lookup4(const ByteTable& t, uint32_t sel, uint32_t& d0, uint32_t& d1) {
@@ -791,15 +789,8 @@ __global__ __launch_bounds__(64 * TS) void decode_mfma_kernel(DecodeArgs a, SeqL
   {
     const uint32_t kc[4] = {cbraw[0].x, cbraw[0].y, cbraw[0].z, cbraw[0].w};
     const uint32_t vc[4] = {cbraw[1].x, cbraw[1].y, cbraw[1].z, cbraw[1].w};
-    uint16_t c[8];
-    if (KFMT != kFmtF16) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = uint16_t(kc[i >> 1] >> (16 * (i & 1)));
-      ktab = make_table(c);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = uint16_t(vc[i >> 1] >> (16 * (i & 1)));
-    vtab = make_table(c);
+    if (KFMT != kFmtF16) ktab = make_table(kc);
+    vtab = make_table(vc);
   }
 
   if constexpr (TS > 1) q_finish_w(a, qs, lane, wv, qrw, a.q_rotate != 0);

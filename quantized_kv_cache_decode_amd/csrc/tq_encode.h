@@ -314,10 +314,9 @@ __device__ __forceinline__ void store_f16_v_row(const EncodeArgs& a, size_t row,
 }
 
 // ---- One row over a whole wave (the single-row appends: the decode step's and the
-// one-row append kernel's).  Lane
-// l = 16q + 4c + b holds elements e0 = 32q + 8c + b and e0 + 4: element bits 0-1 are
-// lane bits 0-1, bit 2 is the lane's pair, bits 3-4 are lane bits 2-3 and bits 5-6
-// lane bits 4-5.  The arithmetic is encode_row's (the same exact binary64
+// one-row append kernel's).  Lane l = 16q + 4c + b holds elements e0 = 32q + 8c + b
+// and e0 + 4: element bits 0-1 are lane bits 0-1, bit 2 is the lane's pair, bits 3-4
+// are lane bits 2-3 and bits 5-6 lane bits 4-5.  The arithmetic is encode_row's (the same exact binary64
 // transform, the same norm decision, the same thresholds), so codes and norms are
 // bit-identical to it; each stage handles two values per lane instead of eight.
 // All 64 lanes of the wave execute these routines together.
@@ -450,8 +449,9 @@ __device__ __forceinline__ uint16_t append_k_row_wave(const EncodeArgs& a, size_
 
 // The V side over the whole wave: this lane's two dims 8j + b and 8j + 4 + b (j = 4q + c)
 // sit in chunk 16 g + j of the token's tile (g its slot group), in chunk words b and
-// 4 + b (turbo4) or word b of the chunk's two sub-blocks (turbo3), where the token's
-// field is chunk element 8 * (dim % 4) + ei.  turbo3: the fields of dims 8j + 3 and
+// 4 + b (turbo4: a dim's word holds its 8 slots' nibbles) or word b of the chunk's two
+// sub-blocks (turbo3: the token's field for dim d is element 8 (d % 4) + ei of d's
+// sub-block, ei the slot's element index).  turbo3: the fields of dims 8j + 3 and
 // 8j + 7 (sub-block elements 24 + ei) are split over words 0-2, so lane 3 of each
 // quad writes nothing and lanes 0-2 take its codes (a quad broadcast) into the words
 // they rewrite.  Every other slot's fields are kept.

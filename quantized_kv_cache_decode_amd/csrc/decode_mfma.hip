@@ -377,15 +377,16 @@ __device__ __forceinline__ void store_head_scores_wave(const DecodeArgs& a, cons
   }
 }
 
-// K side, quantised K, over the whole wave: encode and store the row, rebuild
-// k = s_K * H(n_K * c_K[idx]) / sqrt(128) two elements per lane (q stays unrotated:
-// q_rot . k_hat = q . k, the rotation being orthonormal) and score it.
+// K side, quantised K, over the whole wave: encode and store the row and rebuild
+// k = s_K * H(n_K * c_K[idx]) / sqrt(128), two elements per lane (x0, x1: elements e0,
+// e0 + 4); q stays unrotated, since q_rot . k_hat = q . k (the rotation is orthonormal).
 template <int KFMT>
-__device__ __forceinline__ void append_k_partial_wave(const DecodeArgs& a, const float (*qs)[kDim], size_t row, int L,
-                                                      int lane, const WaveRowInputs<KFMT>& kin) {
+__device__ __forceinline__ void append_k_rebuild_wave(const DecodeArgs& a, size_t row, int L, int lane,
+                                                      const WaveRowInputs<KFMT>& kin, float& x0, float& x1) {
   uint32_t code[2];
   const float nk = half_bits_to_float(append_k_row_wave<KFMT>(a.app, row, L, kin, lane, code));
-  float x0 = nk * codebook_at<KFMT>(kin.tab, code[0]), x1 = nk * codebook_at<KFMT>(kin.tab, code[1]);
+  x0 = nk * codebook_at<KFMT>(kin.tab, code[0]);
+  x1 = nk * codebook_at<KFMT>(kin.tab, code[1]);
   {
     const float u = x0, v = x1;   // element bit 2, in-lane
     x0 = u + v;
@@ -404,6 +405,10 @@ __device__ __forceinline__ void append_k_partial_wave(const DecodeArgs& a, const
   stage(std::integral_constant<int, 5>{});
   x0 = x0 * kInvSqrtD * kin.sg[0];
   x1 = x1 * kInvSqrtD * kin.sg[1];
+}
+
+__device__ __forceinline__ void append_k_scores_wave(const DecodeArgs& a, const float (*qs)[kDim], size_t row,
+                                                     int lane, float x0, float x1) {
   const int e0 = wave_row_elem(lane);
   if (a.group <= 4) store_head_scores_wave<4>(a, qs, row, lane, e0, x0, x1);
   else if (a.group <= 8) store_head_scores_wave<8>(a, qs, row, lane, e0, x0, x1);
@@ -585,30 +590,48 @@ __device__ __forceinline__ void q_finish_w(const DecodeArgs& a, float (*qs)[kDim
   }
 }
 
-// Decode step, K side as a whole: request the row and thresholds, stage q while
-// they arrive, then encode, store and score.  All 64 lanes of the wave.
-template <int KFMT, int VFMT>
+// Decode step, K side as a whole: request the row and thresholds, encode, store and
+// rebuild the row, then score it against the unrotated q rows in qs after the work
+// group's one barrier.  STAGE_Q: this wave also stages q (requested first, so its
+// round trip overlaps the row's); otherwise another wave of the work group does
+// (append_stage_q), off this wave's chain.
+template <int KFMT, bool STAGE_Q>
 __device__ __forceinline__ void append_k_work(const DecodeArgs& a, float (*qs)[kDim], size_t row, int L, int lane) {
   QRaw q;
-  q_request<false>(a, row, lane, q);   // q stays unrotated: the K row is taken back out of the codec basis
+  if constexpr (STAGE_Q) q_request<false>(a, row, lane, q);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (KFMT == kFmtF16) {
     uint4 kraw = make_uint4(0, 0, 0, 0);
     if (lane < 16) kraw = *reinterpret_cast<const uint4*>(a.app.k_new + row * kDim + 8 * lane);
     __builtin_amdgcn_sched_barrier(0);
-    q_pin(q);
-    q_finish(a, qs, lane, q, false);
+    if constexpr (STAGE_Q) {
+      q_pin(q);
+      q_finish(a, qs, lane, q, false);
+    }
     __syncthreads();
     append_k_partial_f16(a, qs, row, L, lane, kraw);
   } else {
     WaveRowInputs<KFMT> kin;
     load_wave_row_inputs<KFMT>(a.app.k_new + row * kDim, a.app.k_signs, a.app.k_cb, lane, kin);
     __builtin_amdgcn_sched_barrier(0);
-    q_pin(q);
-    q_finish(a, qs, lane, q, false);
+    float x0, x1;
+    append_k_rebuild_wave<KFMT>(a, row, L, lane, kin, x0, x1);
+    if constexpr (STAGE_Q) {
+      q_pin(q);
+      q_finish(a, qs, lane, q, false);
+    }
     __syncthreads();
-    append_k_partial_wave<KFMT>(a, qs, row, L, lane, kin);
+    append_k_scores_wave(a, qs, row, lane, x0, x1);
   }
+}
+
+// The q staging of append_k_work<KFMT, false>, on another wave of its work group.
+__device__ __forceinline__ void append_stage_q(const DecodeArgs& a, float (*qs)[kDim], size_t row, int lane) {
+  QRaw q;
+  q_request<false>(a, row, lane, q);
+  q_pin(q);
+  q_finish(a, qs, lane, q, false);
+  __syncthreads();
 }
 
 
@@ -701,15 +724,29 @@ __global__ __launch_bounds__(64 * TS) void decode_mfma_kernel(DecodeArgs a, SeqL
   const uint32_t v_lane = VFMT == kFmtTurbo4 ? lane * 16 : lane * 12;
   __shared__ float qs[kMaxGroup][kDim];
   if (append_wg) {
-    if (wv != 0) {   // one wave appends; the others meet its one barrier (K side) and end
-      if (s == -2) __syncthreads();
-      return;
-    }
     // The append is one long dependent chain (binary64 butterflies, exact norm,
     // thresholds) sharing its SIMD with streaming decode waves: let it issue first.
-    __builtin_amdgcn_s_setprio(3);
-    if (s == -1) append_v_partial<KFMT, VFMT>(a, row, L, lane);  // the V side needs no q
-    else append_k_work<KFMT, VFMT>(a, qs, row, L, lane);
+    // Wave 0 encodes; on the K side of a four-wave work group wave 1 stages q
+    // meanwhile and the others only meet the one barrier.
+    if (s == -1) {                         // the V side needs no q
+      if (wv == 0) {
+        __builtin_amdgcn_s_setprio(3);
+        append_v_partial<KFMT, VFMT>(a, row, L, lane);
+      }
+      return;
+    }
+    if constexpr (TS == 1) {
+      __builtin_amdgcn_s_setprio(3);
+      append_k_work<KFMT, true>(a, qs, row, L, lane);
+    } else if (wv == 0) {
+      __builtin_amdgcn_s_setprio(3);
+      append_k_work<KFMT, false>(a, qs, row, L, lane);
+    } else if (wv == 1) {
+      __builtin_amdgcn_s_setprio(3);
+      append_stage_q(a, qs, row, lane);
+    } else {
+      __syncthreads();
+    }
     return;
   }
   if (TS == 1 && a.split_append && s < 2) {
@@ -717,7 +754,7 @@ __global__ __launch_bounds__(64 * TS) void decode_mfma_kernel(DecodeArgs a, SeqL
     // splits, so the first two splits of the row append the token before their own
     // tokens (the kernel's other waves keep streaming meanwhile).
     __builtin_amdgcn_s_setprio(3);
-    if (s == 0) append_k_work<KFMT, VFMT>(a, qs, row, L, lane);
+    if (s == 0) append_k_work<KFMT, true>(a, qs, row, L, lane);
     if (s == 1 || a.plan.max_splits == 1) append_v_partial<KFMT, VFMT>(a, row, L, lane);
     __builtin_amdgcn_s_setprio(0);
     if (s >= nsplit) return;

@@ -380,6 +380,22 @@ def test_one_row_of_many_splits(variant, codebooks):
     _say(f"[one row of many splits v{variant}] rel-L2 {rel:.2e} max-abs {mx:.2e}")
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("fmt,tokens", [("turbo4", 262144), ("turbo3", 393216)])
+def test_middle_sized_decode_step(fmt, tokens, codebooks):
+    """A decode step past the small-call plan (32 MB of packed K and V) and short of the
+    bandwidth-bound one (4M token-heads): one row of 35 / 39 MB, one wave per split, and the
+    token appended by two extra one-wave work groups whose K side stages q itself.  Codes and
+    norms bit-exact, the output against the oracle on the GPU-written bytes."""
+    w = S.scaled(get_workload(3), batch=1, num_kv_heads=1, num_q_heads=4, k_format=fmt, v_format=fmt)
+    _say(f"[middle-sized step {fmt}] generating + encoding")
+    cache, k_list, v_list, L, q, got = S.prefill_then_decode_step(w, lengths=np.array([tokens]))
+    m, g, t = S.compare_codes(cache, 0, k_list[0], v_list[0], int(L[0]), w, codebooks)
+    assert g <= 1e-4 * t
+    rel, mx = S.assert_close(got[0], S.oracle_on_bytes(cache, 0, int(L[0]), q[0], codebooks), "on GPU bytes")
+    _say(f"[middle-sized step {fmt}] rel-L2 {rel:.2e} max-abs {mx:.2e}; codes {m} / {t} mismatched, {g} in the margin")
+
+
 @pytest.mark.parametrize("variant", [0, "fused"])
 @pytest.mark.parametrize("fmt,hq", [("turbo4", 4), ("turbo3", 8)])
 def test_row_at_maximum_capacity(fmt, hq, variant, codebooks):

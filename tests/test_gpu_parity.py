@@ -751,7 +751,8 @@ def _adversarial_rows():
 def test_encode_adversarial_norms_and_codes(fmt, codebooks):
     """Rows whose norm rounding is decided by the encoder's exact fallback (ties and near-ties),
     subnormal and saturating norms, zero rows: norms bit for bit and codes equal to the oracle's
-    outside the 1e-5 boundary margin, through the bulk append and through the decode step."""
+    outside the 1e-5 boundary margin, through the bulk append, the decode step and the one-row
+    append kernel."""
     import torch
 
     import quantized_kv_cache_decode_amd as tq
@@ -772,3 +773,10 @@ def test_encode_adversarial_norms_and_codes(fmt, codebooks):
         S.gpu_decode_step(cache2, x[None, None, i:i + 1], x[None, None, i:i + 1], q)
     m2, g2, t2 = S.compare_codes(cache2, 0, x[None], x[None], n, w, codebooks)
     assert m2 <= g2
+    # the one-row append kernel: each row in turn through tq_encode_append of one token
+    cache3 = S.make_cache(w, cap)
+    for i in range(n):
+        xi = torch.from_numpy(np.ascontiguousarray(x[None, None, i:i + 1])).cuda()
+        tq.tq_encode_append(cache3, xi, xi.clone())
+    m3, g3, t3 = S.compare_codes(cache3, 0, x[None], x[None], n, w, codebooks)
+    assert m3 <= g3

@@ -683,6 +683,23 @@ def test_split_waves_with_few_or_no_tokens(group, k_format, v_format, variant, c
         S.assert_close(got[b], want, f"{variant} G={group} {k_format}/{v_format} L={int(L[b])}")
 
 
+@pytest.mark.parametrize("k_format,v_format", [("turbo3", "turbo3"), ("turbo4", "turbo3")])
+@pytest.mark.parametrize("variant", [0, "fused", "step"])
+def test_uneven_split_waves(k_format, v_format, variant, codebooks):
+    """A small call whose plan cuts 320-token splits (4 rows of 18000 tokens): the four waves of
+    a split take 3, 3, 3 and 1 of its 32-token iterations, and the last split's short tail
+    leaves two of them without tokens."""
+    lens = np.array([18000])
+    w = S.scaled(get_workload(1), batch=1, k_format=k_format, v_format=v_format)
+    if variant == "step":
+        cache, k_list, v_list, L, q, got = S.prefill_then_decode_step(w, lengths=lens)
+    else:
+        cache, k_list, v_list, L, q = S.prefill_and_step(w, lengths=lens)
+        got = S.gpu_decode(cache, q, variant=variant)
+    want = S.oracle_end_to_end(w, k_list[0], v_list[0], int(L[0]), q[0], codebooks)
+    S.assert_close(got[0], want, f"{variant} {k_format}/{v_format} L={int(L[0])}")
+
+
 # ----------------------------------------------------------------------------- many sequences
 
 @pytest.mark.parametrize("variant", ["fused", "step"])
